@@ -1,0 +1,156 @@
+/*
+ * logo.h — C ABI of the token-level dynamic local-global attention forward
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages: "LoGo: Token-Level Dynamic Local-Global Attention",
+ * abstract; "Learning When to Attend", section "The Architecture of
+ * Conditional Attention"; "Local-global attention", attention-mask sketch):
+ *
+ *   every query i attends causally over its last W keys
+ *       L(i) = [max(0, i-W+1), i]                          (local branch)
+ *   a gate logit per (batch, token) and a budget controller pick, per
+ *   sequence, the k = ceil(rho*n) tokens with the largest logits, ties to
+ *   the lower position                                     (selection S)
+ *   the tokens in S also attend over the whole causal prefix
+ *       G(i) = [0, i]                                      (global branch)
+ *   o_i = o_local_i + sigmoid(gate_i) * o_global_i   for i in S
+ *   o_i = o_local_i                                   otherwise
+ *
+ * Scores are scale * <q_i, k_j>; the softmax is exact (no approximation of
+ * either branch). Grouped-query heads: query head h reads key/value head
+ * h / (Hq/Hkv).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Pointers: device pointers (hipMalloc'ed or equivalent), 16-byte aligned,
+ *   owned by the caller. The library never allocates, frees or keeps device
+ *   memory. Scratch space comes from the caller's workspace argument.
+ * Layouts (row-major, contiguous, element strides implied by the shape):
+ *   q, o          [B][Hq][n][d]     dtype = problem.dtype
+ *   k, v          [B][Hkv][n][d]    dtype = problem.dtype
+ *   gate          [B][n]            float32 logits
+ *   mask          [B][n]            uint8, 1 = selected
+ *   idx           [B][k]            int32, selected positions, ascending
+ *   rank          [B][n]            int32, index of the token in idx or -1
+ *   o_local       [B][Hq][n][d]     float32
+ *   o_global      [B][Hq][k][d]     float32, rows in idx order
+ * Streams: `stream` is a hipStream_t (NULL = the default stream). Every call
+ *   only enqueues work on it and returns; nothing synchronises.
+ * Errors: argument errors are detected on the host before anything is
+ *   enqueued; outputs are then untouched. A failed kernel launch returns
+ *   LOGO_ERR_HIP. logo_last_error() gives a readable message for the last
+ *   failure on the calling thread. No C++ exception crosses this boundary.
+ * Empty problems (B == 0 or n == 0) are valid and enqueue nothing.
+ * Supported: d in {64, 128}; dtype LOGO_F32 or LOGO_BF16 (float32
+ *   accumulation in both); 1 <= window; 0 <= rho <= 1; Hq % Hkv == 0;
+ *   n < 2^30; B*Hq*n*d < 2^62.
+ */
+#ifndef LOGO_H
+#define LOGO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LOGO_OK = 0,
+  LOGO_ERR_INVALID_ARG = 1,  /* NULL/misaligned pointer, bad size or ratio */
+  LOGO_ERR_UNSUPPORTED = 2,  /* well-formed but not built (e.g. d = 96)    */
+  LOGO_ERR_WORKSPACE = 3,    /* workspace missing or smaller than needed  */
+  LOGO_ERR_HIP = 4           /* a HIP runtime call or launch failed       */
+} logo_status;
+
+typedef enum { LOGO_F32 = 0, LOGO_BF16 = 1 } logo_dtype;
+
+/* One attention layer's problem description. */
+typedef struct {
+  int64_t B;       /* batch (sequences)                                     */
+  int64_t Hq;      /* query heads                                           */
+  int64_t Hkv;     /* key/value heads; Hq % Hkv == 0                        */
+  int64_t n;       /* tokens per sequence                                   */
+  int64_t d;       /* head dimension: 64 or 128                             */
+  int64_t window;  /* W >= 1: keys each query reads locally, itself included */
+  double rho;      /* target global ratio in [0, 1]; k = ceil(rho * n)      */
+  float scale;     /* score scale; 0 means 1/sqrt(d)                        */
+  int32_t dtype;   /* logo_dtype of q, k, v, o                              */
+} logo_problem;
+
+/* Number of selected tokens per sequence: ceil(rho * n) computed in double
+ * and clamped to [0, n] (LoGo abstract: the budget controller keeps a target
+ * global ratio). Returns -1 when rho is NaN or n < 0. */
+int64_t logo_target_count(double rho, int64_t n);
+
+/* Bytes of workspace logo_forward needs for this problem (float32 local
+ * outputs of the selected rows: B*Hq*k*d*4, rounded up to 256). Writes 0
+ * when nothing is needed. Errors: LOGO_ERR_INVALID_ARG / _UNSUPPORTED as
+ * for logo_forward. */
+logo_status logo_workspace_size(const logo_problem* p, size_t* bytes);
+
+/* Budget controller + compaction (LoGo abstract: threshold-based budget
+ * controller; "Learning When to Attend": one binary decision per token).
+ * For each sequence b, selects the k = ceil(rho*n) largest gate[b][.]
+ * (ties to the lower position, -0.0 == +0.0, NaN below every number) and
+ * writes mask, idx (ascending) and rank. The result is unique and
+ * bit-exact. idx may be NULL when k == 0. */
+logo_status logo_select_queries(const logo_problem* p, const float* gate,
+                                uint8_t* mask, int32_t* idx, int32_t* rank,
+                                void* stream);
+
+/* Local branch for every query: softmax over L(i) = [max(0,i-W+1), i],
+ * times V ("Local-global attention", attention-mask sketch: causal and
+ * within-window). Writes o_local [B][Hq][n][d] float32. */
+logo_status logo_local_attn(const logo_problem* p, const void* q, const void* k,
+                            const void* v, float* o_local, void* stream);
+
+/* Global branch for the selected queries only: softmax over G(i) = [0, i],
+ * times V ("Learning When to Attend": exact attention over the full context
+ * for a sparse subset of query tokens). idx [B][k] are the rows (ascending
+ * positions, each in [0, n)); writes o_global [B][Hq][k][d] float32 in idx
+ * order. Nothing is enqueued when k == 0 (idx, o_global may be NULL). */
+logo_status logo_global_attn_sparse(const logo_problem* p, const void* q,
+                                    const void* k, const void* v,
+                                    const int32_t* idx, float* o_global,
+                                    void* stream);
+
+/* Gated combine: o = o_local + sigmoid(gate) * o_global[rank] where
+ * rank >= 0, o = o_local elsewhere; float32 arithmetic, one rounding to the
+ * output dtype. o_global may be NULL when k == 0. */
+logo_status logo_combine(const logo_problem* p, const float* o_local,
+                         const float* o_global, const int32_t* rank,
+                         const float* gate, void* o, void* stream);
+
+/* The whole layer in one call: selection, local branch, global branch on S,
+ * combine, on one stream with no host synchronisation. Writes o and the
+ * selection (mask, idx, rank). `workspace` must hold logo_workspace_size
+ * bytes (may be NULL when that is 0). Output equals logo_select_queries ->
+ * logo_local_attn -> logo_global_attn_sparse -> logo_combine up to float32
+ * rounding order. */
+logo_status logo_forward(const logo_problem* p, const void* q, const void* k,
+                         const void* v, const float* gate, void* o,
+                         uint8_t* mask, int32_t* idx, int32_t* rank,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* logo_status_string(logo_status s);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char* logo_last_error(void);
+
+/* Kernel timing for measurement. Between logo_profile_begin() and
+ * logo_profile_end(), logo_forward records a HIP event pair around each of
+ * its kernels on the caller's stream (at most 4096 pairs; later launches go
+ * unrecorded). logo_profile_end() waits for those events and writes, per
+ * stage (0 select, 1 local, 2 global, 3 combine), the summed milliseconds
+ * and the number of launches into arrays of `n_stages` entries. */
+logo_status logo_profile_begin(void);
+logo_status logo_profile_end(double* stage_ms, int64_t* stage_launches,
+                             int32_t n_stages);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOGO_H */

@@ -1,0 +1,140 @@
+"""The C ABI on the CPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments before enqueueing anything (no
+call here reaches a kernel launch). No GPU."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import token_level_dynamic_amd as T
+from token_level_dynamic_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "logo.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return T.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(logo_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("logo_select_queries", "logo_local_attn", "logo_global_attn_sparse",
+                 "logo_combine", "logo_forward", "logo_target_count", "logo_workspace_size"):
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s+(logo_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(L, name) is not None
+
+
+def test_target_count(L):
+    for rho, n, k in [(0.2, 32768, 6554), (0.25, 256, 64), (0.2, 131072, 26215),
+                      (0.05, 65536, 3277), (0.0, 10, 0), (1.0, 10, 10), (0.11, 10, 2)]:
+        assert T.logo_target_count(rho, n) == k
+    assert T.logo_target_count(math.nan, 10) == -1
+    assert T.logo_target_count(0.5, -1) == -1
+
+
+def _prob(**kw):
+    base = dict(B=2, Hq=4, Hkv=2, n=100, d=128, window=16, rho=0.2, scale=0.0, dtype=1)
+    base.update(kw)
+    return _lib.logo_problem(**base)
+
+
+FAKE = 1 << 20          # an aligned non-null address; never dereferenced here
+MISALIGNED = FAKE + 4
+
+
+def _forward(L, p, q=FAKE, k=FAKE, v=FAKE, gate=FAKE, o=FAKE, mask=FAKE, idx=FAKE,
+             rank=FAKE, ws=None, ws_bytes=0):
+    return L.logo_forward(ctypes.byref(p) if p is not None else None, q, k, v, gate, o, mask,
+                          idx, rank, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=3, Hkv=2), _lib.LOGO_ERR_INVALID_ARG),
+    (dict(rho=-0.1), _lib.LOGO_ERR_INVALID_ARG),
+    (dict(rho=1.5), _lib.LOGO_ERR_INVALID_ARG),
+    (dict(rho=math.nan), _lib.LOGO_ERR_INVALID_ARG),
+    (dict(window=0), _lib.LOGO_ERR_INVALID_ARG),
+    (dict(d=96), _lib.LOGO_ERR_UNSUPPORTED),
+    (dict(dtype=7), _lib.LOGO_ERR_INVALID_ARG),
+    (dict(scale=-1.0), _lib.LOGO_ERR_INVALID_ARG),
+    (dict(scale=math.inf), _lib.LOGO_ERR_INVALID_ARG),
+    (dict(n=-1), _lib.LOGO_ERR_INVALID_ARG),
+    (dict(Hkv=0), _lib.LOGO_ERR_INVALID_ARG),
+    (dict(n=1 << 31), _lib.LOGO_ERR_UNSUPPORTED),
+])
+def test_problem_validation(L, kw, status):
+    p = _prob(**kw)
+    assert _forward(L, p) == status
+    assert L.logo_last_error()
+    size = ctypes.c_size_t(123)
+    assert L.logo_workspace_size(ctypes.byref(p), ctypes.byref(size)) == status
+    assert L.logo_local_attn(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None) == status
+
+
+def test_null_problem(L):
+    assert _forward(L, None) == _lib.LOGO_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "gate", "o", "mask", "idx", "rank"])
+def test_null_and_misaligned_pointers(L, field):
+    p = _prob()
+    assert _forward(L, p, **{field: None}) == _lib.LOGO_ERR_INVALID_ARG
+    assert field.encode() in L.logo_last_error()
+    assert _forward(L, p, **{field: MISALIGNED}) == _lib.LOGO_ERR_INVALID_ARG
+
+
+def test_workspace_checks(L):
+    p = _prob()
+    size = ctypes.c_size_t(0)
+    assert L.logo_workspace_size(ctypes.byref(p), ctypes.byref(size)) == 0
+    k = T.logo_target_count(0.2, 100)
+    want = 2 * 4 * k * 128 * 4
+    assert size.value == (want + 255) // 256 * 256
+    assert _forward(L, p, ws=None) == _lib.LOGO_ERR_WORKSPACE
+    assert _forward(L, p, ws=FAKE, ws_bytes=size.value - 1) == _lib.LOGO_ERR_WORKSPACE
+    # rho = 0 selects nothing: no workspace needed
+    p0 = _prob(rho=0.0)
+    assert L.logo_workspace_size(ctypes.byref(p0), ctypes.byref(size)) == 0
+    assert size.value == 0
+
+
+def test_empty_problems_enqueue_nothing(L):
+    for kw in (dict(B=0), dict(n=0)):
+        p = _prob(**kw)
+        assert _forward(L, p, q=None, k=None, v=None, gate=None, o=None, mask=None, idx=None,
+                        rank=None) == 0
+        assert L.logo_select_queries(ctypes.byref(p), None, None, None, None, None) == 0
+        assert L.logo_combine(ctypes.byref(p), None, None, None, None, None, None) == 0
+
+
+def test_status_strings(L):
+    for s in range(5):
+        assert L.logo_status_string(s)
+    assert L.logo_status_string(99) == b"unknown status"
+
+
+def test_profile_end_argument_check(L):
+    assert L.logo_profile_begin() == 0
+    assert L.logo_profile_end(None, None, 4) == _lib.LOGO_ERR_INVALID_ARG
+    assert L.logo_profile_end(None, None, 0) == 0

@@ -1,0 +1,26 @@
+"""Token-level dynamic local-global attention (forward) for AMD MI355X.
+
+The computation lives in liblogo.so (HIP kernels for gfx950 behind the C ABI
+of include/logo.h). This package is its Python binding: the same entry
+points, taking torch tensors for device memory and a HIP stream.
+"""
+from ._lib import (  # noqa: F401
+    LOGO_BF16,
+    LOGO_F32,
+    STAGES,
+    LogoError,
+    alloc_forward_buffers,
+    io_dtype,
+    lib,
+    logo_combine,
+    logo_forward,
+    logo_global_attn_sparse,
+    logo_local_attn,
+    logo_problem,
+    logo_profile_begin,
+    logo_profile_end,
+    logo_select_queries,
+    logo_target_count,
+    logo_workspace_size,
+    make_problem,
+)

@@ -1,0 +1,230 @@
+"""ctypes binding of liblogo.so (include/logo.h), argument marshalling only.
+
+Every function here has the name of the C entry point it calls and does no
+arithmetic of the method: it checks tensor placement, dtypes and shapes,
+passes device pointers and the current HIP stream, and turns a non-zero
+status into an exception. PyTorch supplies device memory and streams.
+If the shared library is missing, every call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblogo.so")
+
+LOGO_OK = 0
+LOGO_ERR_INVALID_ARG = 1
+LOGO_ERR_UNSUPPORTED = 2
+LOGO_ERR_WORKSPACE = 3
+LOGO_ERR_HIP = 4
+LOGO_F32 = 0
+LOGO_BF16 = 1
+STAGES = ("select", "local", "global", "combine")
+
+
+class LogoError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status}: {detail}")
+        self.status = status
+
+
+class logo_problem(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int64),
+        ("Hq", ctypes.c_int64),
+        ("Hkv", ctypes.c_int64),
+        ("n", ctypes.c_int64),
+        ("d", ctypes.c_int64),
+        ("window", ctypes.c_int64),
+        ("rho", ctypes.c_double),
+        ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+def make_problem(B: int, Hq: int, Hkv: int, n: int, d: int, window: int, rho: float,
+                 scale: float = 0.0, dtype: str = "bf16") -> logo_problem:
+    dt = {"bf16": LOGO_BF16, "f32": LOGO_F32}[dtype]
+    return logo_problem(B, Hq, Hkv, n, d, window, float(rho), float(scale), dt)
+
+
+_lib = None
+_P = ctypes.c_void_p
+_PP = ctypes.POINTER(logo_problem)
+
+_SIGS = {
+    "logo_target_count": (ctypes.c_int64, [ctypes.c_double, ctypes.c_int64]),
+    "logo_workspace_size": (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_size_t)]),
+    "logo_select_queries": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P]),
+    "logo_local_attn": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P]),
+    "logo_global_attn_sparse": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P]),
+    "logo_combine": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P]),
+    "logo_forward": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                    ctypes.c_size_t, _P]),
+    "logo_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "logo_last_error": (ctypes.c_char_p, []),
+    "logo_profile_begin": (ctypes.c_int, []),
+    "logo_profile_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_int64), ctypes.c_int32]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded liblogo.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m token_level_dynamic_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != LOGO_OK:
+        detail = lib().logo_last_error().decode(errors="replace")
+        raise LogoError(status, where, detail)
+
+
+def _ptr(t: Optional[torch.Tensor], name: str) -> Optional[int]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _expect(t: Optional[torch.Tensor], name: str, dtype: torch.dtype, numel: int) -> None:
+    if t is None:
+        if numel:
+            raise ValueError(f"{name} is required")
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+
+
+def io_dtype(p: logo_problem) -> torch.dtype:
+    return torch.bfloat16 if p.dtype == LOGO_BF16 else torch.float32
+
+
+def logo_target_count(rho: float, n: int) -> int:
+    return int(lib().logo_target_count(float(rho), int(n)))
+
+
+def logo_workspace_size(p: logo_problem) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().logo_workspace_size(ctypes.byref(p), ctypes.byref(out)), "logo_workspace_size")
+    return int(out.value)
+
+
+def logo_select_queries(p: logo_problem, gate, mask, idx, rank, stream=None) -> None:
+    k = logo_target_count(p.rho, p.n)
+    _expect(gate, "gate", torch.float32, p.B * p.n)
+    _expect(mask, "mask", torch.uint8, p.B * p.n)
+    _expect(idx, "idx", torch.int32, p.B * k)
+    _expect(rank, "rank", torch.int32, p.B * p.n)
+    _check(lib().logo_select_queries(ctypes.byref(p), _ptr(gate, "gate"), _ptr(mask, "mask"),
+                                     _ptr(idx, "idx"), _ptr(rank, "rank"), _stream(stream)),
+           "logo_select_queries")
+
+
+def _qkv(p: logo_problem, q, k, v) -> None:
+    dt = io_dtype(p)
+    _expect(q, "q", dt, p.B * p.Hq * p.n * p.d)
+    _expect(k, "k", dt, p.B * p.Hkv * p.n * p.d)
+    _expect(v, "v", dt, p.B * p.Hkv * p.n * p.d)
+
+
+def logo_local_attn(p: logo_problem, q, k, v, o_local, stream=None) -> None:
+    _qkv(p, q, k, v)
+    _expect(o_local, "o_local", torch.float32, p.B * p.Hq * p.n * p.d)
+    _check(lib().logo_local_attn(ctypes.byref(p), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"),
+                                 _ptr(o_local, "o_local"), _stream(stream)), "logo_local_attn")
+
+
+def logo_global_attn_sparse(p: logo_problem, q, k, v, idx, o_global, stream=None) -> None:
+    kk = logo_target_count(p.rho, p.n)
+    _qkv(p, q, k, v)
+    _expect(idx, "idx", torch.int32, p.B * kk)
+    _expect(o_global, "o_global", torch.float32, p.B * p.Hq * kk * p.d)
+    _check(lib().logo_global_attn_sparse(ctypes.byref(p), _ptr(q, "q"), _ptr(k, "k"),
+                                         _ptr(v, "v"), _ptr(idx, "idx"),
+                                         _ptr(o_global, "o_global"), _stream(stream)),
+           "logo_global_attn_sparse")
+
+
+def logo_combine(p: logo_problem, o_local, o_global, rank, gate, o, stream=None) -> None:
+    kk = logo_target_count(p.rho, p.n)
+    _expect(o_local, "o_local", torch.float32, p.B * p.Hq * p.n * p.d)
+    _expect(o_global, "o_global", torch.float32, p.B * p.Hq * kk * p.d)
+    _expect(rank, "rank", torch.int32, p.B * p.n)
+    _expect(gate, "gate", torch.float32, p.B * p.n)
+    _expect(o, "o", io_dtype(p), p.B * p.Hq * p.n * p.d)
+    _check(lib().logo_combine(ctypes.byref(p), _ptr(o_local, "o_local"),
+                              _ptr(o_global, "o_global"), _ptr(rank, "rank"),
+                              _ptr(gate, "gate"), _ptr(o, "o"), _stream(stream)), "logo_combine")
+
+
+def logo_forward(p: logo_problem, q, k, v, gate, o, mask, idx, rank, workspace,
+                 stream=None) -> None:
+    kk = logo_target_count(p.rho, p.n)
+    _qkv(p, q, k, v)
+    _expect(gate, "gate", torch.float32, p.B * p.n)
+    _expect(o, "o", io_dtype(p), p.B * p.Hq * p.n * p.d)
+    _expect(mask, "mask", torch.uint8, p.B * p.n)
+    _expect(idx, "idx", torch.int32, p.B * kk)
+    _expect(rank, "rank", torch.int32, p.B * p.n)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().logo_forward(ctypes.byref(p), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"),
+                              _ptr(gate, "gate"), _ptr(o, "o"), _ptr(mask, "mask"),
+                              _ptr(idx, "idx"), _ptr(rank, "rank"),
+                              _ptr(workspace, "workspace"), ws_bytes, _stream(stream)),
+           "logo_forward")
+
+
+def logo_profile_begin() -> None:
+    _check(lib().logo_profile_begin(), "logo_profile_begin")
+
+
+def logo_profile_end() -> Tuple[list, list]:
+    n = len(STAGES)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    _check(lib().logo_profile_end(ms, cnt, n), "logo_profile_end")
+    return list(ms), list(cnt)
+
+
+def alloc_forward_buffers(p: logo_problem, device="cuda") -> dict:
+    """Output, selection and workspace tensors for logo_forward."""
+    kk = logo_target_count(p.rho, p.n)
+    ws = logo_workspace_size(p)
+    return {
+        "o": torch.empty((p.B, p.Hq, p.n, p.d), dtype=io_dtype(p), device=device),
+        "mask": torch.empty((p.B, p.n), dtype=torch.uint8, device=device),
+        "idx": torch.empty((p.B, kk), dtype=torch.int32, device=device),
+        "rank": torch.empty((p.B, p.n), dtype=torch.int32, device=device),
+        "workspace": torch.empty((ws,), dtype=torch.uint8, device=device) if ws else None,
+    }

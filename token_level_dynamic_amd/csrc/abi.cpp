@@ -1,0 +1,336 @@
+// C ABI of the token-level dynamic local-global attention forward: argument
+// validation, target count, workspace sizing, dispatch to the HIP kernels,
+// kernel timing. Every entry point is declared and documented in
+// include/logo.h. No C++ exception leaves this file.
+#include "../../include/logo.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "logo_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+logo_status fail(logo_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+logo_status fail(logo_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+logo_status hip_fail(hipError_t e, const char* what) {
+  return fail(LOGO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t target_count(double rho, int64_t n) {
+  if (std::isnan(rho) || n < 0) return -1;
+  double k = std::ceil(rho * (double)n);
+  if (k < 0) k = 0;
+  if (k > (double)n) k = (double)n;
+  return (int64_t)k;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validates the problem and fills the kernels' view of it.
+logo_status check_problem(const logo_problem* p, logo::Dims* out) {
+  if (!p) return fail(LOGO_ERR_INVALID_ARG, "problem is NULL");
+  if (p->B < 0 || p->n < 0) return fail(LOGO_ERR_INVALID_ARG, "B and n must be >= 0");
+  if (p->Hq < 1 || p->Hkv < 1) return fail(LOGO_ERR_INVALID_ARG, "Hq and Hkv must be >= 1");
+  if (p->Hq % p->Hkv != 0)
+    return fail(LOGO_ERR_INVALID_ARG, "Hq (%lld) must be a multiple of Hkv (%lld)",
+                (long long)p->Hq, (long long)p->Hkv);
+  if (p->window < 1) return fail(LOGO_ERR_INVALID_ARG, "window must be >= 1");
+  if (std::isnan(p->rho) || p->rho < 0.0 || p->rho > 1.0)
+    return fail(LOGO_ERR_INVALID_ARG, "rho must be in [0, 1]");
+  if (!std::isfinite(p->scale) || p->scale < 0.0f)
+    return fail(LOGO_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if (p->dtype != LOGO_F32 && p->dtype != LOGO_BF16)
+    return fail(LOGO_ERR_INVALID_ARG, "dtype must be LOGO_F32 or LOGO_BF16");
+  if (p->d != 64 && p->d != 128)
+    return fail(LOGO_ERR_UNSUPPORTED, "head dimension %lld not supported (64 or 128)",
+                (long long)p->d);
+  if (p->n >= (int64_t(1) << 30) || p->Hq >= (int64_t(1) << 20) || p->B >= (int64_t(1) << 20))
+    return fail(LOGO_ERR_UNSUPPORTED, "sizes beyond the supported range");
+  const double elems = (double)p->B * (double)p->Hq * (double)p->n * (double)p->d;
+  if (elems >= 4.0e18) return fail(LOGO_ERR_UNSUPPORTED, "problem too large");
+  out->B = (int)p->B;
+  out->Hq = (int)p->Hq;
+  out->Hkv = (int)p->Hkv;
+  out->n = (int)p->n;
+  out->d = (int)p->d;
+  out->window = (int)std::min<int64_t>(p->window, int64_t(1) << 30);
+  out->k = (int)target_count(p->rho, p->n);
+  out->scale = p->scale == 0.0f ? (float)(1.0 / std::sqrt((double)p->d)) : p->scale;
+  out->dtype = p->dtype;
+  return LOGO_OK;
+}
+
+bool empty(const logo::Dims& d) { return d.B == 0 || d.n == 0; }
+
+logo_status need_ptr(const void* ptr, const char* name) {
+  if (!ptr) return fail(LOGO_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(ptr)) return fail(LOGO_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return LOGO_OK;
+}
+
+#define LOGO_TRY(expr)                 \
+  do {                                 \
+    logo_status _s = (expr);           \
+    if (_s != LOGO_OK) return _s;      \
+  } while (0)
+
+size_t scratch_bytes(const logo::Dims& d) {
+  const size_t b = (size_t)d.B * d.Hq * d.k * d.d * sizeof(float);
+  return (b + 255) / 256 * 256;
+}
+
+// ---- kernel timing --------------------------------------------------------
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  struct Rec {
+    hipEvent_t a, b;
+    int stage;
+  };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+};
+Profiler g_prof;
+constexpr size_t kMaxRecords = 4096;
+
+// Records the start event of a stage; returns the record slot or -1.
+long prof_start(int stage, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (!g_prof.on || g_prof.recs.size() >= kMaxRecords) return -1;
+  while (g_prof.pool.size() < 2 * (g_prof.recs.size() + 1)) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return -1;
+    g_prof.pool.push_back(e);
+  }
+  Profiler::Rec r{g_prof.pool[2 * g_prof.recs.size()], g_prof.pool[2 * g_prof.recs.size() + 1],
+                  stage};
+  if (hipEventRecord(r.a, s) != hipSuccess) return -1;
+  g_prof.recs.push_back(r);
+  return (long)g_prof.recs.size() - 1;
+}
+
+void prof_stop(long slot, hipStream_t s) {
+  if (slot < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (slot < (long)g_prof.recs.size()) (void)hipEventRecord(g_prof.recs[slot].b, s);
+}
+
+struct StageTimer {
+  long slot;
+  hipStream_t s;
+  StageTimer(int stage, hipStream_t st) : slot(prof_start(stage, st)), s(st) {}
+  ~StageTimer() { prof_stop(slot, s); }
+};
+
+hipError_t run_attn(const logo::Dims& d, logo::Epi epi, const logo::AttnArgs& a,
+                    hipStream_t s) {
+  return d.dtype == LOGO_BF16 ? logo::launch_attn_bf16(d, epi, a, s)
+                              : logo::launch_attn_f32(d, epi, a, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t logo_target_count(double rho, int64_t n) { return target_count(rho, n); }
+
+const char* logo_status_string(logo_status s) {
+  switch (s) {
+    case LOGO_OK: return "ok";
+    case LOGO_ERR_INVALID_ARG: return "invalid argument";
+    case LOGO_ERR_UNSUPPORTED: return "unsupported problem";
+    case LOGO_ERR_WORKSPACE: return "workspace missing or too small";
+    case LOGO_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* logo_last_error(void) { return g_last_error; }
+
+logo_status logo_workspace_size(const logo_problem* p, size_t* bytes) {
+  logo::Dims d;
+  LOGO_TRY(check_problem(p, &d));
+  if (!bytes) return fail(LOGO_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = empty(d) ? 0 : scratch_bytes(d);
+  return LOGO_OK;
+}
+
+logo_status logo_select_queries(const logo_problem* p, const float* gate, uint8_t* mask,
+                                int32_t* idx, int32_t* rank, void* stream) {
+  logo::Dims d;
+  LOGO_TRY(check_problem(p, &d));
+  if (empty(d)) return LOGO_OK;
+  LOGO_TRY(need_ptr(gate, "gate"));
+  LOGO_TRY(need_ptr(mask, "mask"));
+  LOGO_TRY(need_ptr(rank, "rank"));
+  if (d.k > 0) LOGO_TRY(need_ptr(idx, "idx"));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  StageTimer tm(0, s);
+  hipError_t e = logo::launch_select(d, gate, mask, d.k > 0 ? idx : nullptr, rank, s);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  return LOGO_OK;
+}
+
+logo_status logo_local_attn(const logo_problem* p, const void* q, const void* k,
+                            const void* v, float* o_local, void* stream) {
+  logo::Dims d;
+  LOGO_TRY(check_problem(p, &d));
+  if (empty(d)) return LOGO_OK;
+  LOGO_TRY(need_ptr(q, "q"));
+  LOGO_TRY(need_ptr(k, "k"));
+  LOGO_TRY(need_ptr(v, "v"));
+  LOGO_TRY(need_ptr(o_local, "o_local"));
+  logo::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out_f32 = o_local;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  StageTimer tm(1, s);
+  hipError_t e = run_attn(d, logo::Epi::LocalAll, a, s);
+  if (e != hipSuccess) return hip_fail(e, "local attention launch");
+  return LOGO_OK;
+}
+
+logo_status logo_global_attn_sparse(const logo_problem* p, const void* q, const void* k,
+                                    const void* v, const int32_t* idx, float* o_global,
+                                    void* stream) {
+  logo::Dims d;
+  LOGO_TRY(check_problem(p, &d));
+  if (empty(d) || d.k == 0) return LOGO_OK;
+  LOGO_TRY(need_ptr(q, "q"));
+  LOGO_TRY(need_ptr(k, "k"));
+  LOGO_TRY(need_ptr(v, "v"));
+  LOGO_TRY(need_ptr(idx, "idx"));
+  LOGO_TRY(need_ptr(o_global, "o_global"));
+  logo::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.idx = idx;
+  a.out_f32 = o_global;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  StageTimer tm(2, s);
+  hipError_t e = run_attn(d, logo::Epi::GlobalAll, a, s);
+  if (e != hipSuccess) return hip_fail(e, "global attention launch");
+  return LOGO_OK;
+}
+
+logo_status logo_combine(const logo_problem* p, const float* o_local, const float* o_global,
+                         const int32_t* rank, const float* gate, void* o, void* stream) {
+  logo::Dims d;
+  LOGO_TRY(check_problem(p, &d));
+  if (empty(d)) return LOGO_OK;
+  LOGO_TRY(need_ptr(o_local, "o_local"));
+  LOGO_TRY(need_ptr(rank, "rank"));
+  LOGO_TRY(need_ptr(gate, "gate"));
+  LOGO_TRY(need_ptr(o, "o"));
+  if (d.k > 0) LOGO_TRY(need_ptr(o_global, "o_global"));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  StageTimer tm(3, s);
+  hipError_t e = logo::launch_combine(d, o_local, o_global, rank, gate, o, s);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return LOGO_OK;
+}
+
+logo_status logo_forward(const logo_problem* p, const void* q, const void* k, const void* v,
+                         const float* gate, void* o, uint8_t* mask, int32_t* idx,
+                         int32_t* rank, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  logo::Dims d;
+  LOGO_TRY(check_problem(p, &d));
+  if (empty(d)) return LOGO_OK;
+  LOGO_TRY(need_ptr(q, "q"));
+  LOGO_TRY(need_ptr(k, "k"));
+  LOGO_TRY(need_ptr(v, "v"));
+  LOGO_TRY(need_ptr(gate, "gate"));
+  LOGO_TRY(need_ptr(o, "o"));
+  LOGO_TRY(need_ptr(mask, "mask"));
+  LOGO_TRY(need_ptr(rank, "rank"));
+  const size_t ws_need = scratch_bytes(d);
+  if (d.k > 0) {
+    LOGO_TRY(need_ptr(idx, "idx"));
+    if (!workspace || workspace_bytes < ws_need)
+      return fail(LOGO_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws_need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(LOGO_ERR_INVALID_ARG, "workspace misaligned");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  {
+    StageTimer tm(0, s);
+    e = logo::launch_select(d, gate, mask, d.k > 0 ? idx : nullptr, rank, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  logo::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.idx = idx;
+  a.rank = rank;
+  a.gate = gate;
+  a.out_f32 = static_cast<float*>(workspace);
+  a.scratch = static_cast<const float*>(workspace);
+  a.out_io = o;
+  {
+    StageTimer tm(1, s);
+    e = run_attn(d, logo::Epi::LocalFused, a, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "local attention launch");
+  if (d.k > 0) {
+    StageTimer tm(2, s);
+    e = run_attn(d, logo::Epi::GlobalFused, a, s);
+    if (e != hipSuccess) return hip_fail(e, "global attention launch");
+  }
+  return LOGO_OK;
+}
+
+logo_status logo_profile_begin(void) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.on = true;
+  g_prof.recs.clear();
+  return LOGO_OK;
+}
+
+logo_status logo_profile_end(double* stage_ms, int64_t* stage_launches, int32_t n_stages) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.on = false;
+  if (n_stages < 0 || (n_stages > 0 && (!stage_ms || !stage_launches)))
+    return fail(LOGO_ERR_INVALID_ARG, "stage arrays missing");
+  for (int i = 0; i < n_stages; ++i) {
+    stage_ms[i] = 0.0;
+    stage_launches[i] = 0;
+  }
+  for (auto& r : g_prof.recs) {
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return hip_fail(e, "profile event wait");
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return hip_fail(e, "profile event time");
+    if (r.stage >= 0 && r.stage < n_stages) {
+      stage_ms[r.stage] += ms;
+      stage_launches[r.stage] += 1;
+    }
+  }
+  g_prof.recs.clear();
+  return LOGO_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Internal interface between the C ABI (abi.cpp) and the HIP kernels.
+// gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace logo {
+
+// Validated problem, as the kernels see it.
+struct Dims {
+  int B, Hq, Hkv, n, d, window;
+  int k;          // selected tokens per sequence
+  float scale;    // score scale
+  int dtype;      // 0 f32, 1 bf16 (for q, k, v, o)
+};
+
+// What the attention kernels write for each row they finish.
+enum class Epi : int {
+  LocalAll = 0,    // o_local[b][h][i][:] (f32) for every row
+  LocalFused = 1,  // rank[i] >= 0: scratch[b][h][rank][:] (f32); else o (io dtype)
+  GlobalAll = 2,   // o_global[b][h][r][:] (f32), r = row in idx
+  GlobalFused = 3  // o = scratch[b][h][r] + sigmoid(gate) * o_global (io dtype)
+};
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* idx;    // global branch rows [B][k]
+  const int32_t* rank;   // fused local: [B][n]
+  const float* gate;     // fused global: [B][n]
+  float* out_f32;        // o_local / o_global / scratch (fused local)
+  const float* scratch;  // fused global: local outputs of selected rows
+  void* out_io;          // fused: final output o
+};
+
+hipError_t launch_select(const Dims& d, const float* gate, uint8_t* mask,
+                         int32_t* idx, int32_t* rank, hipStream_t s);
+
+hipError_t launch_attn_bf16(const Dims& d, Epi epi, const AttnArgs& a,
+                            hipStream_t s);
+
+hipError_t launch_attn_f32(const Dims& d, Epi epi, const AttnArgs& a,
+                           hipStream_t s);
+
+hipError_t launch_combine(const Dims& d, const float* o_local,
+                          const float* o_global, const int32_t* rank,
+                          const float* gate, void* o, hipStream_t s);
+
+}  // namespace logo
