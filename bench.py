@@ -1,0 +1,230 @@
+"""Benchmark: one forward of token-level dynamic local-global attention.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa32k]
+                    [--rho R] [--no-cpu-baseline]
+
+A step is one logo_forward over one batch of seeded synthetic input already
+resident in HBM: budget-controller selection, local band attention for every
+query, query-sparse global attention for the selected rows, gated combine.
+Prints one JSON line.
+
+value    effective attention TFLOP/s of the whole layer:
+         F = 4 d sum_b sum_h [ sum_i min(W, i+1) + sum_{i in S_b} (i+1) ]
+         (2 flops per multiply-add, Q K^T and P V both counted, softmax not
+         counted, masked pairs not counted; S is the realised selection)
+         divided by the measured time per step.
+roofline the dominant kernel (the query-sparse global branch at the default
+         workload): its algorithmic FLOPs per launch over its average launch
+         time, measured with HIP events recorded by the library on the
+         kernel's own stream during the timed steps, against the bf16 dense
+         matrix-core peak of MI355X (2500 TFLOP/s). `traffic` is the HBM
+         bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE counters,
+         scaled by a copy-kernel calibration (profiles/), reported only while
+         the kernel sources match the ones the counters were taken on.
+cpu_baseline the CPU fp64 oracle, timed on this host on a bounded random
+         sample of the same layer's rows (the oracle is a reported baseline,
+         not a target).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
+HBM_PEAK_GBS = 8000.0
+METRIC = "effective attn TFLOP/s + ms/layer fwd at 32K ctx, rho=0.2; % of bf16 MFMA peak"
+KERNEL_SOURCES = ["attn_bf16.hip", "select.hip", "combine.hip", "abi.cpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "token_level_dynamic_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def effective_flops(w, idx: np.ndarray) -> dict:
+    """Effective FLOPs of the layer from the realised selection idx [B, k]."""
+    i = np.arange(w.n, dtype=np.float64)
+    band_pairs = float(np.minimum(w.window, i + 1).sum())          # per (b, h)
+    glob_pairs = [float((idx[b].astype(np.float64) + 1).sum()) for b in range(w.B)]
+    per_pair = 4.0 * w.d
+    local = per_pair * w.Hq * w.B * band_pairs
+    glob = per_pair * w.Hq * sum(glob_pairs)
+    return {"local": local, "global": glob, "total": local + glob}
+
+
+def cpu_baseline(w, inp, idx, budget_s: float = 15.0, seed: int = 0) -> dict:
+    """Times the CPU oracle on a random sample of the layer's rows."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: numpy's BLAS threads unknown
+        threads = 1
+    r = np.random.default_rng(seed)
+    sel = np.zeros((w.B, w.n), dtype=bool)
+    for b in range(w.B):
+        sel[b, idx[b]] = True
+    flops = 0.0
+    n_rows = n_glob = 0
+    t0 = time.perf_counter()
+    # the selection over the whole sequence is part of every oracle call
+    while time.perf_counter() - t0 < budget_s:
+        chunk = [(int(r.integers(0, w.B)), int(r.integers(0, w.Hq)), int(r.integers(0, w.n)))
+                 for _ in range(64)]
+        oracle.forward_rows(inp.q, inp.k, inp.v, inp.gate, w.window, w.rho, chunk)
+        for b, h, i in chunk:
+            flops += 4.0 * w.d * min(w.window, i + 1)
+            if sel[b, i]:
+                flops += 4.0 * w.d * (i + 1)
+                n_glob += 1
+        n_rows += len(chunk)
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n_rows} rows (b, h, i) drawn uniformly with seed {seed} from the "
+                      f"{w.name} layer ({n_glob} of them selected, so also global), one "
+                      f"oracle.forward_rows call per 64 rows, {dt:.1f} s wall"}
+
+
+def load_traffic(workload: str, current_hash: str):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(workload)
+    if not ent or ent.get("source_hash") != current_hash:
+        return None
+    return ent.get("global_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gqa32k")
+    ap.add_argument("--rho", type=float, default=None)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import token_level_dynamic_amd as T
+    from workloads import get_workload, make_inputs
+
+    from token_level_dynamic_amd._lib import LIB_PATH
+    if not os.path.exists(LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    T.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+
+    w = get_workload(args.workload)
+    if args.rho is not None:
+        w = w.with_(rho=args.rho)
+    inp = make_inputs(w, args.seed)
+    dev = torch.device("cuda:0")
+    if w.dtype == "bf16":
+        def cv(bits):
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        q, k, v = cv(inp.q_bits), cv(inp.k_bits), cv(inp.v_bits)
+    else:
+        q, k, v = (torch.from_numpy(x).to(dev) for x in (inp.q, inp.k, inp.v))
+    gate = torch.from_numpy(inp.gate).to(dev)
+    p = T.make_problem(w.B, w.Hq, w.Hkv, w.n, w.d, w.window, w.rho, dtype=w.dtype)
+    buf = T.alloc_forward_buffers(p, dev)
+
+    def step():
+        T.logo_forward(p, q, k, v, gate, buf["o"], buf["mask"], buf["idx"], buf["rank"],
+                       buf["workspace"])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    T.logo_profile_begin()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    stage_ms, stage_n = T.logo_profile_end()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    idx = buf["idx"].cpu().numpy()
+    F = effective_flops(w, idx)
+    tflops = F["total"] / (ms_per_step * 1e-3) / 1e12
+    avg = {s: (stage_ms[j] / stage_n[j] if stage_n[j] else None)
+           for j, s in enumerate(T.STAGES)}
+    dom = "global" if F["global"] >= F["local"] else "local"
+    dom_ms = avg[dom]
+    dom_flops = F[dom]
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms else None
+    traffic = load_traffic(w.name, kernel_source_hash()) if dom == "global" else None
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "n": w.n,
+                   "d": w.d, "window": w.window, "rho": w.rho,
+                   "k_sel": int(T.logo_target_count(w.rho, w.n)), "seed": args.seed,
+                   "parallelism": "none (1 GPU)"},
+        "pct_of_bf16_peak": round(100.0 * tflops / BF16_PEAK_TFLOPS, 2),
+        "effective_flops": F["total"],
+        "stage_ms_avg": {s: (round(x, 4) if x is not None else None) for s, x in avg.items()},
+        "roofline": {
+            "kernel": f"attn_bf16_kernel ({dom} branch, fused epilogue)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2) if achieved else None,
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / BF16_PEAK_TFLOPS, 4) if achieved else None,
+            "traffic": traffic,
+            "algorithmic_flops_per_launch": dom_flops,
+            "avg_launch_ms": round(dom_ms, 4) if dom_ms else None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, inp, idx, budget_s=args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
