@@ -26,9 +26,9 @@
 //   O^T[32 d x 32 queries] += V^T(32 x 16 keys) * P^T(16 keys x 32 queries)
 //     B = the probabilities straight from the S^T accumulator (converted to
 //     bf16); the contraction order over keys is permuted so each lane's own
-//     8 scores form its B operand, and V^T is read from LDS in the same key
-//     order. V^T is produced by transposing 4x8 blocks in registers while
-//     staging V (global V is [key][d]).
+//     8 scores form its B operand. A = V^T comes from the row-major V tile
+//     in LDS through the gfx950 transposing LDS read (ds_read_b64_tr_b16),
+//     which hands each lane 4 consecutive keys of its own d column.
 //
 // Workgroup order is XCD-aware: workgroup ids are dealt to the 8 XCDs in
 // turn, so logical tiles are renumbered so each XCD walks a contiguous
@@ -51,13 +51,17 @@ constexpr int kKeys = 64;     // keys per tile
 constexpr int kNumXcd = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInit = -1.0e30f;
+constexpr float kLazy = 8.0f;  // log2 headroom before the running max moves
 
 template <int D>
 struct Smem {
-  static constexpr int kStride = D + 8;        // bf16 per K row (16 B pad)
-  static constexpr int vStride = kKeys + 4;    // bf16 per V^T row (8 B pad)
+  // Row strides (bf16): K rows 16 B of pad (stride = 4 mod 32 banks) keep
+  // the 16-byte operand reads conflict-free; V rows 32 B of pad (stride =
+  // 8 mod 32 banks) keep the transposing 8-byte reads conflict-free.
+  static constexpr int kStride = D + 8;
+  static constexpr int vStride = D + 16;
   static constexpr int kElems = kKeys * kStride;
-  static constexpr int vElems = D * vStride;
+  static constexpr int vElems = kKeys * vStride;
   static constexpr int stage = kElems + vElems;
   static constexpr int bytes = 2 * stage * 2;  // two stages, 2 B each
 };
@@ -91,7 +95,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 template <int D, bool GLOBAL, int EPI>
-__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
+__global__ __launch_bounds__(kThreads, 2)
+__attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   using SM = Smem<D>;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
@@ -181,64 +186,63 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
     }
   }
 
-  // ---- staging of K / V^T tiles ----------------------------------------
-  constexpr int KCH = kKeys * D / 8 / kThreads;   // 16-B K chunks per thread
-  constexpr int VBLK = (kKeys / 4) * (D / 8);     // 4x8 V blocks per tile
-  uint4 kpre[KCH];
-  uint4 vpre[4];
-  const bool v_thread = tid < VBLK;
-  const int v_dg = tid % (D / 8);
-  const int v_kg = tid / (D / 8);
+  // ---- staging of K / V tiles ------------------------------------------
+  // Both are copied row-major in 16-byte chunks through registers. Rows past
+  // the end are clamped to the last key: such keys only occur in tiles that
+  // are masked per element (they lie after every query), so their scores
+  // are discarded and their values are finite. The loads have no branches,
+  // so they stay in flight across the tile's matrix work.
+  constexpr int KCH = kKeys * D / 8 / kThreads;   // 16-B chunks per thread: 2 or 4
+  static_assert(KCH == 2 || KCH == 4, "staging assumes 2 or 4 chunks per thread");
+  constexpr int kRowStep = kThreads / (D / 8);    // rows between a thread's chunks
+  uint4 kp0, kp1, kp2, kp3, vp0, vp1, vp2, vp3;
+  const int st_row0 = tid / (D / 8);
+  const int st_col = (tid % (D / 8)) * 8;
+  const uint16_t* kg_thread = kg + st_col;
+  const uint16_t* vg_thread = vg + st_col;
+  uint16_t* ks_thread = smem + st_row0 * SM::kStride + st_col;
+  uint16_t* vs_thread = smem + SM::kElems + st_row0 * SM::vStride + st_col;
+  const int last_key = p.n - 1;
 
-  auto load_tile = [&](int t) {
-    const int key0 = t * kKeys;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * kThreads;
-      const int row = c / (D / 8);
-      const int c8 = c % (D / 8);
-      const int key = key0 + row;
-      kpre[i] = key < p.n ? *reinterpret_cast<const uint4*>(kg + (size_t)key * D + c8 * 8)
-                          : make_uint4(0, 0, 0, 0);
-    }
-    if (v_thread) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = key0 + v_kg * 4 + r;
-        vpre[r] = key < p.n ? *reinterpret_cast<const uint4*>(vg + (size_t)key * D + v_dg * 8)
-                            : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto store_tile = [&](int stage) {
-    uint16_t* ks = smem + stage * SM::stage;
-    uint16_t* vs = ks + SM::kElems;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * kThreads;
-      const int row = c / (D / 8);
-      const int c8 = c % (D / 8);
-      *reinterpret_cast<uint4*>(ks + row * SM::kStride + c8 * 8) = kpre[i];
-    }
-    if (v_thread) {
-      // rows r0..r3 (keys), dwords m (d pairs 2m, 2m+1) -> V^T rows d, 4 keys each
-      const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&vpre[0]);
-      const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&vpre[1]);
-      const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&vpre[2]);
-      const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&vpre[3]);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        uint2 even, odd;
-        even.x = (r0[m] & 0xffffu) | (r1[m] << 16);
-        even.y = (r2[m] & 0xffffu) | (r3[m] << 16);
-        odd.x = (r0[m] >> 16) | (r1[m] & 0xffff0000u);
-        odd.y = (r2[m] >> 16) | (r3[m] & 0xffff0000u);
-        const int d0 = v_dg * 8 + 2 * m;
-        *reinterpret_cast<uint2*>(vs + d0 * SM::vStride + v_kg * 4) = even;
-        *reinterpret_cast<uint2*>(vs + (d0 + 1) * SM::vStride + v_kg * 4) = odd;
-      }
-    }
-  };
+#define LOGO_ROW(I_) ((size_t)min(key0_ + st_row0 + (I_) * kRowStep, last_key) * D)
+#define LOGO_LOAD_TILE(T_)                                                          \
+  do {                                                                              \
+    const int key0_ = (T_) * kKeys;                                                 \
+    kp0 = *reinterpret_cast<const uint4*>(kg_thread + LOGO_ROW(0));                 \
+    vp0 = *reinterpret_cast<const uint4*>(vg_thread + LOGO_ROW(0));                 \
+    kp1 = *reinterpret_cast<const uint4*>(kg_thread + LOGO_ROW(1));                 \
+    vp1 = *reinterpret_cast<const uint4*>(vg_thread + LOGO_ROW(1));                 \
+    if constexpr (KCH == 4) {                                                       \
+      kp2 = *reinterpret_cast<const uint4*>(kg_thread + LOGO_ROW(2));               \
+      vp2 = *reinterpret_cast<const uint4*>(vg_thread + LOGO_ROW(2));               \
+      kp3 = *reinterpret_cast<const uint4*>(kg_thread + LOGO_ROW(3));               \
+      vp3 = *reinterpret_cast<const uint4*>(vg_thread + LOGO_ROW(3));               \
+    }                                                                               \
+  } while (0)
+
+#define LOGO_STORE_TILE(STAGE_)                                                     \
+  do {                                                                              \
+    const int off_ = (STAGE_) * SM::stage;                                          \
+    *reinterpret_cast<uint4*>(ks_thread + off_) = kp0;                              \
+    *reinterpret_cast<uint4*>(vs_thread + off_) = vp0;                              \
+    *reinterpret_cast<uint4*>(ks_thread + off_ + kRowStep * SM::kStride) = kp1;     \
+    *reinterpret_cast<uint4*>(vs_thread + off_ + kRowStep * SM::vStride) = vp1;     \
+    if constexpr (KCH == 4) {                                                       \
+      *reinterpret_cast<uint4*>(ks_thread + off_ + 2 * kRowStep * SM::kStride) = kp2; \
+      *reinterpret_cast<uint4*>(vs_thread + off_ + 2 * kRowStep * SM::vStride) = vp2; \
+      *reinterpret_cast<uint4*>(ks_thread + off_ + 3 * kRowStep * SM::kStride) = kp3; \
+      *reinterpret_cast<uint4*>(vs_thread + off_ + 3 * kRowStep * SM::vStride) = vp3; \
+    }                                                                               \
+  } while (0)
+
+  // Transposing V reads (ds_read_b64_tr_b16). Within each 16-lane group the
+  // instruction gives destination lane 4q+j, element e, the element j of the
+  // 8 bytes addressed by source lane 4e+q. Source lane s of group G = l/16
+  // therefore addresses key row (s/4) and d columns 16*(G%2) + 4*(s%4): the
+  // destination lane then holds 4 consecutive keys for its own d column,
+  // d = l % 32 of the 32-wide block, as the MFMA A operand needs.
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
 
   // ---- online softmax state --------------------------------------------
   constexpr int DB = D / 32;  // 32-wide d blocks of the output
@@ -249,8 +253,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   float l_run = 0.0f;
 
   if (t_lo <= t_hi) {
-    load_tile(t_lo);
-    store_tile(0);
+    LOGO_LOAD_TILE(t_lo);
+    LOGO_STORE_TILE(0);
   }
   __syncthreads();
 
@@ -258,24 +262,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   for (int t = t_lo; t <= t_hi; ++t) {
     const int stage = (t - t_lo) & 1;
     const bool more = t < t_hi;
-    if (more) load_tile(t + 1);
+    // unconditional (rows clamped): a branch here would make the compiler
+    // wait for these loads before the tile's matrix work
+    LOGO_LOAD_TILE(t + 1);
 
     const int key0 = t * kKeys;
     const bool active = wave_on && key0 <= wkey_hi && key0 + kKeys - 1 >= wkey_lo;
-    if (active) {
+    if (__builtin_amdgcn_readfirstlane(active)) {  // uniform per wave
       const uint16_t* ks = smem + stage * SM::stage;
       const uint16_t* vs = ks + SM::kElems;
-      // S^T = K Q^T for two 32-key blocks
+      // S^T = K Q^T for two 32-key blocks; each block's K fragments are all
+      // requested from LDS before its MFMA chain starts
       f32x16 sc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        sc[kb] = (f32x16){};
         const uint16_t* krow = ks + (kb * 32 + col) * SM::kStride + half * 8;
+        bf16x8 kf[QS];
 #pragma unroll
-        for (int s = 0; s < QS; ++s) {
-          bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + s * 16));
-          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], sc[kb], 0, 0, 0);
-        }
+        for (int s = 0; s < QS; ++s)
+          kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + s * 16));
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qreg[0], (f32x16){}, 0, 0, 0);
+#pragma unroll
+        for (int s = 1; s < QS; ++s)
+          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qreg[s], sc[kb], 0, 0, 0);
       }
       // mask only where some row of this wave sees an invalid key here
       bool full;
@@ -284,26 +293,38 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
       } else {
         full = key0 >= wpos_hi - p.W + 1 && key0 + kKeys - 1 <= wpos_lo;
       }
-      float mx = kNegInit;
+      if (!full) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float x = sc[kb][e] * p.scale_log2;
-          if (!full) {
+          for (int e = 0; e < 16; ++e) {
             const int key = key0 + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
             bool ok = key <= pos;
             if (!GLOBAL) ok = ok && key >= pos - p.W + 1;
-            x = ok ? x : -INFINITY;
+            sc[kb][e] = ok ? sc[kb][e] : -INFINITY;
           }
-          sc[kb][e] = x;
-          mx = fmaxf(mx, x);
         }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+      // raw row max; the scale (> 0) is folded into the exponent below
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * p.scale_log2;
+      // Lazy rescaling: the running max m_run (log2 units) only moves when a
+      // row's new max exceeds it by more than kLazy, so probabilities stay
+      // below 2^kLazy and the output is rescaled only on those tiles.
+      const bool grow = mx > m_run + kLazy;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float m_new = grow ? mx : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc_o[db] *= alpha;
+      }
+      const float neg_m = -m_run;
       float lsum = 0.0f;
       bf16x8 pb16[2][2];
 #pragma unroll
@@ -311,7 +332,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
         float pv[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          pv[e] = __builtin_amdgcn_exp2f(sc[kb][e] - m_new);
+          pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], p.scale_log2, neg_m));
           lsum += pv[e];
         }
 #pragma unroll
@@ -324,26 +345,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
           pb16[kb][hh] = __builtin_bit_cast(bf16x8, packed);
         }
       }
-      l_run = l_run * alpha + lsum;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc_o[db] *= alpha;
-      // O^T += V^T P^T, 4 steps of 16 keys
+      l_run += lsum;
+      // O^T += V^T P^T, 4 steps of 16 keys per 32-wide d block. Step st
+      // covers keys kb*32 + hh*16 + [0, 16); this lane's half supplies keys
+      // +4*half+[0,4) and +8+4*half+[0,4), matching its probabilities.
+      typedef short v4i16 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const uint16_t* vrow = vs + (db * 32 + col) * SM::vStride + half * 4;
+        bf16x8 vf[4];
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-          const int kb = st >> 1, hh = st & 1;
-          const int k0 = kb * 32 + hh * 16;
-          uint2 lo = *reinterpret_cast<const uint2*>(vrow + k0);
-          uint2 hi = *reinterpret_cast<const uint2*>(vrow + k0 + 8);
-          uint4 a4 = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, a4), pb16[kb][hh], acc_o[db], 0, 0, 0);
+          const int kbase = (st >> 1) * 32 + (st & 1) * 16 + half * 4 + tr_row;
+          const uint16_t* a0 = vs + kbase * SM::vStride + db * 32 + tr_col;
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(a0));
+          const v4i16 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(a0 + 8 * SM::vStride));
+          const uint2 l2 = __builtin_bit_cast(uint2, lo);
+          const uint2 h2 = __builtin_bit_cast(uint2, hi);
+          vf[st] = __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
         }
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st], pb16[st >> 1][st & 1],
+                                                              acc_o[db], 0, 0, 0);
       }
     }
-    if (more) store_tile(stage ^ 1);
+    if (more) LOGO_STORE_TILE(stage ^ 1);
     __syncthreads();
   }
 
@@ -386,6 +414,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
     }
   }
 }
+
+#undef LOGO_ROW
+#undef LOGO_LOAD_TILE
+#undef LOGO_STORE_TILE
 
 template <int D, bool GLOBAL, int EPI>
 hipError_t launch_one(const Params& prm, hipStream_t s) {
