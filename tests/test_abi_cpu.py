@@ -138,3 +138,12 @@ def test_profile_end_argument_check(L):
     assert L.logo_profile_begin() == 0
     assert L.logo_profile_end(None, None, 4) == _lib.LOGO_ERR_INVALID_ARG
     assert L.logo_profile_end(None, None, 0) == 0
+
+
+def test_no_undefined_kernel_stubs(L):
+    """Every kernel launch stub is defined in the library: a device-only
+    construct that fails on the host compile pass can otherwise drop a stub
+    silently and leave the library unloadable on the GPU side."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    assert "device_stub" not in out, [l for l in out.splitlines() if "device_stub" in l]

@@ -52,18 +52,24 @@ constexpr int kNumXcd = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInit = -1.0e30f;
 constexpr float kLazy = 8.0f;  // log2 headroom before the running max moves
+// s_waitcnt immediate for vmcnt(0) with expcnt/lgkmcnt left alone (gfx9 encoding)
+constexpr int kWaitVm0 = 0x0F70;
 
 template <int D>
 struct Smem {
-  // Row strides (bf16): K rows 16 B of pad (stride = 4 mod 32 banks) keep
-  // the 16-byte operand reads conflict-free; V rows 32 B of pad (stride =
-  // 8 mod 32 banks) keep the transposing 8-byte reads conflict-free.
-  static constexpr int kStride = D + 8;
-  static constexpr int vStride = D + 16;
+  // Tiles are filled by bounds-checked buffer loads that write LDS
+  // directly: one instruction moves 64 lanes x 16 B into 1 KiB of
+  // consecutive LDS. A tile of 64 rows is laid out as 64 x kChunks 16-byte
+  // slots, the last slot(s) of each row being padding, so kChunks
+  // instructions fill a tile exactly. Row strides in bf16: K rows carry 16 B
+  // of pad (stride = 4 mod 32 banks: conflict-free 16-byte operand reads),
+  // V rows 32 B (stride = 8 mod 32 banks: conflict-free transposing reads).
+  static constexpr int kChunks = D / 8 + 1;
+  static constexpr int vChunks = D / 8 + 2;
+  static constexpr int kStride = kChunks * 8;
+  static constexpr int vStride = vChunks * 8;
   static constexpr int kElems = kKeys * kStride;
   static constexpr int vElems = kKeys * vStride;
-  static constexpr int stage = kElems + vElems;
-  static constexpr int bytes = 2 * stage * 2;  // two stages, 2 B each
 };
 
 struct Params {
@@ -94,11 +100,39 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Wave `wave` issues its share (instructions j = wave, wave+4, ...) of the
+// NCH buffer-load-to-LDS instructions that fill one tile: lane l of
+// instruction j moves 16 bytes from byte voff[i] + soff of the buffer
+// [base, base + nbytes) to LDS byte 1024*j + 16*l of dst. Offsets at or past
+// nbytes read as zero (hardware bounds check), so rows past the end of the
+// sequence need no clamping. The buffer resource is built here: its type
+// is device-only and must not appear where the host pass compiles the
+// kernel's signature or lambdas.
+template <int NJ, int NCH>
+__device__ __forceinline__ void issue_tile(const uint16_t* base, int nbytes, uint16_t* dst,
+                                           const uint32_t* voff, int soff, int wave) {
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(base), (short)0, nbytes, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < NJ; ++i) {
+    const int j = wave + kWaves * i;
+    if (j < NCH)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)(dst + j * 512), 16, voff[i], soff,
+                                               0, 0);
+  }
+}
+
 template <int D, bool GLOBAL, int EPI>
 __global__ __launch_bounds__(kThreads, 2)
 __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   using SM = Smem<D>;
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  // Four distinct LDS objects, so the compiler can tell that reads of one
+  // buffer do not wait on buffer loads still landing in another.
+  __shared__ __attribute__((aligned(16))) uint16_t K0[SM::kElems];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[SM::kElems];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[SM::vElems];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[SM::vElems];
 
   // ---- which tile -------------------------------------------------------
   const int bid = blockIdx.x;
@@ -169,8 +203,12 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   const int t_hi = gkey_hi / kKeys;
 
   const size_t kv_base = (size_t)(b * p.Hkv + hk) * p.n * D;
-  const uint16_t* kg = p.k + kv_base;
-  const uint16_t* vg = p.v + kv_base;
+  // This (b, kv head)'s K and V, read through bounds-checked buffer loads:
+  // keys past the end read as zero (they only occur in tiles masked per
+  // element, after every query of the tile).
+  const int kv_bytes = p.n * D * 2;
+  const uint16_t* const kg = p.k + kv_base;
+  const uint16_t* const vg = p.v + kv_base;
 
   // ---- Q rows into registers -------------------------------------------
   constexpr int QS = D / 16;  // k-steps of 16 along d
@@ -186,54 +224,32 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
     }
   }
 
-  // ---- staging of K / V tiles ------------------------------------------
-  // Both are copied row-major in 16-byte chunks through registers. Rows past
-  // the end are clamped to the last key: such keys only occur in tiles that
-  // are masked per element (they lie after every query), so their scores
-  // are discarded and their values are finite. The loads have no branches,
-  // so they stay in flight across the tile's matrix work.
-  constexpr int KCH = kKeys * D / 8 / kThreads;   // 16-B chunks per thread: 2 or 4
-  static_assert(KCH == 2 || KCH == 4, "staging assumes 2 or 4 chunks per thread");
-  constexpr int kRowStep = kThreads / (D / 8);    // rows between a thread's chunks
-  uint4 kp0, kp1, kp2, kp3, vp0, vp1, vp2, vp3;
-  const int st_row0 = tid / (D / 8);
-  const int st_col = (tid % (D / 8)) * 8;
-  const uint16_t* kg_thread = kg + st_col;
-  const uint16_t* vg_thread = vg + st_col;
-  uint16_t* ks_thread = smem + st_row0 * SM::kStride + st_col;
-  uint16_t* vs_thread = smem + SM::kElems + st_row0 * SM::vStride + st_col;
-  const int last_key = p.n - 1;
-
-#define LOGO_ROW(I_) ((size_t)min(key0_ + st_row0 + (I_) * kRowStep, last_key) * D)
-#define LOGO_LOAD_TILE(T_)                                                          \
-  do {                                                                              \
-    const int key0_ = (T_) * kKeys;                                                 \
-    kp0 = *reinterpret_cast<const uint4*>(kg_thread + LOGO_ROW(0));                 \
-    vp0 = *reinterpret_cast<const uint4*>(vg_thread + LOGO_ROW(0));                 \
-    kp1 = *reinterpret_cast<const uint4*>(kg_thread + LOGO_ROW(1));                 \
-    vp1 = *reinterpret_cast<const uint4*>(vg_thread + LOGO_ROW(1));                 \
-    if constexpr (KCH == 4) {                                                       \
-      kp2 = *reinterpret_cast<const uint4*>(kg_thread + LOGO_ROW(2));               \
-      vp2 = *reinterpret_cast<const uint4*>(vg_thread + LOGO_ROW(2));               \
-      kp3 = *reinterpret_cast<const uint4*>(kg_thread + LOGO_ROW(3));               \
-      vp3 = *reinterpret_cast<const uint4*>(vg_thread + LOGO_ROW(3));               \
-    }                                                                               \
-  } while (0)
-
-#define LOGO_STORE_TILE(STAGE_)                                                     \
-  do {                                                                              \
-    const int off_ = (STAGE_) * SM::stage;                                          \
-    *reinterpret_cast<uint4*>(ks_thread + off_) = kp0;                              \
-    *reinterpret_cast<uint4*>(vs_thread + off_) = vp0;                              \
-    *reinterpret_cast<uint4*>(ks_thread + off_ + kRowStep * SM::kStride) = kp1;     \
-    *reinterpret_cast<uint4*>(vs_thread + off_ + kRowStep * SM::vStride) = vp1;     \
-    if constexpr (KCH == 4) {                                                       \
-      *reinterpret_cast<uint4*>(ks_thread + off_ + 2 * kRowStep * SM::kStride) = kp2; \
-      *reinterpret_cast<uint4*>(vs_thread + off_ + 2 * kRowStep * SM::vStride) = vp2; \
-      *reinterpret_cast<uint4*>(ks_thread + off_ + 3 * kRowStep * SM::kStride) = kp3; \
-      *reinterpret_cast<uint4*>(vs_thread + off_ + 3 * kRowStep * SM::vStride) = vp3; \
-    }                                                                               \
-  } while (0)
+  // ---- tile staging: buffer loads straight into LDS ----------------------
+  // Wave w issues the tile's instructions j = w, w+4, ...; lane l of
+  // instruction j fills slot j*64 + l = (row, chunk). Padding slots read an
+  // out-of-range offset (zero, no fault).
+  constexpr int KJ = (SM::kChunks + kWaves - 1) / kWaves;  // instructions per wave
+  constexpr int VJ = (SM::vChunks + kWaves - 1) / kWaves;
+  constexpr uint32_t kPadOff = 0x40000000u;
+  uint32_t k_voff[KJ], v_voff[VJ];
+#pragma unroll
+  for (int i = 0; i < KJ; ++i) {
+    const int slot = (wave + kWaves * i) * 64 + lane;
+    const int row = slot / SM::kChunks, chunk = slot % SM::kChunks;
+    k_voff[i] = chunk < D / 8 ? (uint32_t)(row * D * 2 + chunk * 16) : kPadOff;
+  }
+#pragma unroll
+  for (int i = 0; i < VJ; ++i) {
+    const int slot = (wave + kWaves * i) * 64 + lane;
+    const int row = slot / SM::vChunks, chunk = slot % SM::vChunks;
+    v_voff[i] = chunk < D / 8 ? (uint32_t)(row * D * 2 + chunk * 16) : kPadOff;
+  }
+  auto issue_k = [&] __device__ (int t, uint16_t* dst) {
+    issue_tile<KJ, SM::kChunks>(kg, kv_bytes, dst, k_voff, t * kKeys * D * 2, wave);
+  };
+  auto issue_v = [&] __device__ (int t, uint16_t* dst) {
+    issue_tile<VJ, SM::vChunks>(vg, kv_bytes, dst, v_voff, t * kKeys * D * 2, wave);
+  };
 
   // Transposing V reads (ds_read_b64_tr_b16). Within each 16-lane group the
   // instruction gives destination lane 4q+j, element e, the element j of the
@@ -244,139 +260,186 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   const int tr_row = (lane & 15) >> 2;
   const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
 
-  // ---- online softmax state --------------------------------------------
+  // ---- per-tile pieces ---------------------------------------------------
   constexpr int DB = D / 32;  // 32-wide d blocks of the output
   f32x16 acc_o[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc_o[i] = (f32x16){};
-  float m_run = kNegInit;
-  float l_run = 0.0f;
+  float m_run = kNegInit;   // running row max, log2 units (per lane = per row)
+  float l_run = 0.0f;       // this lane's half of the row sum
 
-  if (t_lo <= t_hi) {
-    LOGO_LOAD_TILE(t_lo);
-    LOGO_STORE_TILE(0);
-  }
-  __syncthreads();
-
-#pragma unroll 1
-  for (int t = t_lo; t <= t_hi; ++t) {
-    const int stage = (t - t_lo) & 1;
-    const bool more = t < t_hi;
-    // unconditional (rows clamped): a branch here would make the compiler
-    // wait for these loads before the tile's matrix work
-    LOGO_LOAD_TILE(t + 1);
-
+  auto is_active = [&] __device__ (int t) {
     const int key0 = t * kKeys;
-    const bool active = wave_on && key0 <= wkey_hi && key0 + kKeys - 1 >= wkey_lo;
-    if (__builtin_amdgcn_readfirstlane(active)) {  // uniform per wave
-      const uint16_t* ks = smem + stage * SM::stage;
-      const uint16_t* vs = ks + SM::kElems;
-      // S^T = K Q^T for two 32-key blocks; each block's K fragments are all
-      // requested from LDS before its MFMA chain starts
+    return wave_on && key0 <= wkey_hi && key0 + kKeys - 1 >= wkey_lo;
+  };
+  auto is_full = [&] __device__ (int t) {
+    const int key0 = t * kKeys;
+    if (GLOBAL) return key0 + kKeys - 1 <= wpos_lo;
+    return key0 >= wpos_hi - p.W + 1 && key0 + kKeys - 1 <= wpos_lo;
+  };
+  // S^T = K Q^T for the two 32-key blocks of a tile
+  auto qk = [&] __device__ (const uint16_t* ks, f32x16* sc) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint16_t* krow = ks + (kb * 32 + col) * SM::kStride + half * 8;
+      bf16x8 kf[QS];
+#pragma unroll
+      for (int s = 0; s < QS; ++s)
+        kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + s * 16));
+      sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qreg[0], (f32x16){}, 0, 0, 0);
+#pragma unroll
+      for (int s = 1; s < QS; ++s)
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qreg[s], sc[kb], 0, 0, 0);
+    }
+  };
+  auto mask_tile = [&] __device__ (int t, f32x16* sc) {
+    const int key0 = t * kKeys;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = key0 + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+        bool ok = key <= pos;
+        if (!GLOBAL) ok = ok && key >= pos - p.W + 1;
+        sc[kb][e] = ok ? sc[kb][e] : -INFINITY;
+      }
+    }
+  };
+  // Row max of a tile in log2 units and the lazily moved running max: the
+  // max only moves when a row's tile max exceeds it by more than kLazy, so
+  // probabilities stay below 2^kLazy and the output is rescaled rarely.
+  auto new_max = [&] __device__ (const f32x16* sc) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                      false, false);
+    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * p.scale_log2;
+    return mx > m_run + kLazy ? mx : m_run;
+  };
+  // probabilities of a tile (bf16 operand layout) and their row sum
+  auto probs = [&] __device__ (const f32x16* sc, float m, bf16x8 (*pb)[2]) {
+    const float neg_m = -m;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float pv[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], p.scale_log2, neg_m));
+        lsum += pv[e];
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        uint4 packed;
+        packed.x = pack_bf16x2(pv[hh * 8 + 0], pv[hh * 8 + 1]);
+        packed.y = pack_bf16x2(pv[hh * 8 + 2], pv[hh * 8 + 3]);
+        packed.z = pack_bf16x2(pv[hh * 8 + 4], pv[hh * 8 + 5]);
+        packed.w = pack_bf16x2(pv[hh * 8 + 6], pv[hh * 8 + 7]);
+        pb[kb][hh] = __builtin_bit_cast(bf16x8, packed);
+      }
+    }
+    return lsum;
+  };
+  // O^T += V^T P^T, 4 steps of 16 keys per 32-wide d block. Step st covers
+  // keys kb*32 + hh*16 + [0, 16); this lane's half supplies keys
+  // +4*half+[0,4) and +8+4*half+[0,4), matching its probabilities.
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
+  auto pv_tile = [&] __device__ (const uint16_t* vs, bf16x8 (*pb)[2]) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      bf16x8 vf[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int kbase = (st >> 1) * 32 + (st & 1) * 16 + half * 4 + tr_row;
+        const uint16_t* a0 = vs + kbase * SM::vStride + db * 32 + tr_col;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(a0));
+        const v4i16 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(a0 + 8 * SM::vStride));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo);
+        const uint2 h2 = __builtin_bit_cast(uint2, hi);
+        vf[st] = __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+      }
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st], pb[st >> 1][st & 1],
+                                                            acc_o[db], 0, 0, 0);
+    }
+  };
+
+  // ---- software-pipelined main loop --------------------------------------
+  // Iteration t: PV of tile t (its probabilities were made in iteration t-1)
+  // overlaps the QK and softmax of tile t+1. K is staged one tile ahead of
+  // V: during iteration t, K(t+2) and V(t+1) stream into the buffers that
+  // K(t) and V(t-1) left free. One barrier per iteration.
+  bf16x8 pcur[2][2];
+  bool act_cur = false;
+  if (t_lo <= t_hi) {
+    issue_k(t_lo, K0);
+    issue_v(t_lo, V0);
+    if (t_lo + 1 <= t_hi) issue_k(t_lo + 1, K1);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    act_cur = __builtin_amdgcn_readfirstlane(is_active(t_lo));
+    if (act_cur) {
       f32x16 sc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const uint16_t* krow = ks + (kb * 32 + col) * SM::kStride + half * 8;
-        bf16x8 kf[QS];
-#pragma unroll
-        for (int s = 0; s < QS; ++s)
-          kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + s * 16));
-        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qreg[0], (f32x16){}, 0, 0, 0);
-#pragma unroll
-        for (int s = 1; s < QS; ++s)
-          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qreg[s], sc[kb], 0, 0, 0);
-      }
-      // mask only where some row of this wave sees an invalid key here
-      bool full;
-      if (GLOBAL) {
-        full = key0 + kKeys - 1 <= wpos_lo;
-      } else {
-        full = key0 >= wpos_hi - p.W + 1 && key0 + kKeys - 1 <= wpos_lo;
-      }
-      if (!full) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = key0 + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-            bool ok = key <= pos;
-            if (!GLOBAL) ok = ok && key >= pos - p.W + 1;
-            sc[kb][e] = ok ? sc[kb][e] : -INFINITY;
-          }
-        }
-      }
-      // raw row max; the scale (> 0) is folded into the exponent below
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * p.scale_log2;
-      // Lazy rescaling: the running max m_run (log2 units) only moves when a
-      // row's new max exceeds it by more than kLazy, so probabilities stay
-      // below 2^kLazy and the output is rescaled only on those tiles.
-      const bool grow = mx > m_run + kLazy;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float m_new = grow ? mx : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
+      qk(K0, sc);
+      if (!is_full(t_lo)) mask_tile(t_lo, sc);
+      m_run = new_max(sc);
+      l_run = probs(sc, m_run, pcur);
+    }
+  }
+  // One iteration; the buffers are compile-time distinct objects at every
+  // call site (the loop is unrolled by two), which keeps the LDS reads
+  // below free of waits on the buffer loads issued at its top.
+  auto step = [&] __device__ (int t, const uint16_t* k_next, const uint16_t* v_cur, uint16_t* k_fill,
+                  uint16_t* v_fill) {
+    if (t + 1 <= t_hi) issue_v(t + 1, v_fill);
+    if (t + 2 <= t_hi) issue_k(t + 2, k_fill);
+    const bool act_next =
+        (t + 1 <= t_hi) && __builtin_amdgcn_readfirstlane(is_active(t + 1));
+    bf16x8 pnext[2][2];
+    if (act_next) {
+      f32x16 sc[2];
+      qk(k_next, sc);
+      if (!is_full(t + 1)) mask_tile(t + 1, sc);
+      const float m_new = new_max(sc);
+      const float lsum = probs(sc, m_new, pnext);
+      if (act_cur) pv_tile(v_cur, pcur);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run = l_run * alpha + lsum;
+      if (__builtin_amdgcn_ballot_w64(m_new != m_run) != 0) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc_o[db] *= alpha;
       }
-      const float neg_m = -m_run;
-      float lsum = 0.0f;
-      bf16x8 pb16[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float pv[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], p.scale_log2, neg_m));
-          lsum += pv[e];
-        }
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          uint4 packed;
-          packed.x = pack_bf16x2(pv[hh * 8 + 0], pv[hh * 8 + 1]);
-          packed.y = pack_bf16x2(pv[hh * 8 + 2], pv[hh * 8 + 3]);
-          packed.z = pack_bf16x2(pv[hh * 8 + 4], pv[hh * 8 + 5]);
-          packed.w = pack_bf16x2(pv[hh * 8 + 6], pv[hh * 8 + 7]);
-          pb16[kb][hh] = __builtin_bit_cast(bf16x8, packed);
-        }
-      }
-      l_run += lsum;
-      // O^T += V^T P^T, 4 steps of 16 keys per 32-wide d block. Step st
-      // covers keys kb*32 + hh*16 + [0, 16); this lane's half supplies keys
-      // +4*half+[0,4) and +8+4*half+[0,4), matching its probabilities.
-      typedef short v4i16 __attribute__((ext_vector_type(4)));
-      typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        bf16x8 vf[4];
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const int kbase = (st >> 1) * 32 + (st & 1) * 16 + half * 4 + tr_row;
-          const uint16_t* a0 = vs + kbase * SM::vStride + db * 32 + tr_col;
-          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(a0));
-          const v4i16 hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(a0 + 8 * SM::vStride));
-          const uint2 l2 = __builtin_bit_cast(uint2, lo);
-          const uint2 h2 = __builtin_bit_cast(uint2, hi);
-          vf[st] = __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
-        }
-#pragma unroll
-        for (int st = 0; st < 4; ++st)
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st], pb16[st >> 1][st & 1],
-                                                              acc_o[db], 0, 0, 0);
-      }
+      m_run = m_new;
+    } else if (act_cur) {
+      pv_tile(v_cur, pcur);
     }
-    if (more) LOGO_STORE_TILE(stage ^ 1);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) pcur[kb][hh] = pnext[kb][hh];
+    act_cur = act_next;
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
+  };
+  // Iteration t (counted from t_lo): tile t's V and tile t+1's K are in
+  // buffers (t-t_lo)&1 and (t+1-t_lo)&1; V(t+1) and K(t+2) are loaded into
+  // the other two.
+#pragma unroll 1
+  for (int t = t_lo; t <= t_hi; t += 2) {
+    step(t, K1, V0, K0, V1);
+    if (t + 1 <= t_hi) step(t + 1, K0, V1, K1, V0);
   }
 
   // ---- epilogue ----------------------------------------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
+                                                     __float_as_uint(l_run), false, false);
+  const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
   if (!row_ok) return;
   const float inv = 1.0f / l_tot;
   const size_t head_row = (size_t)(b * p.Hq + h);
@@ -415,20 +478,11 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   }
 }
 
-#undef LOGO_ROW
-#undef LOGO_LOAD_TILE
-#undef LOGO_STORE_TILE
-
 template <int D, bool GLOBAL, int EPI>
 hipError_t launch_one(const Params& prm, hipStream_t s) {
-  // more than 64 KiB of dynamic LDS must be allowed per kernel (idempotent)
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&attn_bf16_kernel<D, GLOBAL, EPI>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, Smem<D>::bytes);
-  if (attr != hipSuccess) return attr;
   const int grid = prm.per_xcd * kNumXcd;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, GLOBAL, EPI>), dim3(grid), dim3(kThreads),
-                     Smem<D>::bytes, s, prm);
+  hipLaunchKernelGGL((attn_bf16_kernel<D, GLOBAL, EPI>), dim3(grid), dim3(kThreads), 0, s,
+                     prm);
   return hipGetLastError();
 }
 
