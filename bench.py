@@ -43,6 +43,7 @@ BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
 HBM_PEAK_GBS = 8000.0
 METRIC = "effective attn TFLOP/s + ms/layer fwd at 32K ctx, rho=0.2; % of bf16 MFMA peak"
 KERNEL_SOURCES = ["attn_bf16.hip", "select.hip", "combine.hip", "abi.cpp"]
+COPY_BYTES = 1 << 30
 
 
 def kernel_source_hash() -> str:
@@ -110,6 +111,19 @@ def load_traffic(workload: str, current_hash: str):
     return ent.get("global_bytes_per_launch")
 
 
+def copy_calibration(torch) -> int:
+    """An elementwise copy that reads and writes exactly COPY_BYTES each."""
+    n = COPY_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.add(src, 0.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                                           "launches": 3, "kernel": "torch elementwise add"}}))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +134,9 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of known size (read N, write N "
+                         "bytes) so HBM counters can be scaled to bytes")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -131,6 +148,9 @@ def main() -> int:
 
     import token_level_dynamic_amd as T
     from workloads import get_workload, make_inputs
+
+    if args.copy_calibration:
+        return copy_calibration(torch)
 
     from token_level_dynamic_amd._lib import LIB_PATH
     if not os.path.exists(LIB_PATH):

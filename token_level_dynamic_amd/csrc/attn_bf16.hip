@@ -370,6 +370,68 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
     }
   };
 
+  // The softmax of one tile (probabilities in bf16 operand layout, row-sum
+  // partial) computed in 16 slices of 2 scores, each slice issued right after
+  // one PV MFMA of the previous tile, so the exponentials run in the shadow
+  // of the matrix cores. V fragments are read one d block ahead.
+  auto probs_pv_interleaved = [&] __device__ (const f32x16* sc, float m, bf16x8 (*pb)[2],
+                                              const uint16_t* vs, bf16x8 (*pprev)[2]) {
+    const float neg_m = -m;
+    float lsum = 0.0f;
+    uint32_t packed[2][8];
+    auto read_vf = [&] __device__ (int db, bf16x8* vf) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int kbase = (st >> 1) * 32 + (st & 1) * 16 + half * 4 + tr_row;
+        const uint16_t* a0 = vs + kbase * SM::vStride + db * 32 + tr_col;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(a0));
+        const v4i16 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(a0 + 8 * SM::vStride));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo);
+        const uint2 h2 = __builtin_bit_cast(uint2, hi);
+        vf[st] = __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+      }
+    };
+    bf16x8 vf[2][4];
+    read_vf(0, vf[0]);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      if (db + 1 < DB) read_vf(db + 1, vf[(db + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db & 1][st], pprev[st >> 1][st & 1],
+                                                            acc_o[db], 0, 0, 0);
+        // slice c of the softmax: scores 2*(c%8), 2*(c%8)+1 of block c/8
+        constexpr int kSlices = 16;
+        for (int c = (db * 4 + st) * kSlices / (4 * DB); c < (db * 4 + st + 1) * kSlices / (4 * DB);
+             ++c) {
+          const int kb = c >> 3, e = (c & 7) * 2;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], p.scale_log2, neg_m));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][e + 1], p.scale_log2, neg_m));
+          lsum += p0 + p1;
+          uint32_t pk = pack_bf16x2(p0, p1);
+          // an empty asm that "reads and writes" the slice's results pins
+          // the slice here (their only uses come after a branch, where the
+          // optimiser would otherwise sink them)
+          asm volatile("" : "+v"(pk), "+v"(lsum));
+          packed[kb][e >> 1] = pk;
+        }
+        // keep this MFMA and its slice together: the scheduler would
+        // otherwise cluster all MFMAs and all exponentials apart
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        pb[kb][hh] = __builtin_bit_cast(
+            bf16x8, make_uint4(packed[kb][hh * 4 + 0], packed[kb][hh * 4 + 1],
+                               packed[kb][hh * 4 + 2], packed[kb][hh * 4 + 3]));
+    return lsum;
+  };
+
   // ---- software-pipelined main loop --------------------------------------
   // Iteration t: PV of tile t (its probabilities were made in iteration t-1)
   // overlaps the QK and softmax of tile t+1. K is staged one tile ahead of
@@ -402,7 +464,22 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
     const bool act_next =
         (t + 1 <= t_hi) && __builtin_amdgcn_readfirstlane(is_active(t + 1));
     bf16x8 pnext[2][2];
-    if (act_next) {
+    if (act_cur && act_next && is_full(t + 1)) {
+      // Common case, one basic block: QK of tile t+1, its row max, then its
+      // softmax VALU interleaved with the PV MFMAs of tile t (independent
+      // work), so the matrix cores stay busy while the exponentials run.
+      f32x16 sc[2];
+      qk(k_next, sc);
+      const float m_new = new_max(sc);
+      const float lsum = probs_pv_interleaved(sc, m_new, pnext, v_cur, pcur);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run = l_run * alpha + lsum;
+      if (__builtin_amdgcn_ballot_w64(m_new != m_run) != 0) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc_o[db] *= alpha;
+      }
+      m_run = m_new;
+    } else if (act_next) {
       f32x16 sc[2];
       qk(k_next, sc);
       if (!is_full(t + 1)) mask_tile(t + 1, sc);
