@@ -160,47 +160,21 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   const int pb = (wave_on ? u : u_last) / G;
   const int h = hk * G + (wave_on ? u : u_last) % G;
 
-  // Row positions of this lane and the wave's / workgroup's key range.
+  auto row_pos = [&] __device__ (int r) __attribute__((always_inline)) {
+    return GLOBAL ? p.idx[(size_t)b * p.ksel + r] : r;
+  };
+  // Row of this lane and the wave's / workgroup's key range.
   const int r_lane = pb * kRows + col;
   const bool row_ok = wave_on && r_lane < R;
-  int pos;
-  if (GLOBAL) {
-    pos = (r_lane < R) ? p.idx[(size_t)b * p.ksel + r_lane] : -1;
-  } else {
-    pos = r_lane;
-  }
-  const int r_first = pb * kRows;
-  const int r_last = min(pb * kRows + kRows, R) - 1;
-  // positions of this wave's first and last real rows (ascending in rows)
-  int wpos_lo, wpos_hi;
-  if (GLOBAL) {
-    wpos_lo = p.idx[(size_t)b * p.ksel + r_first];
-    wpos_hi = p.idx[(size_t)b * p.ksel + r_last];
-  } else {
-    wpos_lo = r_first;
-    wpos_hi = r_last;
-  }
+  const int pos = r_lane < R ? row_pos(r_lane) : -1;
+  const int wpos_lo = row_pos(pb * kRows);                 // rows ascend
+  const int wpos_hi = row_pos(min(pb * kRows + kRows, R) - 1);
   const int wkey_lo = GLOBAL ? 0 : max(0, wpos_lo - p.W + 1);
   const int wkey_hi = wpos_hi;
-  // workgroup range: first unit's first row to last unit's last row
-  const int pb_first = u_first / G;
-  const int pb_last = u_last / G;
-  int gpos_lo, gpos_hi;
-  {
-    const int rf = pb_first * kRows;
-    const int rl = min(pb_last * kRows + kRows, R) - 1;
-    if (GLOBAL) {
-      gpos_lo = p.idx[(size_t)b * p.ksel + rf];
-      gpos_hi = p.idx[(size_t)b * p.ksel + rl];
-    } else {
-      gpos_lo = rf;
-      gpos_hi = rl;
-    }
-  }
-  const int gkey_lo = GLOBAL ? 0 : max(0, gpos_lo - p.W + 1);
-  const int gkey_hi = gpos_hi;
-  const int t_lo = gkey_lo / kKeys;
-  const int t_hi = gkey_hi / kKeys;
+  const int gpos_lo = row_pos((u_first / G) * kRows);
+  const int gpos_hi = row_pos(min((u_last / G) * kRows + kRows, R) - 1);
+  const int t_lo = (GLOBAL ? 0 : max(0, gpos_lo - p.W + 1)) / kKeys;
+  const int t_hi = gpos_hi / kKeys;
 
   const size_t kv_base = (size_t)(b * p.Hkv + hk) * p.n * D;
   // This (b, kv head)'s K and V, read through bounds-checked buffer loads:
@@ -244,11 +218,10 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
     const int row = slot / SM::vChunks, chunk = slot % SM::vChunks;
     v_voff[i] = chunk < D / 8 ? (uint32_t)(row * D * 2 + chunk * 16) : kPadOff;
   }
-  auto issue_k = [&] __device__ (int t, uint16_t* dst) {
-    issue_tile<KJ, SM::kChunks>(kg, kv_bytes, dst, k_voff, t * kKeys * D * 2, wave);
-  };
-  auto issue_v = [&] __device__ (int t, uint16_t* dst) {
-    issue_tile<VJ, SM::vChunks>(vg, kv_bytes, dst, v_voff, t * kKeys * D * 2, wave);
+  auto issue_kv = [&] __device__ (int t, uint16_t* kdst, uint16_t* vdst)
+      __attribute__((always_inline)) {
+    issue_tile<KJ, SM::kChunks>(kg, kv_bytes, kdst, k_voff, t * kKeys * D * 2, wave);
+    issue_tile<VJ, SM::vChunks>(vg, kv_bytes, vdst, v_voff, t * kKeys * D * 2, wave);
   };
 
   // Transposing V reads (ds_read_b64_tr_b16). Within each 16-lane group the
@@ -259,258 +232,182 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   // d = l % 32 of the 32-wide block, as the MFMA A operand needs.
   const int tr_row = (lane & 15) >> 2;
   const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
 
-  // ---- per-tile pieces ---------------------------------------------------
+  // ---- online softmax state ----------------------------------------------
   constexpr int DB = D / 32;  // 32-wide d blocks of the output
   f32x16 acc_o[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc_o[i] = (f32x16){};
-  float m_run = kNegInit;   // running row max, log2 units (per lane = per row)
+  float m_run = kNegInit;   // running row max, log2 units
   float l_run = 0.0f;       // this lane's half of the row sum
 
-  auto is_active = [&] __device__ (int t) {
+  auto is_active = [&] __device__ (int t) __attribute__((always_inline)) {
     const int key0 = t * kKeys;
     return wave_on && key0 <= wkey_hi && key0 + kKeys - 1 >= wkey_lo;
   };
-  auto is_full = [&] __device__ (int t) {
+  auto is_full = [&] __device__ (int t) __attribute__((always_inline)) {
     const int key0 = t * kKeys;
     if (GLOBAL) return key0 + kKeys - 1 <= wpos_lo;
     return key0 >= wpos_hi - p.W + 1 && key0 + kKeys - 1 <= wpos_lo;
   };
-  // S^T = K Q^T for the two 32-key blocks of a tile
-  auto qk = [&] __device__ (const uint16_t* ks, f32x16* sc) {
+  // V fragment for keys kb*32 + hh*16 + [0,16) of d block db (A operand of
+  // O^T += V^T P^T); this lane's half supplies keys +4*half+[0,4) and
+  // +8+4*half+[0,4), matching its probabilities.
+  auto read_vf = [&] __device__ (const uint16_t* vs, int kb, int hh, int db)
+      __attribute__((always_inline)) {
+    const int kbase = kb * 32 + hh * 16 + half * 4 + tr_row;
+    const uint16_t* a0 = vs + kbase * SM::vStride + db * 32 + tr_col;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(a0));
+    const v4i16 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(a0 + 8 * SM::vStride));
+    const uint2 l2 = __builtin_bit_cast(uint2, lo);
+    const uint2 h2 = __builtin_bit_cast(uint2, hi);
+    return __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+  };
+  // Row max of one 32-key block in log2 units, and the lazily moved running
+  // max: it only moves when the block max exceeds it by more than kLazy, so
+  // probabilities stay below 2^kLazy and the output is rescaled rarely.
+  // Returns the factor for the output accumulator (1 when unmoved).
+  auto block_max = [&] __device__ (const f32x16& s) __attribute__((always_inline)) {
+    float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const uint16_t* krow = ks + (kb * 32 + col) * SM::kStride + half * 8;
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                      false, false);
+    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * p.scale_log2;
+    const float m_new = mx > m_run + kLazy ? mx : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+    return alpha;
+  };
+  // two probabilities: exp2, partial row sum, bf16 pack
+  auto prob_pair = [&] __device__ (float s0, float s1) __attribute__((always_inline)) {
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(s0, p.scale_log2, -m_run));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(s1, p.scale_log2, -m_run));
+    l_run += p0 + p1;
+    uint32_t pk = pack_bf16x2(p0, p1);
+    // an empty asm that "reads and writes" the result pins the pair where it
+    // is written (the optimiser would otherwise cluster all exponentials)
+    asm volatile("" : "+v"(pk), "+v"(l_run));
+    return pk;
+  };
+  auto mask_block = [&] __device__ (int key0, f32x16& s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = key0 + (e >> 2) * 8 + half * 4 + (e & 3);
+      bool ok = key <= pos;
+      if (!GLOBAL) ok = ok && key >= pos - p.W + 1;
+      s[e] = ok ? s[e] : -INFINITY;
+    }
+  };
+  auto rescale = [&] __device__ (float alpha) __attribute__((always_inline)) {
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc_o[db] *= alpha;
+    }
+  };
+
+  // One tile of 64 keys as two 32-key blocks (kb), in four phases:
+  //   QK(kb0) | QK(kb1) + softmax(kb0) | PV(kb0) + softmax(kb1) | PV(kb1)
+  // so half of the MFMAs carry softmax VALU work of the other block in their
+  // shadow; the second wave of the SIMD covers the rest.
+  auto tile = [&] __device__ (int t, const uint16_t* ks, const uint16_t* vs)
+      __attribute__((always_inline)) {
+    const bool full = __builtin_amdgcn_readfirstlane(is_full(t));
+    const int key0 = t * kKeys;
+    f32x16 sc0, sc1;
+    uint32_t pk0[8], pk1[8];   // bf16 probability pairs of blocks 0 and 1
+    {
+      const uint16_t* krow = ks + col * SM::kStride + half * 8;
       bf16x8 kf[QS];
 #pragma unroll
       for (int s = 0; s < QS; ++s)
         kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + s * 16));
-      sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qreg[0], (f32x16){}, 0, 0, 0);
 #pragma unroll
-      for (int s = 1; s < QS; ++s)
-        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qreg[s], sc[kb], 0, 0, 0);
+      for (int s = 0; s < QS; ++s)
+        sc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qreg[s], s ? sc0 : (f32x16){}, 0,
+                                                       0, 0);
     }
-  };
-  auto mask_tile = [&] __device__ (int t, f32x16* sc) {
-    const int key0 = t * kKeys;
+    const uint16_t* krow1 = ks + (32 + col) * SM::kStride + half * 8;
+    bf16x8 kf1[QS];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int s = 0; s < QS; ++s)
+      kf1[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow1 + s * 16));
+    if (!full) mask_block(key0, sc0);
+    const float alpha0 = block_max(sc0);
+    __builtin_amdgcn_sched_barrier(0);
+    // QK(kb1), 8 pairs of block 0 spread over its QS MFMAs
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = key0 + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-        bool ok = key <= pos;
-        if (!GLOBAL) ok = ok && key >= pos - p.W + 1;
-        sc[kb][e] = ok ? sc[kb][e] : -INFINITY;
+    for (int s = 0; s < QS; ++s) {
+      sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1[s], qreg[s], s ? sc1 : (f32x16){}, 0, 0,
+                                                     0);
+#pragma unroll
+      for (int i = 0; i < 8 / QS; ++i) {
+        const int c = s * (8 / QS) + i;
+        pk0[c] = prob_pair(sc0[2 * c], sc0[2 * c + 1]);
       }
-    }
-  };
-  // Row max of a tile in log2 units and the lazily moved running max: the
-  // max only moves when a row's tile max exceeds it by more than kLazy, so
-  // probabilities stay below 2^kLazy and the output is rescaled rarely.
-  auto new_max = [&] __device__ (const f32x16* sc) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                      false, false);
-    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * p.scale_log2;
-    return mx > m_run + kLazy ? mx : m_run;
-  };
-  // probabilities of a tile (bf16 operand layout) and their row sum
-  auto probs = [&] __device__ (const f32x16* sc, float m, bf16x8 (*pb)[2]) {
-    const float neg_m = -m;
-    float lsum = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float pv[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], p.scale_log2, neg_m));
-        lsum += pv[e];
-      }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        uint4 packed;
-        packed.x = pack_bf16x2(pv[hh * 8 + 0], pv[hh * 8 + 1]);
-        packed.y = pack_bf16x2(pv[hh * 8 + 2], pv[hh * 8 + 3]);
-        packed.z = pack_bf16x2(pv[hh * 8 + 4], pv[hh * 8 + 5]);
-        packed.w = pack_bf16x2(pv[hh * 8 + 6], pv[hh * 8 + 7]);
-        pb[kb][hh] = __builtin_bit_cast(bf16x8, packed);
-      }
-    }
-    return lsum;
-  };
-  // O^T += V^T P^T, 4 steps of 16 keys per 32-wide d block. Step st covers
-  // keys kb*32 + hh*16 + [0, 16); this lane's half supplies keys
-  // +4*half+[0,4) and +8+4*half+[0,4), matching its probabilities.
-  typedef short v4i16 __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
-  auto pv_tile = [&] __device__ (const uint16_t* vs, bf16x8 (*pb)[2]) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      bf16x8 vf[4];
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const int kbase = (st >> 1) * 32 + (st & 1) * 16 + half * 4 + tr_row;
-        const uint16_t* a0 = vs + kbase * SM::vStride + db * 32 + tr_col;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(a0));
-        const v4i16 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(a0 + 8 * SM::vStride));
-        const uint2 l2 = __builtin_bit_cast(uint2, lo);
-        const uint2 h2 = __builtin_bit_cast(uint2, hi);
-        vf[st] = __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
-      }
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st], pb[st >> 1][st & 1],
-                                                            acc_o[db], 0, 0, 0);
-    }
-  };
-
-  // The softmax of one tile (probabilities in bf16 operand layout, row-sum
-  // partial) computed in 16 slices of 2 scores, each slice issued right after
-  // one PV MFMA of the previous tile, so the exponentials run in the shadow
-  // of the matrix cores. V fragments are read one d block ahead.
-  auto probs_pv_interleaved = [&] __device__ (const f32x16* sc, float m, bf16x8 (*pb)[2],
-                                              const uint16_t* vs, bf16x8 (*pprev)[2]) {
-    const float neg_m = -m;
-    float lsum = 0.0f;
-    uint32_t packed[2][8];
-    auto read_vf = [&] __device__ (int db, bf16x8* vf) {
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const int kbase = (st >> 1) * 32 + (st & 1) * 16 + half * 4 + tr_row;
-        const uint16_t* a0 = vs + kbase * SM::vStride + db * 32 + tr_col;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(a0));
-        const v4i16 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(a0 + 8 * SM::vStride));
-        const uint2 l2 = __builtin_bit_cast(uint2, lo);
-        const uint2 h2 = __builtin_bit_cast(uint2, hi);
-        vf[st] = __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
-      }
-    };
-    bf16x8 vf[2][4];
-    read_vf(0, vf[0]);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      if (db + 1 < DB) read_vf(db + 1, vf[(db + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db & 1][st], pprev[st >> 1][st & 1],
-                                                            acc_o[db], 0, 0, 0);
-        // slice c of the softmax: scores 2*(c%8), 2*(c%8)+1 of block c/8
-        constexpr int kSlices = 16;
-        for (int c = (db * 4 + st) * kSlices / (4 * DB); c < (db * 4 + st + 1) * kSlices / (4 * DB);
-             ++c) {
-          const int kb = c >> 3, e = (c & 7) * 2;
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], p.scale_log2, neg_m));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][e + 1], p.scale_log2, neg_m));
-          lsum += p0 + p1;
-          uint32_t pk = pack_bf16x2(p0, p1);
-          // an empty asm that "reads and writes" the slice's results pins
-          // the slice here (their only uses come after a branch, where the
-          // optimiser would otherwise sink them)
-          asm volatile("" : "+v"(pk), "+v"(lsum));
-          packed[kb][e >> 1] = pk;
-        }
-        // keep this MFMA and its slice together: the scheduler would
-        // otherwise cluster all MFMAs and all exponentials apart
-        __builtin_amdgcn_sched_barrier(0);
-      }
     }
+    rescale(alpha0);
+    if (!full) mask_block(key0 + 32, sc1);
+    const float alpha1 = block_max(sc1);
+    __builtin_amdgcn_sched_barrier(0);
+    // PV(kb0), 8 pairs of block 1 spread over its 2*DB MFMAs
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 v0 = read_vf(vs, 0, 0, db);
+      const bf16x8 v1 = read_vf(vs, 0, 1, db);
+      acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          v0, __builtin_bit_cast(bf16x8, make_uint4(pk0[0], pk0[1], pk0[2], pk0[3])), acc_o[db],
+          0, 0, 0);
+      acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          v1, __builtin_bit_cast(bf16x8, make_uint4(pk0[4], pk0[5], pk0[6], pk0[7])), acc_o[db],
+          0, 0, 0);
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-        pb[kb][hh] = __builtin_bit_cast(
-            bf16x8, make_uint4(packed[kb][hh * 4 + 0], packed[kb][hh * 4 + 1],
-                               packed[kb][hh * 4 + 2], packed[kb][hh * 4 + 3]));
-    return lsum;
+      for (int i = 0; i < 8 / DB; ++i) {
+        const int c = db * (8 / DB) + i;
+        pk1[c] = prob_pair(sc1[2 * c], sc1[2 * c + 1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // block 0's products were made before block 1 moved the max
+    rescale(alpha1);
+    // PV(kb1)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 v0 = read_vf(vs, 1, 0, db);
+      const bf16x8 v1 = read_vf(vs, 1, 1, db);
+      acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          v0, __builtin_bit_cast(bf16x8, make_uint4(pk1[0], pk1[1], pk1[2], pk1[3])), acc_o[db],
+          0, 0, 0);
+      acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          v1, __builtin_bit_cast(bf16x8, make_uint4(pk1[4], pk1[5], pk1[6], pk1[7])), acc_o[db],
+          0, 0, 0);
+    }
   };
 
-  // ---- software-pipelined main loop --------------------------------------
-  // Iteration t: PV of tile t (its probabilities were made in iteration t-1)
-  // overlaps the QK and softmax of tile t+1. K is staged one tile ahead of
-  // V: during iteration t, K(t+2) and V(t+1) stream into the buffers that
-  // K(t) and V(t-1) left free. One barrier per iteration.
-  bf16x8 pcur[2][2];
-  bool act_cur = false;
-  if (t_lo <= t_hi) {
-    issue_k(t_lo, K0);
-    issue_v(t_lo, V0);
-    if (t_lo + 1 <= t_hi) issue_k(t_lo + 1, K1);
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
-    act_cur = __builtin_amdgcn_readfirstlane(is_active(t_lo));
-    if (act_cur) {
-      f32x16 sc[2];
-      qk(K0, sc);
-      if (!is_full(t_lo)) mask_tile(t_lo, sc);
-      m_run = new_max(sc);
-      l_run = probs(sc, m_run, pcur);
-    }
-  }
-  // One iteration; the buffers are compile-time distinct objects at every
-  // call site (the loop is unrolled by two), which keeps the LDS reads
-  // below free of waits on the buffer loads issued at its top.
-  auto step = [&] __device__ (int t, const uint16_t* k_next, const uint16_t* v_cur, uint16_t* k_fill,
-                  uint16_t* v_fill) {
-    if (t + 1 <= t_hi) issue_v(t + 1, v_fill);
-    if (t + 2 <= t_hi) issue_k(t + 2, k_fill);
-    const bool act_next =
-        (t + 1 <= t_hi) && __builtin_amdgcn_readfirstlane(is_active(t + 1));
-    bf16x8 pnext[2][2];
-    if (act_cur && act_next && is_full(t + 1)) {
-      // Common case, one basic block: QK of tile t+1, its row max, then its
-      // softmax VALU interleaved with the PV MFMAs of tile t (independent
-      // work), so the matrix cores stay busy while the exponentials run.
-      f32x16 sc[2];
-      qk(k_next, sc);
-      const float m_new = new_max(sc);
-      const float lsum = probs_pv_interleaved(sc, m_new, pnext, v_cur, pcur);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run = l_run * alpha + lsum;
-      if (__builtin_amdgcn_ballot_w64(m_new != m_run) != 0) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc_o[db] *= alpha;
-      }
-      m_run = m_new;
-    } else if (act_next) {
-      f32x16 sc[2];
-      qk(k_next, sc);
-      if (!is_full(t + 1)) mask_tile(t + 1, sc);
-      const float m_new = new_max(sc);
-      const float lsum = probs(sc, m_new, pnext);
-      if (act_cur) pv_tile(v_cur, pcur);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run = l_run * alpha + lsum;
-      if (__builtin_amdgcn_ballot_w64(m_new != m_run) != 0) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc_o[db] *= alpha;
-      }
-      m_run = m_new;
-    } else if (act_cur) {
-      pv_tile(v_cur, pcur);
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) pcur[kb][hh] = pnext[kb][hh];
-    act_cur = act_next;
+  // ---- main loop: tile t computes from one buffer pair while tile t+1
+  // lands in the other. The loop is unrolled by two so every LDS access
+  // names its buffer at compile time.
+  auto step = [&] __device__ (int t, const uint16_t* ks, const uint16_t* vs, uint16_t* kn,
+                              uint16_t* vn) __attribute__((always_inline)) {
+    if (t + 1 <= t_hi) issue_kv(t + 1, kn, vn);
+    if (__builtin_amdgcn_readfirstlane(is_active(t))) tile(t, ks, vs);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
   };
-  // Iteration t (counted from t_lo): tile t's V and tile t+1's K are in
-  // buffers (t-t_lo)&1 and (t+1-t_lo)&1; V(t+1) and K(t+2) are loaded into
-  // the other two.
+  if (t_lo <= t_hi) {
+    issue_kv(t_lo, K0, V0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+  }
 #pragma unroll 1
   for (int t = t_lo; t <= t_hi; t += 2) {
-    step(t, K1, V0, K0, V1);
-    if (t + 1 <= t_hi) step(t + 1, K0, V1, K1, V0);
+    step(t, K0, V0, K1, V1);
+    if (t + 1 <= t_hi) step(t + 1, K1, V1, K0, V0);
   }
 
   // ---- epilogue ----------------------------------------------------------
