@@ -124,6 +124,29 @@ def copy_calibration(torch) -> int:
     return 0
 
 
+def per_step_timing(torch, step, stream, steps: int) -> dict:
+    """Each forward timed on its own: warm (back to back) and cold (a 1 GiB
+    device write before each forward evicts L2 and the MALL), median/min/max.
+    Runs after the contract's timed region and does not change `value`."""
+    flush = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    out = {}
+    for mode in ("warm", "cold"):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            if mode == "cold":
+                flush.fill_(1.0)
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in ev)
+        out[mode] = {"median_ms": round(float(np.median(ms)), 4), "min_ms": round(ms[0], 4),
+                     "max_ms": round(ms[-1], 4)}
+    del flush
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,6 +220,8 @@ def main() -> int:
     stage_ms, stage_n = T.logo_profile_end()
     ms_per_step = e0.elapsed_time(e1) / args.steps
 
+    per_step = per_step_timing(torch, step, stream, args.steps)
+
     idx = buf["idx"].cpu().numpy()
     F = effective_flops(w, idx)
     tflops = F["total"] / (ms_per_step * 1e-3) / 1e12
@@ -228,6 +253,7 @@ def main() -> int:
         "pct_of_bf16_peak": round(100.0 * tflops / BF16_PEAK_TFLOPS, 2),
         "effective_flops": F["total"],
         "stage_ms_avg": {s: (round(x, 4) if x is not None else None) for s, x in avg.items()},
+        "per_step_ms": per_step,
         "roofline": {
             "kernel": f"attn_bf16_kernel ({dom} branch, fused epilogue)",
             "bound": "mfma",
