@@ -25,9 +25,12 @@
  * Pointers: device pointers (hipMalloc'ed or equivalent), 16-byte aligned,
  *   owned by the caller. The library never allocates, frees or keeps device
  *   memory. Scratch space comes from the caller's workspace argument.
- * Layouts (row-major, contiguous, element strides implied by the shape):
+ * Layouts (row-major; the d elements of one row are always contiguous):
  *   q, o          [B][Hq][n][d]     dtype = problem.dtype
  *   k, v          [B][Hkv][n][d]    dtype = problem.dtype
+ *     q, k, v and o may instead be strided views: problem.q_strides etc.
+ *     give the (batch, head, token) strides in elements (see logo_problem);
+ *     all three zero means the contiguous layout above.
  *   gate          [B][n]            float32 logits
  *   mask          [B][n]            uint8, 1 = selected
  *   idx           [B][k]            int32, selected positions, ascending
@@ -43,7 +46,8 @@
  * Empty problems (B == 0 or n == 0) are valid and enqueue nothing.
  * Supported: d in {64, 128}; dtype LOGO_F32 or LOGO_BF16 (float32
  *   accumulation in both); 1 <= window; 0 <= rho <= 1; Hq % Hkv == 0;
- *   n < 2^30; B*Hq*n*d < 2^62.
+ *   n < 2^30; B*Hq*n*d < 2^62; for strided views, ((n-1)*token stride + d)
+ *   times the element size below 2^31 bytes.
  */
 #ifndef LOGO_H
 #define LOGO_H
@@ -76,6 +80,18 @@ typedef struct {
   double rho;      /* target global ratio in [0, 1]; k = ceil(rho * n)      */
   float scale;     /* score scale; 0 means 1/sqrt(d)                        */
   int32_t dtype;   /* logo_dtype of q, k, v, o                              */
+  /* Strides in elements of q, k, v and o along (batch, head, token); the d
+   * stride is 1. {0, 0, 0} selects the contiguous [B][H][n][d] layout. A
+   * set stride triple must have every stride >= 0, a token stride >= d,
+   * and every stride times the element size a multiple of 16 bytes. Inputs
+   * may overlap (a batch or head stride of 0 broadcasts); o must not: its
+   * strides, sorted, must each be at least the previous stride times that
+   * dimension's extent (LOGO_ERR_INVALID_ARG otherwise). The intermediate
+   * o_local / o_global / workspace buffers are always contiguous. */
+  int64_t q_strides[3];
+  int64_t k_strides[3];
+  int64_t v_strides[3];
+  int64_t o_strides[3];
 } logo_problem;
 
 /* Number of selected tokens per sequence: ceil(rho * n) computed in double

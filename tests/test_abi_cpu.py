@@ -147,3 +147,66 @@ def test_no_undefined_kernel_stubs(L):
     out = subprocess.run(["nm", "-D", "--undefined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     assert "device_stub" not in out, [l for l in out.splitlines() if "device_stub" in l]
+
+
+def _ws_status(L, **kw):
+    p = _prob(**kw)
+    size = ctypes.c_size_t(0)
+    return L.logo_workspace_size(ctypes.byref(p), ctypes.byref(size))
+
+
+def _strides(**kw):
+    out = {}
+    for name, st in kw.items():
+        arr = (ctypes.c_int64 * 3)(*st)
+        out[f"{name}_strides"] = arr
+    return out
+
+
+@pytest.mark.parametrize("kw,status", [
+    # bshd layouts (token stride H*d): valid for inputs and outputs
+    (dict(q=(100 * 4 * 128, 128, 4 * 128), o=(100 * 4 * 128, 128, 4 * 128)), 0),
+    # k, v as halves of one fused [B][n][2][Hkv][d] buffer
+    (dict(k=(100 * 2 * 2 * 128, 128, 2 * 2 * 128), v=(100 * 2 * 2 * 128, 128, 2 * 2 * 128)), 0),
+    # inputs may broadcast over batch / heads
+    (dict(k=(0, 0, 128), v=(0, 100 * 128, 128)), 0),
+    # padded token rows
+    (dict(q=(4 * 100 * 136, 100 * 136, 136)), 0),
+    (dict(q=(4 * 100 * 128, 100 * 128, -128)), _lib.LOGO_ERR_INVALID_ARG),
+    (dict(k=(0, 0, 64)), _lib.LOGO_ERR_INVALID_ARG),            # token stride < d
+    (dict(v=(0, 0, 132)), _lib.LOGO_ERR_INVALID_ARG),           # 264 B: not 16-B multiple
+    (dict(o=(100 * 128, 0, 128)), _lib.LOGO_ERR_INVALID_ARG),   # heads overlap
+    (dict(o=(4 * 100 * 128, 128, 128)), _lib.LOGO_ERR_INVALID_ARG),  # tokens and heads overlap
+    (dict(o=(0, 100 * 128, 128)), _lib.LOGO_ERR_INVALID_ARG),   # batches overlap (B = 2)
+])
+def test_stride_validation(L, kw, status):
+    assert _ws_status(L, **_strides(**kw)) == status, L.logo_last_error()
+
+
+def test_stride_span_limit(L):
+    n = 1 << 20
+    ok = _strides(k=(0, 0, 128))
+    assert _ws_status(L, n=n, **ok) == 0
+    big = _strides(k=(0, 0, 1040))      # one sequence spans over 2 GiB of bf16
+    assert _ws_status(L, n=n, **big) == _lib.LOGO_ERR_UNSUPPORTED
+    # the same stride in float32 with fewer tokens fits
+    assert _ws_status(L, n=1 << 18, dtype=0, **big) == 0
+
+
+def test_problem_struct_layout_matches_header(tmp_path):
+    """The ctypes mirror of logo_problem has the C struct's size and offsets."""
+    src = tmp_path / "layout.c"
+    fields = [f for f, _ in _lib.logo_problem._fields_]
+    body = "".join(f'  printf("{f} %zu\\n", offsetof(logo_problem, {f}));\n' for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "logo.h"\n'
+                   'int main(void) {\n' + body +
+                   '  printf("size %zu\\n", sizeof(logo_problem));\n  return 0;\n}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o",
+                    str(exe)], check=True)
+    out = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True,
+                                                        text=True, check=True).stdout.split("\n")
+               if line)
+    for f in fields:
+        assert int(out[f]) == getattr(_lib.logo_problem, f).offset, f
+    assert int(out["size"]) == ctypes.sizeof(_lib.logo_problem)

@@ -23,4 +23,5 @@ from ._lib import (  # noqa: F401
     logo_target_count,
     logo_workspace_size,
     make_problem,
+    view_strides,
 )

@@ -43,13 +43,33 @@ class logo_problem(ctypes.Structure):
         ("rho", ctypes.c_double),
         ("scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
+        ("q_strides", ctypes.c_int64 * 3),
+        ("k_strides", ctypes.c_int64 * 3),
+        ("v_strides", ctypes.c_int64 * 3),
+        ("o_strides", ctypes.c_int64 * 3),
     ]
 
 
 def make_problem(B: int, Hq: int, Hkv: int, n: int, d: int, window: int, rho: float,
-                 scale: float = 0.0, dtype: str = "bf16") -> logo_problem:
+                 scale: float = 0.0, dtype: str = "bf16", q_strides=None, k_strides=None,
+                 v_strides=None, o_strides=None) -> logo_problem:
+    """Problem description. `*_strides` are (batch, head, token) element
+    strides of a strided [B][H][n][d] view (see view_strides); None means
+    the contiguous layout."""
     dt = {"bf16": LOGO_BF16, "f32": LOGO_F32}[dtype]
-    return logo_problem(B, Hq, Hkv, n, d, window, float(rho), float(scale), dt)
+    p = logo_problem(B, Hq, Hkv, n, d, window, float(rho), float(scale), dt)
+    for name, st in (("q", q_strides), ("k", k_strides), ("v", v_strides), ("o", o_strides)):
+        if st is not None:
+            getattr(p, f"{name}_strides")[:] = [int(x) for x in st]
+    return p
+
+
+def view_strides(t: torch.Tensor) -> Tuple[int, int, int]:
+    """(batch, head, token) element strides of a [B][H][n][d] view whose d
+    elements are contiguous, for make_problem."""
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a [B][H][n][d] view with unit stride along d")
+    return t.stride(0), t.stride(1), t.stride(2)
 
 
 _lib = None
@@ -95,16 +115,39 @@ def _check(status: int, where: str) -> None:
         raise LogoError(status, where, detail)
 
 
-def _ptr(t: Optional[torch.Tensor], name: str) -> Optional[int]:
+def _ptr(t: Optional[torch.Tensor], name: str, strided: bool = False) -> Optional[int]:
     if t is None:
         return None
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a GPU tensor")
-    if not t.is_contiguous():
+    if not strided and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t.data_ptr() if t.numel() > 0 else None
+
+
+def _strided(p: logo_problem, t: Optional[torch.Tensor], name: str, heads: int) -> bool:
+    """True when the problem declares strides for this tensor; then t must be
+    the [B][H][n][d] view those strides describe."""
+    st = tuple(getattr(p, f"{name}_strides"))
+    if st == (0, 0, 0) or t is None:
+        return False
+    if tuple(t.shape) != (p.B, heads, p.n, p.d) or view_strides(t) != st:
+        raise ValueError(f"{name} must be a ({p.B}, {heads}, {p.n}, {p.d}) view with strides "
+                         f"{st + (1,)}, got shape {tuple(t.shape)} strides {t.stride()}")
+    return True
+
+
+def _io(p: logo_problem, t: Optional[torch.Tensor], name: str, heads: int) -> Optional[int]:
+    """Pointer of q, k, v or o: contiguous, or the strided view p declares."""
+    dt = io_dtype(p)
+    if _strided(p, t, name, heads):
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+        return _ptr(t, name, strided=True)
+    _expect(t, name, dt, p.B * heads * p.n * p.d)
+    return _ptr(t, name)
 
 
 def _stream(stream) -> Optional[int]:
@@ -151,27 +194,23 @@ def logo_select_queries(p: logo_problem, gate, mask, idx, rank, stream=None) -> 
            "logo_select_queries")
 
 
-def _qkv(p: logo_problem, q, k, v) -> None:
-    dt = io_dtype(p)
-    _expect(q, "q", dt, p.B * p.Hq * p.n * p.d)
-    _expect(k, "k", dt, p.B * p.Hkv * p.n * p.d)
-    _expect(v, "v", dt, p.B * p.Hkv * p.n * p.d)
+def _qkv(p: logo_problem, q, k, v) -> Tuple[Optional[int], Optional[int], Optional[int]]:
+    return _io(p, q, "q", p.Hq), _io(p, k, "k", p.Hkv), _io(p, v, "v", p.Hkv)
 
 
 def logo_local_attn(p: logo_problem, q, k, v, o_local, stream=None) -> None:
-    _qkv(p, q, k, v)
+    qp, kp, vp = _qkv(p, q, k, v)
     _expect(o_local, "o_local", torch.float32, p.B * p.Hq * p.n * p.d)
-    _check(lib().logo_local_attn(ctypes.byref(p), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"),
-                                 _ptr(o_local, "o_local"), _stream(stream)), "logo_local_attn")
+    _check(lib().logo_local_attn(ctypes.byref(p), qp, kp, vp, _ptr(o_local, "o_local"),
+                                 _stream(stream)), "logo_local_attn")
 
 
 def logo_global_attn_sparse(p: logo_problem, q, k, v, idx, o_global, stream=None) -> None:
     kk = logo_target_count(p.rho, p.n)
-    _qkv(p, q, k, v)
+    qp, kp, vp = _qkv(p, q, k, v)
     _expect(idx, "idx", torch.int32, p.B * kk)
     _expect(o_global, "o_global", torch.float32, p.B * p.Hq * kk * p.d)
-    _check(lib().logo_global_attn_sparse(ctypes.byref(p), _ptr(q, "q"), _ptr(k, "k"),
-                                         _ptr(v, "v"), _ptr(idx, "idx"),
+    _check(lib().logo_global_attn_sparse(ctypes.byref(p), qp, kp, vp, _ptr(idx, "idx"),
                                          _ptr(o_global, "o_global"), _stream(stream)),
            "logo_global_attn_sparse")
 
@@ -182,24 +221,24 @@ def logo_combine(p: logo_problem, o_local, o_global, rank, gate, o, stream=None)
     _expect(o_global, "o_global", torch.float32, p.B * p.Hq * kk * p.d)
     _expect(rank, "rank", torch.int32, p.B * p.n)
     _expect(gate, "gate", torch.float32, p.B * p.n)
-    _expect(o, "o", io_dtype(p), p.B * p.Hq * p.n * p.d)
+    op = _io(p, o, "o", p.Hq)
     _check(lib().logo_combine(ctypes.byref(p), _ptr(o_local, "o_local"),
                               _ptr(o_global, "o_global"), _ptr(rank, "rank"),
-                              _ptr(gate, "gate"), _ptr(o, "o"), _stream(stream)), "logo_combine")
+                              _ptr(gate, "gate"), op, _stream(stream)), "logo_combine")
 
 
 def logo_forward(p: logo_problem, q, k, v, gate, o, mask, idx, rank, workspace,
                  stream=None) -> None:
     kk = logo_target_count(p.rho, p.n)
-    _qkv(p, q, k, v)
+    qp, kp, vp = _qkv(p, q, k, v)
     _expect(gate, "gate", torch.float32, p.B * p.n)
-    _expect(o, "o", io_dtype(p), p.B * p.Hq * p.n * p.d)
+    op = _io(p, o, "o", p.Hq)
     _expect(mask, "mask", torch.uint8, p.B * p.n)
     _expect(idx, "idx", torch.int32, p.B * kk)
     _expect(rank, "rank", torch.int32, p.B * p.n)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().logo_forward(ctypes.byref(p), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"),
-                              _ptr(gate, "gate"), _ptr(o, "o"), _ptr(mask, "mask"),
+    _check(lib().logo_forward(ctypes.byref(p), qp, kp, vp,
+                              _ptr(gate, "gate"), op, _ptr(mask, "mask"),
                               _ptr(idx, "idx"), _ptr(rank, "rank"),
                               _ptr(workspace, "workspace"), ws_bytes, _stream(stream)),
            "logo_forward")

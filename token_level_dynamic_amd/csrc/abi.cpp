@@ -6,11 +6,13 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "logo_internal.h"
@@ -32,6 +34,12 @@ logo_status hip_fail(hipError_t e, const char* what) {
   return fail(LOGO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+#define LOGO_TRY(expr)                 \
+  do {                                 \
+    logo_status _s = (expr);           \
+    if (_s != LOGO_OK) return _s;      \
+  } while (0)
+
 int64_t target_count(double rho, int64_t n) {
   if (std::isnan(rho) || n < 0) return -1;
   double k = std::ceil(rho * (double)n);
@@ -41,6 +49,46 @@ int64_t target_count(double rho, int64_t n) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Resolves and checks one tensor's (batch, head, token) strides.
+logo_status check_view(const char* name, const int64_t st[3], int64_t B, int64_t H, int64_t n,
+                       int64_t d, int64_t esize, bool output, logo::View* out) {
+  int64_t sb = st[0], sh = st[1], stok = st[2];
+  if (sb == 0 && sh == 0 && stok == 0) {
+    stok = d;
+    sh = n * d;
+    sb = H * n * d;
+  } else {
+    if (sb < 0 || sh < 0 || stok < 0)
+      return fail(LOGO_ERR_INVALID_ARG, "%s strides must be >= 0", name);
+    if (stok < d)
+      return fail(LOGO_ERR_INVALID_ARG, "%s token stride %lld is below d = %lld", name,
+                  (long long)stok, (long long)d);
+    if ((sb * esize) % 16 || (sh * esize) % 16 || (stok * esize) % 16)
+      return fail(LOGO_ERR_INVALID_ARG, "%s strides must be multiples of 16 bytes", name);
+    if (sb >= (int64_t(1) << 60) || sh >= (int64_t(1) << 60))
+      return fail(LOGO_ERR_UNSUPPORTED, "%s strides beyond the supported range", name);
+    if (output) {
+      // Sufficient for distinct elements: sorted by stride, each dimension
+      // steps over everything the smaller ones cover.
+      std::pair<int64_t, int64_t> dims[4] = {{1, d}, {stok, n}, {sh, H}, {sb, B}};
+      std::sort(dims, dims + 4);
+      int64_t need = 1;
+      for (const auto& dm : dims) {
+        if (dm.second <= 1) continue;
+        if (dm.first < need)
+          return fail(LOGO_ERR_INVALID_ARG, "%s strides make output rows overlap", name);
+        need = dm.first * dm.second;
+      }
+    }
+  }
+  if (n > 0 && ((n - 1) * stok + d) * esize >= (int64_t(1) << 31))
+    return fail(LOGO_ERR_UNSUPPORTED, "%s: one sequence spans 2^31 bytes or more", name);
+  out->sb = sb;
+  out->sh = sh;
+  out->st = (int)stok;
+  return LOGO_OK;
+}
 
 // Validates the problem and fills the kernels' view of it.
 logo_status check_problem(const logo_problem* p, logo::Dims* out) {
@@ -73,6 +121,11 @@ logo_status check_problem(const logo_problem* p, logo::Dims* out) {
   out->k = (int)target_count(p->rho, p->n);
   out->scale = p->scale == 0.0f ? (float)(1.0 / std::sqrt((double)p->d)) : p->scale;
   out->dtype = p->dtype;
+  const int64_t es = p->dtype == LOGO_BF16 ? 2 : 4;
+  LOGO_TRY(check_view("q", p->q_strides, p->B, p->Hq, p->n, p->d, es, false, &out->vq));
+  LOGO_TRY(check_view("k", p->k_strides, p->B, p->Hkv, p->n, p->d, es, false, &out->vk));
+  LOGO_TRY(check_view("v", p->v_strides, p->B, p->Hkv, p->n, p->d, es, false, &out->vv));
+  LOGO_TRY(check_view("o", p->o_strides, p->B, p->Hq, p->n, p->d, es, true, &out->vo));
   return LOGO_OK;
 }
 
@@ -84,11 +137,6 @@ logo_status need_ptr(const void* ptr, const char* name) {
   return LOGO_OK;
 }
 
-#define LOGO_TRY(expr)                 \
-  do {                                 \
-    logo_status _s = (expr);           \
-    if (_s != LOGO_OK) return _s;      \
-  } while (0)
 
 size_t scratch_bytes(const logo::Dims& d) {
   const size_t b = (size_t)d.B * d.Hq * d.k * d.d * sizeof(float);

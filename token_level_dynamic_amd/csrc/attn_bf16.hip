@@ -88,6 +88,7 @@ struct Params {
   int wg_per_unit;      // workgroups per (b, kv head)
   int total_wg;         // B * Hkv * wg_per_unit
   int per_xcd;          // ceil(total_wg / 8)
+  View vq, vk, vv, vo;  // element strides of q, k, v, o
 };
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
@@ -176,20 +177,22 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   const int t_lo = (GLOBAL ? 0 : max(0, gpos_lo - p.W + 1)) / kKeys;
   const int t_hi = gpos_hi / kKeys;
 
-  const size_t kv_base = (size_t)(b * p.Hkv + hk) * p.n * D;
   // This (b, kv head)'s K and V, read through bounds-checked buffer loads:
   // keys past the end read as zero (they only occur in tiles masked per
   // element, after every query of the tile).
-  const int kv_bytes = p.n * D * 2;
-  const uint16_t* const kg = p.k + kv_base;
-  const uint16_t* const vg = p.v + kv_base;
+  const int k_st = p.vk.st, v_st = p.vv.st;
+  const int k_bytes = ((p.n - 1) * k_st + D) * 2;
+  const int v_bytes = ((p.n - 1) * v_st + D) * 2;
+  const uint16_t* const kg = p.k + b * p.vk.sb + hk * p.vk.sh;
+  const uint16_t* const vg = p.v + b * p.vv.sb + hk * p.vv.sh;
 
   // ---- Q rows into registers -------------------------------------------
   constexpr int QS = D / 16;  // k-steps of 16 along d
   bf16x8 qreg[QS];
   {
     const bool ok = row_ok && pos >= 0;
-    const uint16_t* qrow = p.q + ((size_t)(b * p.Hq + h) * p.n + (ok ? pos : 0)) * D;
+    const uint16_t* qrow =
+        p.q + b * p.vq.sb + h * p.vq.sh + (long long)(ok ? pos : 0) * p.vq.st;
 #pragma unroll
     for (int s = 0; s < QS; ++s) {
       uint4 x = ok ? *reinterpret_cast<const uint4*>(qrow + s * 16 + half * 8)
@@ -210,18 +213,18 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   for (int i = 0; i < KJ; ++i) {
     const int slot = (wave + kWaves * i) * 64 + lane;
     const int row = slot / SM::kChunks, chunk = slot % SM::kChunks;
-    k_voff[i] = chunk < D / 8 ? (uint32_t)(row * D * 2 + chunk * 16) : kPadOff;
+    k_voff[i] = chunk < D / 8 ? (uint32_t)(row * k_st * 2 + chunk * 16) : kPadOff;
   }
 #pragma unroll
   for (int i = 0; i < VJ; ++i) {
     const int slot = (wave + kWaves * i) * 64 + lane;
     const int row = slot / SM::vChunks, chunk = slot % SM::vChunks;
-    v_voff[i] = chunk < D / 8 ? (uint32_t)(row * D * 2 + chunk * 16) : kPadOff;
+    v_voff[i] = chunk < D / 8 ? (uint32_t)(row * v_st * 2 + chunk * 16) : kPadOff;
   }
   auto issue_kv = [&] __device__ (int t, uint16_t* kdst, uint16_t* vdst)
       __attribute__((always_inline)) {
-    issue_tile<KJ, SM::kChunks>(kg, kv_bytes, kdst, k_voff, t * kKeys * D * 2, wave);
-    issue_tile<VJ, SM::vChunks>(vg, kv_bytes, vdst, v_voff, t * kKeys * D * 2, wave);
+    issue_tile<KJ, SM::kChunks>(kg, k_bytes, kdst, k_voff, t * kKeys * k_st * 2, wave);
+    issue_tile<VJ, SM::vChunks>(vg, v_bytes, vdst, v_voff, t * kKeys * v_st * 2, wave);
   };
 
   // Transposing V reads (ds_read_b64_tr_b16). Within each 16-lane group the
@@ -417,6 +420,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   if (!row_ok) return;
   const float inv = 1.0f / l_tot;
   const size_t head_row = (size_t)(b * p.Hq + h);
+  uint16_t* const orow = p.out_io + b * p.vo.sb + h * p.vo.sh + (long long)pos * p.vo.st;
   // EPI: 0 LocalAll, 1 LocalFused, 2 GlobalAll, 3 GlobalFused
   int rk = -1;
   if (EPI == 1) rk = p.rank[(size_t)b * p.n + pos];
@@ -438,7 +442,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
           *reinterpret_cast<float4*>(p.out_f32 + (head_row * p.ksel + rk) * D + d0) = o4;
         } else {
           uint2 w2 = make_uint2(pack_bf16x2(o4.x, o4.y), pack_bf16x2(o4.z, o4.w));
-          *reinterpret_cast<uint2*>(p.out_io + (head_row * p.n + pos) * D + d0) = w2;
+          *reinterpret_cast<uint2*>(orow + d0) = w2;
         }
       } else {
         const float4 l4 =
@@ -446,7 +450,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
         float4 c4 = make_float4(l4.x + sig * o4.x, l4.y + sig * o4.y, l4.z + sig * o4.z,
                                 l4.w + sig * o4.w);
         uint2 w2 = make_uint2(pack_bf16x2(c4.x, c4.y), pack_bf16x2(c4.z, c4.w));
-        *reinterpret_cast<uint2*>(p.out_io + (head_row * p.n + pos) * D + d0) = w2;
+        *reinterpret_cast<uint2*>(orow + d0) = w2;
       }
     }
   }
@@ -500,6 +504,10 @@ hipError_t launch_attn_bf16(const Dims& d, Epi epi, const AttnArgs& a, hipStream
   prm.wg_per_unit = (prm.units + kWaves - 1) / kWaves;
   prm.total_wg = d.B * d.Hkv * prm.wg_per_unit;
   prm.per_xcd = (prm.total_wg + kNumXcd - 1) / kNumXcd;
+  prm.vq = d.vq;
+  prm.vk = d.vk;
+  prm.vv = d.vv;
+  prm.vo = d.vo;
   if (d.d == 64) return dispatch_epi<64>(epi, prm, s);
   if (d.d == 128) return dispatch_epi<128>(epi, prm, s);
   return hipErrorInvalidValue;

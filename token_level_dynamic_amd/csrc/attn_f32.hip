@@ -34,6 +34,7 @@ struct Params {
   int B, Hq, Hkv, n, W, ksel;
   float scale_log2;
   long long rows;  // B * Hq * R
+  View vq, vk, vv, vo;  // element strides of q, k, v, o
 };
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -65,15 +66,14 @@ __global__ __launch_bounds__(kWaves * 64) void attn_f32_kernel(Params p) {
   const int lo = GLOBAL ? 0 : max(0, pos - p.W + 1);
   const int hi = pos;
 
-  const float* qrow = p.q + ((size_t)(b * p.Hq + h) * p.n + pos) * D;
+  const float* qrow = p.q + b * p.vq.sb + h * p.vq.sh + (long long)pos * p.vq.st;
   for (int e = lane; e < D; e += 64) qs[wave][e] = qrow[e];
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  const size_t kv_base = (size_t)(b * p.Hkv + hk) * p.n * D;
-  const float* kg = p.k + kv_base;
-  const float* vg = p.v + kv_base;
+  const float* kg = p.k + b * p.vk.sb + hk * p.vk.sh;
+  const float* vg = p.v + b * p.vv.sb + hk * p.vv.sh;
 
   constexpr int NC = D / 64;  // output columns per lane
   float acc[NC];
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_f32_kernel(Params p) {
     const int j = j0 + lane;
     float s = -INFINITY;
     if (j <= hi) {
-      const float4* kr = reinterpret_cast<const float4*>(kg + (size_t)j * D);
+      const float4* kr = reinterpret_cast<const float4*>(kg + (size_t)j * p.vk.st);
       float dot = 0.0f;
 #pragma unroll 8
       for (int e4 = 0; e4 < D / 4; ++e4) {
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_f32_kernel(Params p) {
     const int cnt = min(64, hi - j0 + 1);
     for (int jj = 0; jj < cnt; ++jj) {
       const float pw = __shfl(pj, jj, 64);
-      const float* vr = vg + (size_t)(j0 + jj) * D;
+      const float* vr = vg + (size_t)(j0 + jj) * p.vv.st;
 #pragma unroll
       for (int c = 0; c < NC; ++c) acc[c] = fmaf(pw, vr[lane + 64 * c], acc[c]);
     }
@@ -115,6 +115,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_f32_kernel(Params p) {
 
   const float inv = 1.0f / l_run;
   const size_t head_row = (size_t)(b * p.Hq + h);
+  float* const orow = p.out_io + b * p.vo.sb + h * p.vo.sh + (long long)pos * p.vo.st;
   float sig = 0.0f;
   if (EPI == 3) sig = 1.0f / (1.0f + expf(-p.gate[(size_t)b * p.n + pos]));
   int rk = -1;
@@ -129,10 +130,10 @@ __global__ __launch_bounds__(kWaves * 64) void attn_f32_kernel(Params p) {
       p.out_f32[(head_row * p.ksel + r) * D + e] = o;
     } else if (EPI == 1) {
       if (rk >= 0) p.out_f32[(head_row * p.ksel + rk) * D + e] = o;
-      else p.out_io[(head_row * p.n + pos) * D + e] = o;
+      else orow[e] = o;
     } else {
       const float l = p.scratch[(head_row * p.ksel + r) * D + e];
-      p.out_io[(head_row * p.n + pos) * D + e] = l + sig * o;
+      orow[e] = l + sig * o;
     }
   }
 }
@@ -180,6 +181,10 @@ hipError_t launch_attn_f32(const Dims& d, Epi epi, const AttnArgs& a, hipStream_
   prm.ksel = d.k;
   prm.scale_log2 = d.scale * kLog2e;
   prm.rows = (long long)d.B * d.Hq * R;
+  prm.vq = d.vq;
+  prm.vk = d.vk;
+  prm.vv = d.vv;
+  prm.vo = d.vo;
   if (d.d == 64) return dispatch_epi<64>(epi, prm, s);
   if (d.d == 128) return dispatch_epi<128>(epi, prm, s);
   return hipErrorInvalidValue;

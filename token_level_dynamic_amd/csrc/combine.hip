@@ -25,7 +25,7 @@ template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ o_local, const float* __restrict__ o_global,
     const int32_t* __restrict__ rank, const float* __restrict__ gate, void* o,
-    int Hq, int n, int d, int ksel, long long total4) {
+    int Hq, int n, int d, int ksel, long long total4, View vo) {
   const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= total4) return;
   const long long e = t * 4;           // element index in [B][Hq][n][d]
@@ -34,6 +34,8 @@ __global__ __launch_bounds__(256) void combine_kernel(
   const int i = (int)(rowi % n);
   const long long bh = rowi / n;
   const int b = (int)(bh / Hq);
+  const int h = (int)(bh % Hq);
+  const long long oe = b * vo.sb + h * vo.sh + (long long)i * vo.st + dcol;
   float4 v = *reinterpret_cast<const float4*>(o_local + e);
   const int r = rank[(size_t)b * n + i];
   if (r >= 0) {
@@ -48,9 +50,9 @@ __global__ __launch_bounds__(256) void combine_kernel(
   }
   if (BF16) {
     uint2 w = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(o) + e) = w;
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(o) + oe) = w;
   } else {
-    *reinterpret_cast<float4*>(static_cast<float*>(o) + e) = v;
+    *reinterpret_cast<float4*>(static_cast<float*>(o) + oe) = v;
   }
 }
 
@@ -63,10 +65,10 @@ hipError_t launch_combine(const Dims& d, const float* o_local, const float* o_gl
   const long long blocks = (total4 + 255) / 256;
   if (d.dtype == 1) {
     hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s,
-                       o_local, o_global, rank, gate, o, d.Hq, d.n, d.d, d.k, total4);
+                       o_local, o_global, rank, gate, o, d.Hq, d.n, d.d, d.k, total4, d.vo);
   } else {
     hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s,
-                       o_local, o_global, rank, gate, o, d.Hq, d.n, d.d, d.k, total4);
+                       o_local, o_global, rank, gate, o, d.Hq, d.n, d.d, d.k, total4, d.vo);
   }
   return hipGetLastError();
 }

@@ -7,12 +7,21 @@
 
 namespace logo {
 
+// Element strides of one [B][H][n][d] tensor view (d stride 1). The host
+// has checked that ((n-1) * st + d) elements of one (b, h) fit in 2^31
+// bytes, so per-sequence offsets fit 32-bit arithmetic.
+struct View {
+  long long sb, sh;  // batch, head
+  int st;            // token
+};
+
 // Validated problem, as the kernels see it.
 struct Dims {
   int B, Hq, Hkv, n, d, window;
   int k;          // selected tokens per sequence
   float scale;    // score scale
   int dtype;      // 0 f32, 1 bf16 (for q, k, v, o)
+  View vq, vk, vv, vo;  // layouts of the caller's q, k, v and o
 };
 
 // What the attention kernels write for each row they finish.
