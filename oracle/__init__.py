@@ -3,10 +3,12 @@
 TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
 CPU-baseline leg are the only callers allowed. The product (the HIP library
 and its Python binding) never imports it, and it imports nothing from the
-product. See ``oracle/logo.py`` for the definition it computes and the
-passages each step follows.
+product. See ``oracle/logo.py`` for the forward's definition and the passages
+each step follows, and ``oracle/backward.py`` for its chain rule (gradients
+of q, k, v and the gate, and the statistics a training forward saves).
 
-Parity status: every function here is pinned (tests/test_oracle.py); none is
+Parity status: every function here is pinned (tests/test_oracle.py,
+tests/test_oracle_backward.py); none is
 "parity unpinned" against the mathematics, though the pages themselves print
 no worked numbers for this method.
 """
@@ -24,3 +26,4 @@ from .logo import (  # noqa: F401
     softmax_weights,
     target_count,
 )
+from . import backward  # noqa: F401,E402
