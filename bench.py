@@ -42,13 +42,16 @@ sys.path.insert(0, ROOT)
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
 HBM_PEAK_GBS = 8000.0
 METRIC = "effective attn TFLOP/s + ms/layer fwd at 32K ctx, rho=0.2; % of bf16 MFMA peak"
+TRAIN_METRIC = ("effective attn TFLOP/s + ms/layer of one training pass (forward with saved "
+                "statistics + backward) at 32K ctx, rho=0.2; % of bf16 MFMA peak")
 KERNEL_SOURCES = ["attn_bf16.hip", "select.hip", "combine.hip", "abi.cpp"]
+TRAIN_SOURCES = KERNEL_SOURCES + ["backward_prep.hip", "backward_bf16.hip"]
 COPY_BYTES = 1 << 30
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, "token_level_dynamic_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -99,7 +102,7 @@ def cpu_baseline(w, inp, idx, budget_s: float = 15.0, seed: int = 0) -> dict:
                       f"oracle.forward_rows call per 64 rows, {dt:.1f} s wall"}
 
 
-def load_traffic(workload: str, current_hash: str):
+def load_traffic(workload: str, current_hash: str, key: str = "global_bytes_per_launch"):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -108,7 +111,7 @@ def load_traffic(workload: str, current_hash: str):
     ent = data.get(workload)
     if not ent or ent.get("source_hash") != current_hash:
         return None
-    return ent.get("global_bytes_per_launch")
+    return ent.get(key)
 
 
 def copy_calibration(torch) -> int:
@@ -147,6 +150,104 @@ def per_step_timing(torch, step, stream, steps: int) -> dict:
     return out
 
 
+def band_pairs(w) -> float:
+    i = np.arange(w.n, dtype=np.float64)
+    return float(np.minimum(w.window, i + 1).sum())
+
+
+def train_bench(args, torch, T, w, inp, p, q, k, v, gate, dev) -> int:
+    """One step = logo_forward_train + logo_backward over one batch."""
+    from workloads import make_dout
+    dvals, dbits = make_dout(w, args.seed)
+    if dbits is not None:
+        dout = torch.from_numpy(dbits.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        dout = torch.from_numpy(dvals).to(dev)
+    del dvals, dbits
+    fw = T.alloc_train_buffers(p, dev)
+    bw = T.alloc_backward_buffers(p, dev)
+
+    def step():
+        T.logo_forward_train(p, q, k, v, gate, fw["o"], fw["mask"], fw["idx"], fw["rank"],
+                             fw["lse_local"], fw["lse_global"], fw["o_local_sel"],
+                             fw["o_global"])
+        T.logo_backward(p, q, k, v, gate, fw["o"], dout, fw["idx"], fw["rank"],
+                        fw["lse_local"], fw["lse_global"], fw["o_local_sel"], fw["o_global"],
+                        bw["dq"], bw["dk"], bw["dv"], bw["dgate"], bw["workspace"])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    T.logo_profile_begin()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    stage_ms, stage_n = T.logo_profile_end()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    per_step = per_step_timing(torch, step, stream, args.steps)
+
+    idx = fw["idx"].cpu().numpy()
+    # pairs (query, key) of each branch, summed over b and query heads
+    local_pairs = band_pairs(w) * w.B * w.Hq
+    glob_pairs = w.Hq * float(sum((idx[b].astype(np.float64) + 1).sum() for b in range(w.B)))
+    pairs = local_pairs + glob_pairs
+    # 2 flops per multiply-add: forward QK^T and PV (4d per pair); backward
+    # recompute QK^T, dO V^T, P^T dO, dS K, dS^T Q (10d per pair)
+    F_fwd, F_bwd = 4.0 * w.d * pairs, 10.0 * w.d * pairs
+    tflops = (F_fwd + F_bwd) / (ms_per_step * 1e-3) / 1e12
+    avg = {s: (stage_ms[j] / stage_n[j] if stage_n[j] else None)
+           for j, s in enumerate(T.STAGES)}
+    # the dK/dV kernel runs QK^T, dO V^T, P^T dO and dS^T Q on every pair
+    # (8d per pair); the dQ kernels run QK^T, dO V^T and dS K (6d per pair)
+    kern = {"bwd_dkdv": 8.0 * w.d * pairs, "bwd_dq": 6.0 * w.d * pairs}
+    dom = max(kern, key=lambda s: avg[s] or 0.0)
+    dom_ms = avg[dom]
+    achieved = kern[dom] / (dom_ms * 1e-3) / 1e12 if dom_ms else None
+    traffic = load_traffic(w.name, kernel_source_hash(TRAIN_SOURCES), f"{dom}_bytes_per_launch")
+    result = {
+        "metric": TRAIN_METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "n": w.n,
+                   "d": w.d, "window": w.window, "rho": w.rho,
+                   "k_sel": int(T.logo_target_count(w.rho, w.n)), "seed": args.seed,
+                   "mode": "train", "parallelism": "none (1 GPU)"},
+        "pct_of_bf16_peak": round(100.0 * tflops / BF16_PEAK_TFLOPS, 2),
+        "effective_flops": {"forward": F_fwd, "backward": F_bwd},
+        "stage_ms_avg": {s: round(x, 4) for s, x in avg.items() if x is not None},
+        "per_step_ms": per_step,
+        "roofline": {
+            "kernel": {"bwd_dkdv": "bwd_dkdv_kernel (dK, dV of both branches)",
+                       "bwd_dq": "bwd_dq_kernel (dQ, local then global launch)"}[dom],
+            "bound": "mfma",
+            "achieved": round(achieved, 2) if achieved else None,
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / BF16_PEAK_TFLOPS, 4) if achieved else None,
+            "traffic": traffic,
+            "algorithmic_flops_per_launch": kern[dom],
+            "avg_launch_ms": round(dom_ms, 4) if dom_ms else None,
+        },
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +258,9 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--mode", choices=("forward", "train"), default="forward",
+                    help="forward: one logo_forward per step (the headline); train: one "
+                         "logo_forward_train + logo_backward per step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (read N, write N "
                          "bytes) so HBM counters can be scaled to bytes")
@@ -197,6 +301,8 @@ def main() -> int:
         q, k, v = (torch.from_numpy(x).to(dev) for x in (inp.q, inp.k, inp.v))
     gate = torch.from_numpy(inp.gate).to(dev)
     p = T.make_problem(w.B, w.Hq, w.Hkv, w.n, w.d, w.window, w.rho, dtype=w.dtype)
+    if args.mode == "train":
+        return train_bench(args, torch, T, w, inp, p, q, k, v, gate, dev)
     buf = T.alloc_forward_buffers(p, dev)
 
     def step():
@@ -252,7 +358,7 @@ def main() -> int:
                    "parallelism": "none (1 GPU)"},
         "pct_of_bf16_peak": round(100.0 * tflops / BF16_PEAK_TFLOPS, 2),
         "effective_flops": F["total"],
-        "stage_ms_avg": {s: (round(x, 4) if x is not None else None) for s, x in avg.items()},
+        "stage_ms_avg": {s: round(x, 4) for s, x in avg.items() if x is not None},
         "per_step_ms": per_step,
         "roofline": {
             "kernel": f"attn_bf16_kernel ({dom} branch, fused epilogue)",

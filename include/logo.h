@@ -149,6 +149,58 @@ logo_status logo_forward(const logo_problem* p, const void* q, const void* k,
                          uint8_t* mask, int32_t* idx, int32_t* rank,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- training: forward that saves statistics, and the backward --------
+ *
+ * The gate is learned (LoGo abstract) and the method is trained ("Learning
+ * When to Attend", section "Empirical Validation and System Optimization"),
+ * but no page prints a backward pass; the one here is the chain rule of the
+ * forward above with the selection S held fixed: choosing the top-k logits
+ * has no derivative and the pages give no rule for passing a gradient
+ * through it, so the gate gets gradient only through sigmoid(gate_i) on
+ * selected tokens, summed over the query heads that share it:
+ *   dgate_i = g_i (1 - g_i) sum_h <dout_{h,i}, o_global_{h,i}>   (i in S)
+ *   dgate_i = 0                                                  otherwise
+ * and q, k, v get the softmax-attention gradients of both branches (the
+ * global one with upstream gradient g_i dout_i); a kv head sums over its
+ * query heads. */
+
+/* As logo_forward (same o, mask, idx, rank), and also writes what
+ * logo_backward needs:
+ *   lse_local   [B][Hq][n]    float32: log sum_j exp(scale <q_i, k_j>) over
+ *                             L(i) (natural log) for every row
+ *   lse_global  [B][Hq][k]    float32: the same over G(i), rows in idx order
+ *   o_local_sel [B][Hq][k][d] float32: local output of the selected rows
+ *                             (this buffer is also the forward's workspace)
+ *   o_global    [B][Hq][k][d] float32: global output of the selected rows
+ * The four may be NULL only in the cases noted (k == 0: all but lse_local).
+ * Errors: as logo_forward. */
+logo_status logo_forward_train(const logo_problem* p, const void* q, const void* k,
+                               const void* v, const float* gate, void* o,
+                               uint8_t* mask, int32_t* idx, int32_t* rank,
+                               float* lse_local, float* lse_global,
+                               float* o_local_sel, float* o_global, void* stream);
+
+/* Bytes of workspace logo_backward needs (row terms and the selected rows'
+ * queries and gated upstream gradients, gathered: about
+ * B*Hq*(n + k)*4 + 2*B*Hq*k*d*sizeof(dtype)). */
+logo_status logo_backward_workspace_size(const logo_problem* p, size_t* bytes);
+
+/* Gradients of the layer for upstream gradient `dout` (o's dtype and
+ * layout, o_strides). Inputs: q, k, v, gate and the outputs of
+ * logo_forward_train for them (o, idx, rank, lse_local, lse_global,
+ * o_local_sel, o_global). Outputs, float32, contiguous, fully overwritten:
+ *   dq [B][Hq][n][d], dk and dv [B][Hkv][n][d], dgate [B][n].
+ * No atomics: results are bitwise reproducible run to run.
+ * Errors: as logo_forward; LOGO_ERR_WORKSPACE if the workspace is missing
+ * or smaller than logo_backward_workspace_size. */
+logo_status logo_backward(const logo_problem* p, const void* q, const void* k,
+                          const void* v, const float* gate, const void* o,
+                          const void* dout, const int32_t* idx, const int32_t* rank,
+                          const float* lse_local, const float* lse_global,
+                          const float* o_local_sel, const float* o_global,
+                          float* dq, float* dk, float* dv, float* dgate,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* logo_status_string(logo_status s);
 
@@ -158,8 +210,10 @@ const char* logo_last_error(void);
 /* Kernel timing for measurement. Between logo_profile_begin() and
  * logo_profile_end(), logo_forward records a HIP event pair around each of
  * its kernels on the caller's stream (at most 4096 pairs; later launches go
- * unrecorded). logo_profile_end() waits for those events and writes, per
- * stage (0 select, 1 local, 2 global, 3 combine), the summed milliseconds
+ * unrecorded); so do logo_forward_train and logo_backward. logo_profile_end()
+ * waits for those events and writes, per stage (0 select, 1 local, 2 global,
+ * 3 combine, 4 backward row terms and dgate, 5 backward dk/dv, 6 backward
+ * dq), the summed milliseconds
  * and the number of launches into arrays of `n_stages` entries. */
 logo_status logo_profile_begin(void);
 logo_status logo_profile_end(double* stage_ms, int64_t* stage_launches,

@@ -59,7 +59,8 @@ import numpy as np
 
 from . import logo as F
 
-__all__ = ["row_grad", "row_lse", "backward", "dq_rows", "dgate_at", "forward_stats"]
+__all__ = ["row_grad", "row_lse", "backward", "dq_rows", "dgate_at", "forward_stats",
+           "dkdv_tail"]
 
 
 def row_lse(qrow, keys, scale: float) -> float:
@@ -203,3 +204,34 @@ def dgate_at(q, k, v, gate, do, rho: float, positions: Iterable[Sequence[int]],
             acc += float(np.asarray(do[b, h, i], np.float64) @ og)
         out[t] = g[b, i] * (1.0 - g[b, i]) * acc
     return out
+
+
+def dkdv_tail(q, k, v, gate, do, window: int, rho: float, b: int, hk: int, j_from: int,
+              scale: Optional[float] = None):
+    """dk, dv [n - j_from, d] of keys j_from..n-1 of (b, kv head hk), for
+    inputs too large to do whole: only rows at or after j_from read those
+    keys, so the rows i >= j_from of the kv head's query heads, both
+    branches, give their gradients exactly."""
+    F._check_shapes(q, k, v)
+    B, Hq, n, d = q.shape
+    Hkv = k.shape[1]
+    scale = F.default_scale(d) if scale is None else scale
+    mask, _, _ = F.select_queries(gate, rho)
+    g = F.sigmoid(gate)
+    G = Hq // Hkv
+    dk = np.zeros((n - j_from, d))
+    dv = np.zeros((n - j_from, d))
+    for h in range(hk * G, hk * G + G):
+        for i in range(j_from, n):
+            e = np.asarray(do[b, h, i], np.float64)
+            lo = max(0, i - window + 1)
+            _, _, gk, gv = row_grad(q[b, h, i], k[b, hk, lo:i + 1], v[b, hk, lo:i + 1], e, scale)
+            a = max(lo, j_from)
+            dk[a - j_from:i + 1 - j_from] += gk[a - lo:]
+            dv[a - j_from:i + 1 - j_from] += gv[a - lo:]
+            if mask[b, i]:
+                _, _, gk, gv = row_grad(q[b, h, i], k[b, hk, :i + 1], v[b, hk, :i + 1],
+                                        g[b, i] * e, scale)
+                dk[:i + 1 - j_from] += gk[j_from:]
+                dv[:i + 1 - j_from] += gv[j_from:]
+    return dk, dv

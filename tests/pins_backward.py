@@ -173,6 +173,10 @@ def pin_bwd_rows_match(F, BW):
     dq = BW.dq_rows(q, k, v, gate, do, 5, 0.35, rows)
     for t, (b, h, i) in enumerate(rows):
         assert np.allclose(dq[t], full["dq"][b, h, i], atol=1e-13)
+    for b, hk, j_from in ((0, 0, 20), (1, 1, 0), (1, 0, 24)):
+        dk, dv = BW.dkdv_tail(q, k, v, gate, do, 5, 0.35, b, hk, j_from)
+        assert np.allclose(dk, full["dk"][b, hk, j_from:], atol=1e-13)
+        assert np.allclose(dv, full["dv"][b, hk, j_from:], atol=1e-13)
     pos = [(b, i) for b in range(2) for i in range(25)]
     dg = BW.dgate_at(q, k, v, gate, do, 0.35, pos)
     assert np.allclose(dg, full["dgate"].reshape(-1), atol=1e-13)

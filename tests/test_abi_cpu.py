@@ -210,3 +210,58 @@ def test_problem_struct_layout_matches_header(tmp_path):
     for f in fields:
         assert int(out[f]) == getattr(_lib.logo_problem, f).offset, f
     assert int(out["size"]) == ctypes.sizeof(_lib.logo_problem)
+
+
+def _backward(L, p, ws=None, ws_bytes=0, **ptrs):
+    names = ["q", "k", "v", "gate", "o", "dout", "idx", "rank", "lse_local", "lse_global",
+             "o_local_sel", "o_global", "dq", "dk", "dv", "dgate"]
+    args = [ptrs.get(nm, FAKE) for nm in names]
+    return L.logo_backward(ctypes.byref(p), *args, ws, ws_bytes, None)
+
+
+def test_backward_workspace_size(L):
+    p = _prob()
+    size = ctypes.c_size_t(0)
+    assert L.logo_backward_workspace_size(ctypes.byref(p), ctypes.byref(size)) == 0
+    k = T.logo_target_count(0.2, 100)
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    want = up(2 * 4 * 100 * 4) + up(2 * 4 * k * 4) + 2 * up(2 * 4 * k * 128 * 2)
+    assert size.value == want
+    p32 = _prob(dtype=0)
+    assert L.logo_backward_workspace_size(ctypes.byref(p32), ctypes.byref(size)) == 0
+    assert size.value == up(2 * 4 * 100 * 4) + up(2 * 4 * k * 4) + 2 * up(2 * 4 * k * 128 * 4)
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "gate", "o", "dout", "idx", "rank",
+                                   "lse_local", "lse_global", "o_local_sel", "o_global", "dq",
+                                   "dk", "dv", "dgate"])
+def test_backward_null_pointers(L, field):
+    p = _prob()
+    assert _backward(L, p, ws=FAKE, ws_bytes=1 << 30, **{field: None}) == \
+        _lib.LOGO_ERR_INVALID_ARG
+    assert field.encode() in L.logo_last_error()
+    assert _backward(L, p, ws=FAKE, ws_bytes=1 << 30, **{field: MISALIGNED}) == \
+        _lib.LOGO_ERR_INVALID_ARG
+
+
+def test_backward_workspace_checks(L):
+    p = _prob()
+    assert _backward(L, p) == _lib.LOGO_ERR_WORKSPACE
+    size = ctypes.c_size_t(0)
+    L.logo_backward_workspace_size(ctypes.byref(p), ctypes.byref(size))
+    assert _backward(L, p, ws=FAKE, ws_bytes=size.value - 1) == _lib.LOGO_ERR_WORKSPACE
+    assert _backward(L, p, ws=MISALIGNED, ws_bytes=size.value) == _lib.LOGO_ERR_INVALID_ARG
+
+
+def test_forward_train_validation(L):
+    p = _prob()
+    names = ["q", "k", "v", "gate", "o", "mask", "idx", "rank", "lse_local", "lse_global",
+             "o_local_sel", "o_global"]
+    for nm in names:
+        args = [None if x == nm else FAKE for x in names]
+        assert L.logo_forward_train(ctypes.byref(p), *args, None) == _lib.LOGO_ERR_INVALID_ARG
+        assert nm.encode() in L.logo_last_error()
+    # empty problems enqueue nothing and accept NULL everywhere
+    p0 = _prob(n=0)
+    assert L.logo_forward_train(ctypes.byref(p0), *([None] * 12), None) == 0
+    assert L.logo_backward(ctypes.byref(p0), *([None] * 16), None, 0, None) == 0

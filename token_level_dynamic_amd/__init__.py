@@ -9,11 +9,16 @@ from ._lib import (  # noqa: F401
     LOGO_F32,
     STAGES,
     LogoError,
+    alloc_backward_buffers,
     alloc_forward_buffers,
+    alloc_train_buffers,
     io_dtype,
     lib,
+    logo_backward,
+    logo_backward_workspace_size,
     logo_combine,
     logo_forward,
+    logo_forward_train,
     logo_global_attn_sparse,
     logo_local_attn,
     logo_problem,

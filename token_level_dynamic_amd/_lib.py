@@ -23,7 +23,7 @@ LOGO_ERR_WORKSPACE = 3
 LOGO_ERR_HIP = 4
 LOGO_F32 = 0
 LOGO_BF16 = 1
-STAGES = ("select", "local", "global", "combine")
+STAGES = ("select", "local", "global", "combine", "bwd_prep", "bwd_dkdv", "bwd_dq")
 
 
 class LogoError(RuntimeError):
@@ -85,6 +85,9 @@ _SIGS = {
     "logo_combine": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P]),
     "logo_forward": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                     ctypes.c_size_t, _P]),
+    "logo_forward_train": (ctypes.c_int, [_PP] + [_P] * 13),
+    "logo_backward_workspace_size": (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_size_t)]),
+    "logo_backward": (ctypes.c_int, [_PP] + [_P] * 17 + [ctypes.c_size_t, _P]),
     "logo_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "logo_last_error": (ctypes.c_char_p, []),
     "logo_profile_begin": (ctypes.c_int, []),
@@ -242,6 +245,90 @@ def logo_forward(p: logo_problem, q, k, v, gate, o, mask, idx, rank, workspace,
                               _ptr(idx, "idx"), _ptr(rank, "rank"),
                               _ptr(workspace, "workspace"), ws_bytes, _stream(stream)),
            "logo_forward")
+
+
+def logo_forward_train(p: logo_problem, q, k, v, gate, o, mask, idx, rank, lse_local,
+                       lse_global, o_local_sel, o_global, stream=None) -> None:
+    """Forward that also saves what logo_backward needs (see include/logo.h)."""
+    kk = logo_target_count(p.rho, p.n)
+    qp, kp, vp = _qkv(p, q, k, v)
+    _expect(gate, "gate", torch.float32, p.B * p.n)
+    op = _io(p, o, "o", p.Hq)
+    _expect(mask, "mask", torch.uint8, p.B * p.n)
+    _expect(idx, "idx", torch.int32, p.B * kk)
+    _expect(rank, "rank", torch.int32, p.B * p.n)
+    _expect(lse_local, "lse_local", torch.float32, p.B * p.Hq * p.n)
+    _expect(lse_global, "lse_global", torch.float32, p.B * p.Hq * kk)
+    _expect(o_local_sel, "o_local_sel", torch.float32, p.B * p.Hq * kk * p.d)
+    _expect(o_global, "o_global", torch.float32, p.B * p.Hq * kk * p.d)
+    _check(lib().logo_forward_train(
+        ctypes.byref(p), qp, kp, vp, _ptr(gate, "gate"), op, _ptr(mask, "mask"),
+        _ptr(idx, "idx"), _ptr(rank, "rank"), _ptr(lse_local, "lse_local"),
+        _ptr(lse_global, "lse_global"), _ptr(o_local_sel, "o_local_sel"),
+        _ptr(o_global, "o_global"), _stream(stream)), "logo_forward_train")
+
+
+def logo_backward_workspace_size(p: logo_problem) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().logo_backward_workspace_size(ctypes.byref(p), ctypes.byref(out)),
+           "logo_backward_workspace_size")
+    return int(out.value)
+
+
+def logo_backward(p: logo_problem, q, k, v, gate, o, dout, idx, rank, lse_local, lse_global,
+                  o_local_sel, o_global, dq, dk, dv, dgate, workspace, stream=None) -> None:
+    """Gradients dq, dk, dv (float32) and dgate for upstream gradient dout."""
+    kk = logo_target_count(p.rho, p.n)
+    qp, kp, vp = _qkv(p, q, k, v)
+    _expect(gate, "gate", torch.float32, p.B * p.n)
+    op = _io(p, o, "o", p.Hq)
+    dop = _io(p, dout, "o", p.Hq)
+    _expect(idx, "idx", torch.int32, p.B * kk)
+    _expect(rank, "rank", torch.int32, p.B * p.n)
+    _expect(lse_local, "lse_local", torch.float32, p.B * p.Hq * p.n)
+    _expect(lse_global, "lse_global", torch.float32, p.B * p.Hq * kk)
+    _expect(o_local_sel, "o_local_sel", torch.float32, p.B * p.Hq * kk * p.d)
+    _expect(o_global, "o_global", torch.float32, p.B * p.Hq * kk * p.d)
+    _expect(dq, "dq", torch.float32, p.B * p.Hq * p.n * p.d)
+    _expect(dk, "dk", torch.float32, p.B * p.Hkv * p.n * p.d)
+    _expect(dv, "dv", torch.float32, p.B * p.Hkv * p.n * p.d)
+    _expect(dgate, "dgate", torch.float32, p.B * p.n)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().logo_backward(
+        ctypes.byref(p), qp, kp, vp, _ptr(gate, "gate"), op, dop, _ptr(idx, "idx"),
+        _ptr(rank, "rank"), _ptr(lse_local, "lse_local"), _ptr(lse_global, "lse_global"),
+        _ptr(o_local_sel, "o_local_sel"), _ptr(o_global, "o_global"), _ptr(dq, "dq"),
+        _ptr(dk, "dk"), _ptr(dv, "dv"), _ptr(dgate, "dgate"), _ptr(workspace, "workspace"),
+        ws_bytes, _stream(stream)), "logo_backward")
+
+
+def alloc_train_buffers(p: logo_problem, device="cuda") -> dict:
+    """Output, selection and saved-statistics tensors for logo_forward_train."""
+    kk = logo_target_count(p.rho, p.n)
+    f32 = dict(dtype=torch.float32, device=device)
+    return {
+        "o": torch.empty((p.B, p.Hq, p.n, p.d), dtype=io_dtype(p), device=device),
+        "mask": torch.empty((p.B, p.n), dtype=torch.uint8, device=device),
+        "idx": torch.empty((p.B, kk), dtype=torch.int32, device=device),
+        "rank": torch.empty((p.B, p.n), dtype=torch.int32, device=device),
+        "lse_local": torch.empty((p.B, p.Hq, p.n), **f32),
+        "lse_global": torch.empty((p.B, p.Hq, kk), **f32),
+        "o_local_sel": torch.empty((p.B, p.Hq, kk, p.d), **f32),
+        "o_global": torch.empty((p.B, p.Hq, kk, p.d), **f32),
+    }
+
+
+def alloc_backward_buffers(p: logo_problem, device="cuda") -> dict:
+    """Gradient and workspace tensors for logo_backward."""
+    ws = logo_backward_workspace_size(p)
+    f32 = dict(dtype=torch.float32, device=device)
+    return {
+        "dq": torch.empty((p.B, p.Hq, p.n, p.d), **f32),
+        "dk": torch.empty((p.B, p.Hkv, p.n, p.d), **f32),
+        "dv": torch.empty((p.B, p.Hkv, p.n, p.d), **f32),
+        "dgate": torch.empty((p.B, p.n), **f32),
+        "workspace": torch.empty((ws,), dtype=torch.uint8, device=device) if ws else None,
+    }
 
 
 def logo_profile_begin() -> None:

@@ -350,6 +350,145 @@ logo_status logo_forward(const logo_problem* p, const void* q, const void* k, co
   return LOGO_OK;
 }
 
+logo_status logo_forward_train(const logo_problem* p, const void* q, const void* k,
+                               const void* v, const float* gate, void* o, uint8_t* mask,
+                               int32_t* idx, int32_t* rank, float* lse_local, float* lse_global,
+                               float* o_local_sel, float* o_global, void* stream) {
+  logo::Dims d;
+  LOGO_TRY(check_problem(p, &d));
+  if (empty(d)) return LOGO_OK;
+  LOGO_TRY(need_ptr(q, "q"));
+  LOGO_TRY(need_ptr(k, "k"));
+  LOGO_TRY(need_ptr(v, "v"));
+  LOGO_TRY(need_ptr(gate, "gate"));
+  LOGO_TRY(need_ptr(o, "o"));
+  LOGO_TRY(need_ptr(mask, "mask"));
+  LOGO_TRY(need_ptr(rank, "rank"));
+  LOGO_TRY(need_ptr(lse_local, "lse_local"));
+  if (d.k > 0) {
+    LOGO_TRY(need_ptr(idx, "idx"));
+    LOGO_TRY(need_ptr(lse_global, "lse_global"));
+    LOGO_TRY(need_ptr(o_local_sel, "o_local_sel"));
+    LOGO_TRY(need_ptr(o_global, "o_global"));
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  {
+    StageTimer tm(0, s);
+    e = logo::launch_select(d, gate, mask, d.k > 0 ? idx : nullptr, rank, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  logo::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.idx = idx;
+  a.rank = rank;
+  a.gate = gate;
+  a.out_f32 = o_local_sel;
+  a.scratch = o_local_sel;
+  a.out_io = o;
+  a.lse_out = lse_local;
+  {
+    StageTimer tm(1, s);
+    e = run_attn(d, logo::Epi::LocalFused, a, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "local attention launch");
+  if (d.k > 0) {
+    a.lse_out = lse_global;
+    a.og_out = o_global;
+    StageTimer tm(2, s);
+    e = run_attn(d, logo::Epi::GlobalFused, a, s);
+    if (e != hipSuccess) return hip_fail(e, "global attention launch");
+  }
+  return LOGO_OK;
+}
+
+logo_status logo_backward_workspace_size(const logo_problem* p, size_t* bytes) {
+  logo::Dims d;
+  LOGO_TRY(check_problem(p, &d));
+  if (!bytes) return fail(LOGO_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = empty(d) ? 0 : logo::bwd_workspace(d).total;
+  return LOGO_OK;
+}
+
+logo_status logo_backward(const logo_problem* p, const void* q, const void* k, const void* v,
+                          const float* gate, const void* o, const void* dout,
+                          const int32_t* idx, const int32_t* rank, const float* lse_local,
+                          const float* lse_global, const float* o_local_sel,
+                          const float* o_global, float* dq, float* dk, float* dv, float* dgate,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  logo::Dims d;
+  LOGO_TRY(check_problem(p, &d));
+  if (empty(d)) return LOGO_OK;
+  LOGO_TRY(need_ptr(q, "q"));
+  LOGO_TRY(need_ptr(k, "k"));
+  LOGO_TRY(need_ptr(v, "v"));
+  LOGO_TRY(need_ptr(gate, "gate"));
+  LOGO_TRY(need_ptr(o, "o"));
+  LOGO_TRY(need_ptr(dout, "dout"));
+  LOGO_TRY(need_ptr(rank, "rank"));
+  LOGO_TRY(need_ptr(lse_local, "lse_local"));
+  LOGO_TRY(need_ptr(dq, "dq"));
+  LOGO_TRY(need_ptr(dk, "dk"));
+  LOGO_TRY(need_ptr(dv, "dv"));
+  LOGO_TRY(need_ptr(dgate, "dgate"));
+  if (d.k > 0) {
+    LOGO_TRY(need_ptr(idx, "idx"));
+    LOGO_TRY(need_ptr(lse_global, "lse_global"));
+    LOGO_TRY(need_ptr(o_local_sel, "o_local_sel"));
+    LOGO_TRY(need_ptr(o_global, "o_global"));
+  }
+  const logo::BwdWorkspace ws = logo::bwd_workspace(d);
+  if (!workspace || workspace_bytes < ws.total)
+    return fail(LOGO_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(LOGO_ERR_INVALID_ARG, "workspace misaligned");
+  char* w = static_cast<char*>(workspace);
+  logo::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.gate = gate;
+  a.o = o;
+  a.dout = dout;
+  a.idx = idx;
+  a.rank = rank;
+  a.lse_l = lse_local;
+  a.lse_g = lse_global;
+  a.o_ls = o_local_sel;
+  a.o_g = o_global;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dgate = dgate;
+  a.D_l = reinterpret_cast<float*>(w + ws.D_l);
+  a.D_g = reinterpret_cast<float*>(w + ws.D_g);
+  a.qs = w + ws.qs;
+  a.dog = w + ws.dog;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf = d.dtype == LOGO_BF16;
+  hipError_t e;
+  {
+    StageTimer tm(4, s);
+    e = logo::launch_bwd_prep(d, a, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "backward prep launch");
+  {
+    StageTimer tm(5, s);
+    e = bf ? logo::launch_bwd_dkdv_bf16(d, a, s) : logo::launch_bwd_dkdv_f32(d, a, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "backward dk/dv launch");
+  {
+    StageTimer tm(6, s);
+    e = bf ? logo::launch_bwd_dq_bf16(d, false, a, s) : logo::launch_bwd_dq_f32(d, false, a, s);
+    if (e == hipSuccess && d.k > 0)
+      e = bf ? logo::launch_bwd_dq_bf16(d, true, a, s) : logo::launch_bwd_dq_f32(d, true, a, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "backward dq launch");
+  return LOGO_OK;
+}
+
 logo_status logo_profile_begin(void) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
   g_prof.on = true;

@@ -50,6 +50,7 @@ constexpr int kRows = 32;     // query rows per wave
 constexpr int kKeys = 64;     // keys per tile
 constexpr int kNumXcd = 8;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInit = -1.0e30f;
 constexpr float kLazy = 8.0f;  // log2 headroom before the running max moves
 // s_waitcnt immediate for vmcnt(0) with expcnt/lgkmcnt left alone (gfx9 encoding)
@@ -89,6 +90,8 @@ struct Params {
   int total_wg;         // B * Hkv * wg_per_unit
   int per_xcd;          // ceil(total_wg / 8)
   View vq, vk, vv, vo;  // element strides of q, k, v, o
+  float* lse_out;       // optional per-row log-sum-exp (natural log)
+  float* og_out;        // optional f32 o_global rows (fused global)
 };
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
@@ -420,6 +423,8 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   if (!row_ok) return;
   const float inv = 1.0f / l_tot;
   const size_t head_row = (size_t)(b * p.Hq + h);
+  if (p.lse_out && half == 0)
+    p.lse_out[head_row * R + (GLOBAL ? r_lane : pos)] = (m_run + __log2f(l_tot)) * kLn2;
   uint16_t* const orow = p.out_io + b * p.vo.sb + h * p.vo.sh + (long long)pos * p.vo.st;
   // EPI: 0 LocalAll, 1 LocalFused, 2 GlobalAll, 3 GlobalFused
   int rk = -1;
@@ -447,6 +452,8 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
       } else {
         const float4 l4 =
             *reinterpret_cast<const float4*>(p.scratch + (head_row * p.ksel + r_lane) * D + d0);
+        if (p.og_out)
+          *reinterpret_cast<float4*>(p.og_out + (head_row * p.ksel + r_lane) * D + d0) = o4;
         float4 c4 = make_float4(l4.x + sig * o4.x, l4.y + sig * o4.y, l4.z + sig * o4.z,
                                 l4.w + sig * o4.w);
         uint2 w2 = make_uint2(pack_bf16x2(c4.x, c4.y), pack_bf16x2(c4.z, c4.w));
@@ -508,6 +515,8 @@ hipError_t launch_attn_bf16(const Dims& d, Epi epi, const AttnArgs& a, hipStream
   prm.vk = d.vk;
   prm.vv = d.vv;
   prm.vo = d.vo;
+  prm.lse_out = a.lse_out;
+  prm.og_out = a.og_out;
   if (d.d == 64) return dispatch_epi<64>(epi, prm, s);
   if (d.d == 128) return dispatch_epi<128>(epi, prm, s);
   return hipErrorInvalidValue;

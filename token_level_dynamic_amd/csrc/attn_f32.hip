@@ -19,6 +19,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInit = -1.0e30f;
 
 struct Params {
@@ -35,6 +36,8 @@ struct Params {
   float scale_log2;
   long long rows;  // B * Hq * R
   View vq, vk, vv, vo;  // element strides of q, k, v, o
+  float* lse_out;       // optional per-row log-sum-exp (natural log)
+  float* og_out;        // optional f32 o_global rows (fused global)
 };
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -115,6 +118,8 @@ __global__ __launch_bounds__(kWaves * 64) void attn_f32_kernel(Params p) {
 
   const float inv = 1.0f / l_run;
   const size_t head_row = (size_t)(b * p.Hq + h);
+  if (p.lse_out && lane == 0)
+    p.lse_out[head_row * R + (GLOBAL ? r : pos)] = (m_run + log2f(l_run)) * kLn2;
   float* const orow = p.out_io + b * p.vo.sb + h * p.vo.sh + (long long)pos * p.vo.st;
   float sig = 0.0f;
   if (EPI == 3) sig = 1.0f / (1.0f + expf(-p.gate[(size_t)b * p.n + pos]));
@@ -133,6 +138,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_f32_kernel(Params p) {
       else orow[e] = o;
     } else {
       const float l = p.scratch[(head_row * p.ksel + r) * D + e];
+      if (p.og_out) p.og_out[(head_row * p.ksel + r) * D + e] = o;
       orow[e] = l + sig * o;
     }
   }
@@ -185,6 +191,8 @@ hipError_t launch_attn_f32(const Dims& d, Epi epi, const AttnArgs& a, hipStream_
   prm.vk = d.vk;
   prm.vv = d.vv;
   prm.vo = d.vo;
+  prm.lse_out = a.lse_out;
+  prm.og_out = a.og_out;
   if (d.d == 64) return dispatch_epi<64>(epi, prm, s);
   if (d.d == 128) return dispatch_epi<128>(epi, prm, s);
   return hipErrorInvalidValue;

@@ -1,0 +1,694 @@
+// bf16 backward of both attention branches on CDNA4 matrix cores.
+//
+// With the selection S held fixed, one softmax-attention row (query q, keys
+// k_j and values v_j of its range R, upstream gradient e) contributes
+//   p_j  = exp(scale <q, k_j> - lse)             (lse saved by the forward)
+//   dv_j += p_j e
+//   ds_j  = p_j (<e, v_j> - Dr),  Dr = <e, o_row> (the row prep kernel)
+//   dq   += scale sum_j ds_j k_j
+//   dk_j += scale ds_j q
+// Local rows: e = do_i over L(i) = [max(0, i-W+1), i] ("Local-global
+// attention", attention-mask sketch). Selected rows: e = g_i do_i over
+// G(i) = [0, i] ("Learning When to Attend", "The Architecture of
+// Conditional Attention"; LoGo abstract for the gate).
+//
+// Two kernels, both on v_mfma_f32_32x32x16_bf16 (A: lane l holds row l%32,
+// k = (l/32)*8 + [0,8); B: column l%32, same k; C: column l%32, rows
+// (e/4)*8 + (l/32)*4 + e%4 for element e):
+//
+// bwd_dkdv_kernel: key-stationary. A workgroup owns 128 keys of one
+//   (b, kv head), 32 per wave; the K and V rows of its keys sit in registers
+//   as B operands. It streams 32-row query tiles through LDS: for each query
+//   head of the group, the local rows that read its keys and then the
+//   selected rows at or after its first key. Per tile and wave:
+//     S  [32 q x 32 keys] = Q  K^T     (A = Q rows from LDS)
+//     dP [32 q x 32 keys] = dO V^T     (A = dO rows from LDS)
+//     P = exp2(S scale log2e - lse log2e), dS = P (dP - Dr)
+//     dV^T[d x keys] += dO^T P,  dK^T[d x keys] += Q^T dS
+//   where dO^T and Q^T come from the same row-major LDS tiles through the
+//   gfx950 transposing read (ds_read_b64_tr_b16) and P, dS feed the B
+//   operand straight from the accumulator layout (the query order of the
+//   contraction is permuted to match, as in the forward's PV product).
+//
+// bwd_dq_kernel: query-stationary, like the forward: 32 rows per wave with
+//   Q and dO rows in registers, K/V tiles of 64 keys through LDS:
+//     S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - Dr), dQ^T += K^T dS^T.
+//   The local launch writes dq for every row; the global launch then adds
+//   the selected rows' global part in place (same stream, so ordered).
+#include "logo_internal.h"
+
+namespace logo {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kNumXcd = 8;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters untouched
+constexpr uint32_t kPadOff = 0x40000000u;
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 r = __builtin_convertvector((f32x2){a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ bf16x8 ld16(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+// Lane l of instruction j fills LDS slot j*64 + l of a tile whose rows are
+// `chunks` 16-byte slots long (the last ones padding). Returns the byte
+// offset of that slot's source within a row block of row stride `st2`
+// bytes, or an out-of-range offset (reads zero) for padding slots.
+__device__ __forceinline__ uint32_t slot_off(int slot, int chunks, int dchunks, int st2) {
+  const int row = slot / chunks, c = slot % chunks;
+  return c < dchunks ? (uint32_t)(row * st2 + c * 16) : kPadOff;
+}
+
+// Issues this wave's share (instructions j = wave, wave+4, ...) of the
+// buffer-load-to-LDS instructions that fill a tile of `rows` rows.
+// Source: bytes [base, base + nbytes), row r of the tile at byte
+// soff + r * st2. Rows past the end read zero (hardware bounds check).
+template <int NCH, int CHUNKS, int DCH>
+__device__ __forceinline__ void issue_rows(const uint16_t* base, int nbytes, uint16_t* dst,
+                                           int soff, int st2, int wave, int lane) {
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(base), (short)0, nbytes, 0x00020000);
+#pragma unroll
+  for (int j = wave; j < NCH; j += kWaves) {
+    const uint32_t voff = slot_off(j * 64 + lane, CHUNKS, DCH, st2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)(dst + j * 512), 16, voff, soff, 0,
+                                             0);
+  }
+}
+
+// Transposing fragment read: rows (a "key" or "query" index of the
+// contraction) r0 + {half*4 + [0,4)} and r0 + 8 + {half*4 + [0,4)} of a
+// row-major LDS tile, d column block `db`; each lane gets 8 values of its
+// own d column (l % 32), the A operand of a product whose B operand comes
+// from an accumulator's 8 consecutive elements (e = hh*8 + [0,8)).
+// Within each 16-lane group ds_read_b64_tr_b16 gives destination lane 4q+j
+// element e the element j of the 8 bytes addressed by source lane 4e+q.
+__device__ __forceinline__ bf16x8 read_tr(const uint16_t* tile, int stride, int r0, int db,
+                                          int lane) {
+  const int half = lane >> 5;
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+  const uint16_t* a0 = tile + (r0 + half * 4 + tr_row) * stride + db * 32 + tr_col;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(a0));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(a0 + 8 * stride));
+  const uint2 l2 = __builtin_bit_cast(uint2, lo);
+  const uint2 h2 = __builtin_bit_cast(uint2, hi);
+  return __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+}
+
+// =========================================================================
+// dK / dV
+// =========================================================================
+constexpr int kQT = 32;    // query rows per tile
+constexpr int kKW = 32;    // keys per wave
+constexpr int kKB = kKW * kWaves;  // keys per workgroup
+
+template <int D>
+struct QTile {
+  static constexpr int kChunks = D / 8 + 2;    // 32 B of padding per row
+  static constexpr int kStride = kChunks * 8;  // elements
+  static constexpr int kElems = kQT * kStride;
+  static constexpr int kInstr = kQT * kChunks / 64;
+  static_assert(kQT * kChunks % 64 == 0, "tile must be whole instructions");
+};
+
+struct DkdvParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const uint16_t* qs;   // [B][Hq][k][D]
+  const uint16_t* dog;  // [B][Hq][k][D]
+  const int32_t* idx;
+  const float* lse_l;
+  const float* lse_g;
+  const float* D_l;
+  const float* D_g;
+  float* dk;
+  float* dv;
+  int B, Hq, Hkv, n, W, ksel;
+  float scale_log2;
+  float scale;
+  int nkb;       // key blocks per (b, kv head)
+  int total_wg;  // B * Hkv * nkb
+  int per_xcd;
+  View vq, vk, vv, vo;
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(DkdvParams p) {
+  using QT = QTile<D>;
+  constexpr int QS = D / 16;  // k-steps along d
+  constexpr int DB = D / 32;  // 32-wide d blocks
+  constexpr int DCH = D / 8;
+  __shared__ __attribute__((aligned(16))) uint16_t Q0[QT::kElems];
+  __shared__ __attribute__((aligned(16))) uint16_t Q1[QT::kElems];
+  __shared__ __attribute__((aligned(16))) uint16_t O0[QT::kElems];
+  __shared__ __attribute__((aligned(16))) uint16_t O1[QT::kElems];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][kQT];
+  __shared__ __attribute__((aligned(16))) float dr_s[2][kQT];
+  __shared__ __attribute__((aligned(16))) int pos_s[2][kQT];
+
+  const int bid = blockIdx.x;
+  const int L = (bid % kNumXcd) * p.per_xcd + bid / kNumXcd;
+  if (L >= p.total_wg) return;
+  const int unit = L / p.nkb;      // b * Hkv + kv head
+  const int kb = L % p.nkb;        // key blocks of a unit run in order: most work first
+  const int b = unit / p.Hkv;
+  const int hk = unit % p.Hkv;
+  const int G = p.Hq / p.Hkv;
+  const int j0 = kb * kKB;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int kw0 = j0 + wave * kKW;
+  const int key = kw0 + col;
+
+  // K and V rows of this lane's key: B operands for the whole kernel.
+  bf16x8 kreg[QS], vreg[QS];
+  {
+    const int kk = min(key, p.n - 1);
+    const uint16_t* kr = p.k + b * p.vk.sb + hk * p.vk.sh + (long long)kk * p.vk.st + half * 8;
+    const uint16_t* vr = p.v + b * p.vv.sb + hk * p.vv.sh + (long long)kk * p.vv.st + half * 8;
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      kreg[s] = ld16(kr + s * 16);
+      vreg[s] = ld16(vr + s * 16);
+    }
+  }
+
+  // Query tiles: per head of the group, T_loc local tiles (rows j0 ... ,
+  // every row whose window reaches a key of the block) then T_glb tiles of
+  // selected rows from the first one at or after j0.
+  const int i_last = min(p.n - 1, j0 + kKB - 1 + p.W - 1);
+  const int T_loc = (i_last - j0) / kQT + 1;
+  const int* idx_b = p.idx + (size_t)b * p.ksel;
+  int r_start = 0;
+  {
+    int lo = 0, hi = p.ksel;  // first r with idx_b[r] >= j0
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (idx_b[mid] < j0) lo = mid + 1;
+      else hi = mid;
+    }
+    r_start = __builtin_amdgcn_readfirstlane(lo);
+  }
+  const int T_glb = (p.ksel - r_start + kQT - 1) / kQT;
+  const int T_h = T_loc + T_glb;
+  const int T = G * T_h;
+
+  // Tile t: head, kind and first row.
+  struct Desc {
+    int h;
+    bool glb;
+    int r0;
+  };
+  auto desc = [&] __device__ (int t) __attribute__((always_inline)) {
+    Desc d;
+    d.h = hk * G + t / T_h;
+    const int u = t % T_h;
+    d.glb = u >= T_loc;
+    d.r0 = d.glb ? r_start + (u - T_loc) * kQT : j0 + u * kQT;
+    return d;
+  };
+  // Staging of tile t: Q and dO rows by buffer loads into LDS; lse, Dr and
+  // positions through registers of wave 0 (written before the barrier).
+  float st_lse = 0.0f, st_dr = 0.0f;
+  int st_pos = -1;
+  auto issue = [&] __device__ (int t, uint16_t* qdst, uint16_t* odst)
+      __attribute__((always_inline)) {
+    const Desc d = desc(t);
+    if (!d.glb) {
+      const int qst2 = p.vq.st * 2, ost2 = p.vo.st * 2;
+      issue_rows<QT::kInstr, QT::kChunks, DCH>(
+          p.q + b * p.vq.sb + d.h * p.vq.sh, ((p.n - 1) * p.vq.st + D) * 2, qdst, d.r0 * qst2,
+          qst2, wave, lane);
+      issue_rows<QT::kInstr, QT::kChunks, DCH>(
+          p.dout + b * p.vo.sb + d.h * p.vo.sh, ((p.n - 1) * p.vo.st + D) * 2, odst,
+          d.r0 * ost2, ost2, wave, lane);
+    } else {
+      const long long cb = ((long long)b * p.Hq + d.h) * p.ksel;
+      issue_rows<QT::kInstr, QT::kChunks, DCH>(p.qs + cb * D, p.ksel * D * 2, qdst,
+                                               d.r0 * D * 2, D * 2, wave, lane);
+      issue_rows<QT::kInstr, QT::kChunks, DCH>(p.dog + cb * D, p.ksel * D * 2, odst,
+                                               d.r0 * D * 2, D * 2, wave, lane);
+    }
+    if (wave == 0 && lane < kQT) {
+      const int r = d.r0 + lane;
+      const long long hb = (long long)b * p.Hq + d.h;
+      if (!d.glb) {
+        const bool ok = r < p.n;
+        st_lse = ok ? p.lse_l[hb * p.n + r] : 0.0f;
+        st_dr = ok ? p.D_l[hb * p.n + r] : 0.0f;
+        st_pos = ok ? r : -1;
+      } else {
+        const bool ok = r < p.ksel;
+        st_lse = ok ? p.lse_g[hb * p.ksel + r] : 0.0f;
+        st_dr = ok ? p.D_g[hb * p.ksel + r] : 0.0f;
+        st_pos = ok ? idx_b[r] : -1;
+      }
+    }
+  };
+  auto publish = [&] __device__ (int buf) __attribute__((always_inline)) {
+    if (wave == 0 && lane < kQT) {
+      lse_s[buf][lane] = st_lse * kLog2e;
+      dr_s[buf][lane] = st_dr;
+      pos_s[buf][lane] = st_pos;
+    }
+  };
+
+  f32x16 acc_dk[DB], acc_dv[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) {
+    acc_dk[i] = (f32x16){};
+    acc_dv[i] = (f32x16){};
+  }
+
+  auto compute = [&] __device__ (int t, int buf, const uint16_t* qt, const uint16_t* ot)
+      __attribute__((always_inline)) {
+    const Desc d = desc(t);
+    // does any row of the tile read a key of this wave?
+    bool act;
+    if (!d.glb) {
+      act = kw0 < p.n && d.r0 <= kw0 + kKW - 1 + p.W - 1 && d.r0 + kQT - 1 >= kw0;
+    } else {
+      const int last = min(kQT, p.ksel - d.r0) - 1;
+      act = kw0 < p.n && pos_s[buf][last] >= kw0;
+    }
+    if (!__builtin_amdgcn_readfirstlane(act)) return;
+    f32x16 sacc = (f32x16){}, pacc = (f32x16){};
+    const uint16_t* qrow = qt + col * QT::kStride + half * 8;
+    const uint16_t* orow = ot + col * QT::kStride + half * 8;
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld16(qrow + s * 16), kreg[s], sacc, 0, 0, 0);
+      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld16(orow + s * 16), vreg[s], pacc, 0, 0, 0);
+    }
+    uint32_t pk[8], dk2[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q0 = j * 8 + half * 4;
+      const float4 l4 = *reinterpret_cast<const float4*>(&lse_s[buf][q0]);
+      const float4 d4 = *reinterpret_cast<const float4*>(&dr_s[buf][q0]);
+      const int4 p4 = *reinterpret_cast<const int4*>(&pos_s[buf][q0]);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+      const int pv[4] = {p4.x, p4.y, p4.z, p4.w};
+      float pr[4], ds[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = j * 4 + i;
+        bool ok = key <= pv[i];
+        if (!d.glb) ok = ok && key >= pv[i] - p.W + 1;
+        pr[i] = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[e], p.scale_log2, -lv[i])) : 0.0f;
+        ds[i] = pr[i] * (pacc[e] - dv[i]);
+      }
+      pk[2 * j] = pack_bf16x2(pr[0], pr[1]);
+      pk[2 * j + 1] = pack_bf16x2(pr[2], pr[3]);
+      dk2[2 * j] = pack_bf16x2(ds[0], ds[1]);
+      dk2[2 * j + 1] = pack_bf16x2(ds[2], ds[3]);
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const bf16x8 pb =
+            __builtin_bit_cast(bf16x8, make_uint4(pk[4 * hh], pk[4 * hh + 1], pk[4 * hh + 2],
+                                                  pk[4 * hh + 3]));
+        const bf16x8 sb =
+            __builtin_bit_cast(bf16x8, make_uint4(dk2[4 * hh], dk2[4 * hh + 1], dk2[4 * hh + 2],
+                                                  dk2[4 * hh + 3]));
+        acc_dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            read_tr(ot, QT::kStride, hh * 16, db, lane), pb, acc_dv[db], 0, 0, 0);
+        acc_dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            read_tr(qt, QT::kStride, hh * 16, db, lane), sb, acc_dk[db], 0, 0, 0);
+      }
+    }
+  };
+
+  auto step = [&] __device__ (int t, int buf, const uint16_t* qt, const uint16_t* ot,
+                              uint16_t* qn, uint16_t* on) __attribute__((always_inline)) {
+    const bool more = t + 1 < T;
+    if (more) issue(t + 1, qn, on);
+    compute(t, buf, qt, ot);
+    if (more) publish(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+  };
+
+  if (T > 0) {
+    issue(0, Q0, O0);
+    publish(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+  }
+#pragma unroll 1
+  for (int t = 0; t < T; t += 2) {
+    step(t, 0, Q0, O0, Q1, O1);
+    if (t + 1 < T) step(t + 1, 1, Q1, O1, Q0, O0);
+  }
+
+  if (key >= p.n) return;
+  float* dkr = p.dk + (((long long)b * p.Hkv + hk) * p.n + key) * D;
+  float* dvr = p.dv + (((long long)b * p.Hkv + hk) * p.n + key) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d0 = db * 32 + j * 8 + half * 4;
+      *reinterpret_cast<float4*>(dkr + d0) =
+          make_float4(acc_dk[db][j * 4] * p.scale, acc_dk[db][j * 4 + 1] * p.scale,
+                      acc_dk[db][j * 4 + 2] * p.scale, acc_dk[db][j * 4 + 3] * p.scale);
+      *reinterpret_cast<float4*>(dvr + d0) =
+          make_float4(acc_dv[db][j * 4], acc_dv[db][j * 4 + 1], acc_dv[db][j * 4 + 2],
+                      acc_dv[db][j * 4 + 3]);
+    }
+  }
+}
+
+// =========================================================================
+// dQ
+// =========================================================================
+constexpr int kRows = 32;  // query rows per wave
+constexpr int kKeys = 64;  // keys per tile
+
+template <int D>
+struct KVTile {
+  // K rows are read both as 16-byte operands and transposed: 32 B of pad
+  // (conflict-free transposing reads). V rows only as 16-byte operands: 16 B.
+  static constexpr int kChunks = D / 8 + 2;
+  static constexpr int vChunks = D / 8 + 1;
+  static constexpr int kStride = kChunks * 8;
+  static constexpr int vStride = vChunks * 8;
+  static constexpr int kElems = kKeys * kStride;
+  static constexpr int vElems = kKeys * vStride;
+  static constexpr int kInstr = kKeys * kChunks / 64;
+  static constexpr int vInstr = kKeys * vChunks / 64;
+};
+
+struct DqParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const uint16_t* qs;
+  const uint16_t* dog;
+  const int32_t* idx;
+  const float* lse;   // local [B][Hq][n] or global [B][Hq][k]
+  const float* Dr;    // same shape as lse
+  float* dq;
+  int B, Hq, Hkv, n, W, ksel;
+  float scale_log2;
+  float scale;
+  int units;
+  int wg_per_unit;
+  int total_wg;
+  int per_xcd;
+  View vq, vk, vv, vo;
+};
+
+template <int D, bool GLOBAL>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqParams p) {
+  using KT = KVTile<D>;
+  constexpr int QS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int DCH = D / 8;
+  __shared__ __attribute__((aligned(16))) uint16_t K0[KT::kElems];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[KT::kElems];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[KT::vElems];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[KT::vElems];
+
+  const int bid = blockIdx.x;
+  const int L = (bid % kNumXcd) * p.per_xcd + bid / kNumXcd;
+  if (L >= p.total_wg) return;
+  const int unit_bh = L / p.wg_per_unit;
+  int w = L % p.wg_per_unit;
+  if (GLOBAL) w = p.wg_per_unit - 1 - w;  // longest prefix first
+  const int b = unit_bh / p.Hkv;
+  const int hk = unit_bh % p.Hkv;
+  const int G = p.Hq / p.Hkv;
+  const int R = GLOBAL ? p.ksel : p.n;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+
+  const int u_first = w * kWaves;
+  const int u_last = min(u_first + kWaves, p.units) - 1;
+  const int u = u_first + wave;
+  const bool wave_on = u < p.units;
+  const int pb = (wave_on ? u : u_last) / G;
+  const int h = hk * G + (wave_on ? u : u_last) % G;
+  auto row_pos = [&] __device__ (int r) __attribute__((always_inline)) {
+    return GLOBAL ? p.idx[(size_t)b * p.ksel + r] : r;
+  };
+  const int r_lane = pb * kRows + col;
+  const bool row_ok = wave_on && r_lane < R;
+  const int pos = r_lane < R ? row_pos(r_lane) : -1;
+  const int wpos_lo = row_pos(pb * kRows);
+  const int wpos_hi = row_pos(min(pb * kRows + kRows, R) - 1);
+  const int wkey_lo = GLOBAL ? 0 : max(0, wpos_lo - p.W + 1);
+  const int wkey_hi = wpos_hi;
+  const int gpos_lo = row_pos((u_first / G) * kRows);
+  const int gpos_hi = row_pos(min((u_last / G) * kRows + kRows, R) - 1);
+  const int t_lo = (GLOBAL ? 0 : max(0, gpos_lo - p.W + 1)) / kKeys;
+  const int t_hi = gpos_hi / kKeys;
+
+  const long long hb = (long long)b * p.Hq + h;
+  // Q and upstream-gradient rows of this lane's query: B operands.
+  bf16x8 qreg[QS], oreg[QS];
+  float lse2 = 0.0f, dr = 0.0f;
+  {
+    const int rr = row_ok ? r_lane : 0;
+    const uint16_t* qr;
+    const uint16_t* orr;
+    if (GLOBAL) {
+      qr = p.qs + (hb * p.ksel + rr) * D;
+      orr = p.dog + (hb * p.ksel + rr) * D;
+    } else {
+      qr = p.q + b * p.vq.sb + h * p.vq.sh + (long long)rr * p.vq.st;
+      orr = p.dout + b * p.vo.sb + h * p.vo.sh + (long long)rr * p.vo.st;
+    }
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      qreg[s] = ld16(qr + s * 16 + half * 8);
+      oreg[s] = ld16(orr + s * 16 + half * 8);
+    }
+    lse2 = p.lse[hb * R + rr] * kLog2e;
+    dr = p.Dr[hb * R + rr];
+  }
+
+  const int k_st2 = p.vk.st * 2, v_st2 = p.vv.st * 2;
+  const uint16_t* const kg = p.k + b * p.vk.sb + hk * p.vk.sh;
+  const uint16_t* const vg = p.v + b * p.vv.sb + hk * p.vv.sh;
+  const int k_bytes = ((p.n - 1) * p.vk.st + D) * 2;
+  const int v_bytes = ((p.n - 1) * p.vv.st + D) * 2;
+  auto issue_kv = [&] __device__ (int t, uint16_t* kdst, uint16_t* vdst)
+      __attribute__((always_inline)) {
+    issue_rows<KT::kInstr, KT::kChunks, DCH>(kg, k_bytes, kdst, t * kKeys * k_st2, k_st2, wave,
+                                             lane);
+    issue_rows<KT::vInstr, KT::vChunks, DCH>(vg, v_bytes, vdst, t * kKeys * v_st2, v_st2, wave,
+                                             lane);
+  };
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) acc[i] = (f32x16){};
+
+  auto is_active = [&] __device__ (int t) __attribute__((always_inline)) {
+    const int key0 = t * kKeys;
+    return wave_on && key0 <= wkey_hi && key0 + kKeys - 1 >= wkey_lo;
+  };
+
+  auto tile = [&] __device__ (int t, const uint16_t* ks, const uint16_t* vs)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 sacc = (f32x16){}, pacc = (f32x16){};
+      const uint16_t* krow = ks + (kb * 32 + col) * KT::kStride + half * 8;
+      const uint16_t* vrow = vs + (kb * 32 + col) * KT::vStride + half * 8;
+#pragma unroll
+      for (int s = 0; s < QS; ++s) {
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld16(krow + s * 16), qreg[s], sacc, 0, 0,
+                                                       0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld16(vrow + s * 16), oreg[s], pacc, 0, 0,
+                                                       0);
+      }
+      uint32_t dk2[8];
+      const int key0 = t * kKeys + kb * 32;
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2) {
+        float ds[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int e = 2 * e2 + i;
+          const int key = key0 + (e >> 2) * 8 + half * 4 + (e & 3);
+          bool ok = row_ok && key <= pos;
+          if (!GLOBAL) ok = ok && key >= pos - p.W + 1;
+          const float pr = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[e], p.scale_log2, -lse2)) : 0.0f;
+          ds[i] = pr * (pacc[e] - dr);
+        }
+        dk2[e2] = pack_bf16x2(ds[0], ds[1]);
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const bf16x8 sb = __builtin_bit_cast(
+              bf16x8, make_uint4(dk2[4 * hh], dk2[4 * hh + 1], dk2[4 * hh + 2], dk2[4 * hh + 3]));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              read_tr(ks, KT::kStride, kb * 32 + hh * 16, db, lane), sb, acc[db], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  auto step = [&] __device__ (int t, const uint16_t* ks, const uint16_t* vs, uint16_t* kn,
+                              uint16_t* vn) __attribute__((always_inline)) {
+    if (t + 1 <= t_hi) issue_kv(t + 1, kn, vn);
+    if (__builtin_amdgcn_readfirstlane(is_active(t))) tile(t, ks, vs);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+  };
+
+  {
+    issue_kv(t_lo, K0, V0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+  }
+#pragma unroll 1
+  for (int t = t_lo; t <= t_hi; t += 2) {
+    step(t, K0, V0, K1, V1);
+    if (t + 1 <= t_hi) step(t + 1, K1, V1, K0, V0);
+  }
+
+  if (!row_ok) return;
+  float* dqr = p.dq + (hb * p.n + pos) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d0 = db * 32 + j * 8 + half * 4;
+      float4 v4 = make_float4(acc[db][j * 4] * p.scale, acc[db][j * 4 + 1] * p.scale,
+                              acc[db][j * 4 + 2] * p.scale, acc[db][j * 4 + 3] * p.scale);
+      float4* dst = reinterpret_cast<float4*>(dqr + d0);
+      if (GLOBAL) {
+        const float4 old = *dst;
+        v4.x += old.x;
+        v4.y += old.y;
+        v4.z += old.z;
+        v4.w += old.w;
+      }
+      *dst = v4;
+    }
+  }
+}
+
+template <int D>
+hipError_t dkdv_t(const Dims& d, const BwdArgs& a, hipStream_t s) {
+  DkdvParams p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.dout = static_cast<const uint16_t*>(a.dout);
+  p.qs = static_cast<const uint16_t*>(a.qs);
+  p.dog = static_cast<const uint16_t*>(a.dog);
+  p.idx = a.idx;
+  p.lse_l = a.lse_l;
+  p.lse_g = a.lse_g;
+  p.D_l = a.D_l;
+  p.D_g = a.D_g;
+  p.dk = a.dk;
+  p.dv = a.dv;
+  p.B = d.B;
+  p.Hq = d.Hq;
+  p.Hkv = d.Hkv;
+  p.n = d.n;
+  p.W = d.window;
+  p.ksel = d.k;
+  p.scale = d.scale;
+  p.scale_log2 = d.scale * kLog2e;
+  p.nkb = (d.n + kKB - 1) / kKB;
+  p.total_wg = d.B * d.Hkv * p.nkb;
+  p.per_xcd = (p.total_wg + kNumXcd - 1) / kNumXcd;
+  p.vq = d.vq;
+  p.vk = d.vk;
+  p.vv = d.vv;
+  p.vo = d.vo;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(p.per_xcd * kNumXcd), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int D, bool GLOBAL>
+hipError_t dq_t(const Dims& d, const BwdArgs& a, hipStream_t s) {
+  const int R = GLOBAL ? d.k : d.n;
+  if (R == 0) return hipSuccess;
+  DqParams p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.dout = static_cast<const uint16_t*>(a.dout);
+  p.qs = static_cast<const uint16_t*>(a.qs);
+  p.dog = static_cast<const uint16_t*>(a.dog);
+  p.idx = a.idx;
+  p.lse = GLOBAL ? a.lse_g : a.lse_l;
+  p.Dr = GLOBAL ? a.D_g : a.D_l;
+  p.dq = a.dq;
+  p.B = d.B;
+  p.Hq = d.Hq;
+  p.Hkv = d.Hkv;
+  p.n = d.n;
+  p.W = d.window;
+  p.ksel = d.k;
+  p.scale = d.scale;
+  p.scale_log2 = d.scale * kLog2e;
+  const int G = d.Hq / d.Hkv;
+  p.units = (R + kRows - 1) / kRows * G;
+  p.wg_per_unit = (p.units + kWaves - 1) / kWaves;
+  p.total_wg = d.B * d.Hkv * p.wg_per_unit;
+  p.per_xcd = (p.total_wg + kNumXcd - 1) / kNumXcd;
+  p.vq = d.vq;
+  p.vk = d.vk;
+  p.vv = d.vv;
+  p.vo = d.vo;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, GLOBAL>), dim3(p.per_xcd * kNumXcd), dim3(kThreads), 0,
+                     s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dkdv_bf16(const Dims& d, const BwdArgs& a, hipStream_t s) {
+  if (d.B == 0 || d.n == 0) return hipSuccess;
+  if (d.d == 64) return dkdv_t<64>(d, a, s);
+  if (d.d == 128) return dkdv_t<128>(d, a, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dq_bf16(const Dims& d, bool global, const BwdArgs& a, hipStream_t s) {
+  if (d.B == 0 || d.n == 0) return hipSuccess;
+  if (d.d == 64) return global ? dq_t<64, true>(d, a, s) : dq_t<64, false>(d, a, s);
+  if (d.d == 128) return global ? dq_t<128, true>(d, a, s) : dq_t<128, false>(d, a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace logo

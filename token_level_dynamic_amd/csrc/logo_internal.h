@@ -42,7 +42,49 @@ struct AttnArgs {
   float* out_f32;        // o_local / o_global / scratch (fused local)
   const float* scratch;  // fused global: local outputs of selected rows
   void* out_io;          // fused: final output o
+  float* lse_out;        // optional: natural-log log-sum-exp of each row's
+                         // scaled scores (local [B][Hq][n], global [B][Hq][k])
+  float* og_out;         // optional, fused global: o_global [B][Hq][k][d] f32
 };
+
+// Everything the backward kernels read and write. q, k, v, o and dout are
+// the caller's (views as in Dims; dout has o's strides); lse_*, o_*_sel,
+// o_global come from the training forward; the rest is workspace or output.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* gate;      // [B][n]
+  const void* o;          // forward output (io dtype)
+  const void* dout;       // upstream gradient of o (io dtype)
+  const int32_t* idx;     // [B][k]
+  const int32_t* rank;    // [B][n]
+  const float* lse_l;     // [B][Hq][n]   natural log
+  const float* lse_g;     // [B][Hq][k]
+  const float* o_ls;      // [B][Hq][k][d] local output of the selected rows
+  const float* o_g;       // [B][Hq][k][d] global output of the selected rows
+  float* dq;              // [B][Hq][n][d]
+  float* dk;              // [B][Hkv][n][d]
+  float* dv;              // [B][Hkv][n][d]
+  float* dgate;           // [B][n]
+  // workspace
+  float* D_l;             // [B][Hq][n]   <do_i, o_local_i>
+  float* D_g;             // [B][Hq][k]   g_i <do_i, o_global_i>
+  void* qs;               // [B][Hq][k][d] io dtype: q of the selected rows
+  void* dog;              // [B][Hq][k][d] io dtype: g_i do_i of the selected rows
+};
+
+// Backward workspace: offsets (bytes, 256-aligned) of D_l, D_g, qs, dog and the total.
+struct BwdWorkspace {
+  size_t D_l, D_g, qs, dog, total;
+};
+BwdWorkspace bwd_workspace(const Dims& d);
+
+hipError_t launch_bwd_prep(const Dims& d, const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_dkdv_bf16(const Dims& d, const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_dq_bf16(const Dims& d, bool global, const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_dkdv_f32(const Dims& d, const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_dq_f32(const Dims& d, bool global, const BwdArgs& a, hipStream_t s);
 
 hipError_t launch_select(const Dims& d, const float* gate, uint8_t* mask,
                          int32_t* idx, int32_t* rank, hipStream_t s);

@@ -189,6 +189,19 @@ def make_inputs(w: Workload, seed: int = 0, *, gate: Optional[np.ndarray] = None
     return inp
 
 
+def make_dout(w: Workload, seed: int = 0):
+    """Upstream gradient of the layer output for the backward: N(0,1) entries
+    of shape [B, Hq, n, d] from a stream of its own (seed, 0xD0), rounded to
+    bf16 when the workload is bf16. Returns (values as float32, bf16 bits or
+    None)."""
+    rng = np.random.default_rng([seed, 0xD0])
+    x = rng.standard_normal((w.B, w.Hq, w.n, w.d), dtype=np.float32)
+    if w.dtype == "bf16":
+        bits = bf16_bits(x)
+        return bits_to_f32(bits), bits
+    return x, None
+
+
 def _skip_normals(rng: np.random.Generator, count: int, chunk: int = 1 << 24) -> None:
     while count > 0:
         m = min(count, chunk)
