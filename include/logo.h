@@ -182,7 +182,7 @@ logo_status logo_forward_train(const logo_problem* p, const void* q, const void*
 
 /* Bytes of workspace logo_backward needs (row terms and the selected rows'
  * queries and gated upstream gradients, gathered: about
- * B*Hq*(n + k)*4 + 2*B*Hq*k*d*sizeof(dtype)). */
+ * 2*B*Hq*(n + k)*4 + 2*B*Hq*k*d*sizeof(dtype)). */
 logo_status logo_backward_workspace_size(const logo_problem* p, size_t* bytes);
 
 /* Gradients of the layer for upstream gradient `dout` (o's dtype and

@@ -225,11 +225,12 @@ def test_backward_workspace_size(L):
     assert L.logo_backward_workspace_size(ctypes.byref(p), ctypes.byref(size)) == 0
     k = T.logo_target_count(0.2, 100)
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    want = up(2 * 4 * 100 * 4) + up(2 * 4 * k * 4) + 2 * up(2 * 4 * k * 128 * 2)
+    want = 2 * (up(2 * 4 * 100 * 4) + up(2 * 4 * k * 4)) + 2 * up(2 * 4 * k * 128 * 2)
     assert size.value == want
     p32 = _prob(dtype=0)
     assert L.logo_backward_workspace_size(ctypes.byref(p32), ctypes.byref(size)) == 0
-    assert size.value == up(2 * 4 * 100 * 4) + up(2 * 4 * k * 4) + 2 * up(2 * 4 * k * 128 * 4)
+    assert size.value == 2 * (up(2 * 4 * 100 * 4) + up(2 * 4 * k * 4)) + \
+        2 * up(2 * 4 * k * 128 * 4)
 
 
 @pytest.mark.parametrize("field", ["q", "k", "v", "gate", "o", "dout", "idx", "rank",

@@ -464,6 +464,8 @@ logo_status logo_backward(const logo_problem* p, const void* q, const void* k, c
   a.dgate = dgate;
   a.D_l = reinterpret_cast<float*>(w + ws.D_l);
   a.D_g = reinterpret_cast<float*>(w + ws.D_g);
+  a.L2_l = reinterpret_cast<float*>(w + ws.L2_l);
+  a.L2_g = reinterpret_cast<float*>(w + ws.L2_g);
   a.qs = w + ws.qs;
   a.dog = w + ws.dog;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -134,8 +134,8 @@ struct DkdvParams {
   const uint16_t* qs;   // [B][Hq][k][D]
   const uint16_t* dog;  // [B][Hq][k][D]
   const int32_t* idx;
-  const float* lse_l;
-  const float* lse_g;
+  const float* L2_l;   // lse * log2(e), [B][Hq][n]
+  const float* L2_g;   // [B][Hq][k]
   const float* D_l;
   const float* D_g;
   float* dk;
@@ -149,19 +149,46 @@ struct DkdvParams {
   View vq, vk, vv, vo;
 };
 
+// Per-tile row data (lse, Dr, positions) also arrive by buffer loads into
+// LDS: one instruction per array, lanes 0..7 carry the 32 values and the
+// others read out of range (zeros), so each array gets a 1 KiB landing slot.
+constexpr int kSlot = 256;  // floats per landing slot
+
+
+// 32 consecutive 4-byte values from byte soff of [src, src + nbytes) into
+// dst[0..32) (values past nbytes read zero); the rest of the slot gets zeros.
+// The buffer resource is built here: its type is device-only and must not
+// appear where the host pass compiles a kernel's lambdas.
+__device__ __forceinline__ void issue_row_data(const void* src, int nbytes, float* dst, int soff,
+                                               int lane) {
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(src), (short)0, nbytes, 0x00020000);
+  const uint32_t voff = lane < kQT / 4 ? (uint32_t)lane * 16 : kPadOff;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)dst, 16, voff, soff, 0, 0);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(DkdvParams p) {
   using QT = QTile<D>;
   constexpr int QS = D / 16;  // k-steps along d
   constexpr int DB = D / 32;  // 32-wide d blocks
   constexpr int DCH = D / 8;
+  constexpr int NQ = QT::kInstr;
+  // Three tile buffers (tile t is consumed while t+1 is read for the next
+  // products and t+2 lands), each a distinct LDS object so the compiler can
+  // tell reads of one from buffer loads still landing in another. (Loading
+  // one tile further ahead, with a fourth buffer, measured slower: the cost
+  // of the loads is LDS and texture-path bandwidth, not latency.)
   __shared__ __attribute__((aligned(16))) uint16_t Q0[QT::kElems];
   __shared__ __attribute__((aligned(16))) uint16_t Q1[QT::kElems];
+  __shared__ __attribute__((aligned(16))) uint16_t Q2[QT::kElems];
   __shared__ __attribute__((aligned(16))) uint16_t O0[QT::kElems];
   __shared__ __attribute__((aligned(16))) uint16_t O1[QT::kElems];
-  __shared__ __attribute__((aligned(16))) float lse_s[2][kQT];
-  __shared__ __attribute__((aligned(16))) float dr_s[2][kQT];
-  __shared__ __attribute__((aligned(16))) int pos_s[2][kQT];
+  __shared__ __attribute__((aligned(16))) uint16_t O2[QT::kElems];
+  __shared__ __attribute__((aligned(16))) float R0[3 * kSlot];  // lse | Dr | pos
+  __shared__ __attribute__((aligned(16))) float R1[3 * kSlot];
+  __shared__ __attribute__((aligned(16))) float R2[3 * kSlot];
 
   const int bid = blockIdx.x;
   const int L = (bid % kNumXcd) * p.per_xcd + bid / kNumXcd;
@@ -194,9 +221,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(DkdvParams p) {
     }
   }
 
-  // Query tiles: per head of the group, T_loc local tiles (rows j0 ... ,
-  // every row whose window reaches a key of the block) then T_glb tiles of
-  // selected rows from the first one at or after j0.
+  // Query tiles: selected rows at or after j0 (T_glb tiles per head of the
+  // group), then per head T_loc local tiles (rows j0 ..., every row whose
+  // window reaches a key of the block).
   const int i_last = min(p.n - 1, j0 + kKB - 1 + p.W - 1);
   const int T_loc = (i_last - j0) / kQT + 1;
   const int* idx_b = p.idx + (size_t)b * p.ksel;
@@ -210,11 +237,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(DkdvParams p) {
     }
     r_start = __builtin_amdgcn_readfirstlane(lo);
   }
-  const int T_glb = (p.ksel - r_start + kQT - 1) / kQT;
-  const int T_h = T_loc + T_glb;
-  const int T = G * T_h;
+  // Selected-row tiles lie on one grid of 32-row blocks shared by every
+  // workgroup of the (b, kv head) and run from the last block backwards,
+  // heads innermost: the workgroups of an XCD then read the same tile at
+  // about the same time (a unit's gathered rows are larger than one XCD's
+  // L2). Rows of the first block before r_start sit before j0: P = 0 there.
+  const int rb0 = r_start / kQT;
+  const int T_glb = r_start < p.ksel ? (p.ksel + kQT - 1) / kQT - rb0 : 0;
+  const int T_gs = G * T_glb;  // selected-row tiles come first
+  const int T = T_gs + G * T_loc;
 
-  // Tile t: head, kind and first row.
   struct Desc {
     int h;
     bool glb;
@@ -222,55 +254,52 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(DkdvParams p) {
   };
   auto desc = [&] __device__ (int t) __attribute__((always_inline)) {
     Desc d;
-    d.h = hk * G + t / T_h;
-    const int u = t % T_h;
-    d.glb = u >= T_loc;
-    d.r0 = d.glb ? r_start + (u - T_loc) * kQT : j0 + u * kQT;
+    d.glb = t < T_gs;
+    if (d.glb) {
+      d.h = hk * G + t % G;
+      d.r0 = (rb0 + T_glb - 1 - t / G) * kQT;
+    } else {
+      const int u = t - T_gs;
+      d.h = hk * G + u / T_loc;
+      d.r0 = j0 + (u % T_loc) * kQT;
+    }
     return d;
   };
-  // Staging of tile t: Q and dO rows by buffer loads into LDS; lse, Dr and
-  // positions through registers of wave 0 (written before the barrier).
-  float st_lse = 0.0f, st_dr = 0.0f;
-  int st_pos = -1;
-  auto issue = [&] __device__ (int t, uint16_t* qdst, uint16_t* odst)
+
+  // Buffer loads of tile t: Q and dO rows (NQ instructions each, shared by
+  // the four waves), then lse, Dr and, for selected rows, their positions
+  // (one instruction each, waves 0..2).
+  auto issue = [&] __device__ (int t, uint16_t* qdst, uint16_t* odst, float* rdst)
       __attribute__((always_inline)) {
     const Desc d = desc(t);
+    const long long hb = (long long)b * p.Hq + d.h;
     if (!d.glb) {
       const int qst2 = p.vq.st * 2, ost2 = p.vo.st * 2;
-      issue_rows<QT::kInstr, QT::kChunks, DCH>(
-          p.q + b * p.vq.sb + d.h * p.vq.sh, ((p.n - 1) * p.vq.st + D) * 2, qdst, d.r0 * qst2,
-          qst2, wave, lane);
-      issue_rows<QT::kInstr, QT::kChunks, DCH>(
-          p.dout + b * p.vo.sb + d.h * p.vo.sh, ((p.n - 1) * p.vo.st + D) * 2, odst,
-          d.r0 * ost2, ost2, wave, lane);
+      issue_rows<NQ, QT::kChunks, DCH>(p.q + b * p.vq.sb + d.h * p.vq.sh,
+                                       ((p.n - 1) * p.vq.st + D) * 2, qdst, d.r0 * qst2, qst2,
+                                       wave, lane);
+      issue_rows<NQ, QT::kChunks, DCH>(p.dout + b * p.vo.sb + d.h * p.vo.sh,
+                                       ((p.n - 1) * p.vo.st + D) * 2, odst, d.r0 * ost2, ost2,
+                                       wave, lane);
     } else {
-      const long long cb = ((long long)b * p.Hq + d.h) * p.ksel;
-      issue_rows<QT::kInstr, QT::kChunks, DCH>(p.qs + cb * D, p.ksel * D * 2, qdst,
-                                               d.r0 * D * 2, D * 2, wave, lane);
-      issue_rows<QT::kInstr, QT::kChunks, DCH>(p.dog + cb * D, p.ksel * D * 2, odst,
-                                               d.r0 * D * 2, D * 2, wave, lane);
+      const long long cb = hb * p.ksel;
+      issue_rows<NQ, QT::kChunks, DCH>(p.qs + cb * D, p.ksel * D * 2, qdst, d.r0 * D * 2,
+                                       D * 2, wave, lane);
+      issue_rows<NQ, QT::kChunks, DCH>(p.dog + cb * D, p.ksel * D * 2, odst, d.r0 * D * 2,
+                                       D * 2, wave, lane);
     }
-    if (wave == 0 && lane < kQT) {
-      const int r = d.r0 + lane;
-      const long long hb = (long long)b * p.Hq + d.h;
-      if (!d.glb) {
-        const bool ok = r < p.n;
-        st_lse = ok ? p.lse_l[hb * p.n + r] : 0.0f;
-        st_dr = ok ? p.D_l[hb * p.n + r] : 0.0f;
-        st_pos = ok ? r : -1;
+    if (wave < 3) {
+      const void* src;
+      int nbytes;
+      if (wave == 0) {
+        src = d.glb ? (const void*)(p.L2_g + hb * p.ksel) : (const void*)(p.L2_l + hb * p.n);
+      } else if (wave == 1) {
+        src = d.glb ? (const void*)(p.D_g + hb * p.ksel) : (const void*)(p.D_l + hb * p.n);
       } else {
-        const bool ok = r < p.ksel;
-        st_lse = ok ? p.lse_g[hb * p.ksel + r] : 0.0f;
-        st_dr = ok ? p.D_g[hb * p.ksel + r] : 0.0f;
-        st_pos = ok ? idx_b[r] : -1;
+        src = idx_b;
       }
-    }
-  };
-  auto publish = [&] __device__ (int buf) __attribute__((always_inline)) {
-    if (wave == 0 && lane < kQT) {
-      lse_s[buf][lane] = st_lse * kLog2e;
-      dr_s[buf][lane] = st_dr;
-      pos_s[buf][lane] = st_pos;
+      nbytes = (d.glb ? p.ksel : p.n) * 4;
+      if (wave < 2 || d.glb) issue_row_data(src, nbytes, rdst + wave * kSlot, d.r0 * 4, lane);
     }
   };
 
@@ -281,88 +310,156 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(DkdvParams p) {
     acc_dv[i] = (f32x16){};
   }
 
-  auto compute = [&] __device__ (int t, int buf, const uint16_t* qt, const uint16_t* ot)
-      __attribute__((always_inline)) {
+  // One iteration, scheduled by hand (one wave per SIMD: nothing else hides
+  // latency). Step s of QS issues the S / dP products of tile t+1 for d
+  // slice s, the elementwise slice s-1 of tile t (P, dS of 16/QS of this
+  // lane's 16 elements), and LDS reads 1-2 steps ahead of their use: the
+  // next operands, the next row group, and the transposed dO / Q fragments
+  // of tile t for its dV / dK products, which follow (the last elementwise
+  // slice runs after the first half of them).
+  constexpr int E = 16 / QS;        // elements per slice
+  constexpr int NT = 2 * DB;        // transposed operands per matrix (dV: dO^T, dK: Q^T)
+  constexpr int TPS = (2 * NT + QS - 1) / QS;  // transposed operands read per step
+  auto iter = [&] __device__ (int t, const uint16_t* qc, const uint16_t* oc, const float* rc,
+                              const uint16_t* qn, const uint16_t* on, uint16_t* qm,
+                              uint16_t* om, float* rm, const f32x16& s_in, const f32x16& p_in,
+                              f32x16& s_out, f32x16& p_out) __attribute__((always_inline)) {
+    if (t + 2 < T) issue(t + 2, qm, om, rm);
     const Desc d = desc(t);
-    // does any row of the tile read a key of this wave?
-    bool act;
-    if (!d.glb) {
-      act = kw0 < p.n && d.r0 <= kw0 + kKW - 1 + p.W - 1 && d.r0 + kQT - 1 >= kw0;
-    } else {
-      const int last = min(kQT, p.ksel - d.r0) - 1;
-      act = kw0 < p.n && pos_s[buf][last] >= kw0;
+    // key j is read by row pos iff 0 <= pos - j < wlim (window, or any
+    // earlier key for selected rows). Rows past the end of the tile's list
+    // have zero Q / dO rows and zero row terms, so they add exactly zero.
+    const uint32_t wlim = d.glb ? 0x80000000u : (uint32_t)p.W;
+    const int r0 = d.r0;
+    const bool glb = d.glb;
+    const uint16_t* qrow = qn + col * QT::kStride + half * 8;
+    const uint16_t* orow = on + col * QT::kStride + half * 8;
+    bf16x8 qa[QS], oa[QS];
+    bf16x8 tr[2 * NT];  // [0, NT): dO^T for dV, [NT, 2NT): Q^T for dK; index db*2 + hh
+    float4 gl[4], gd[4];
+    int4 gp[4];
+    auto read_group = [&] __device__ (int j) __attribute__((always_inline)) {
+      const int q0 = j * 8 + half * 4;
+      gl[j] = *reinterpret_cast<const float4*>(rc + q0);
+      gd[j] = *reinterpret_cast<const float4*>(rc + kSlot + q0);
+      // loaded for every tile and blended without a branch (a select here
+      // becomes a branch around the read, which splits the schedule)
+      const int4 pr = *reinterpret_cast<const int4*>(rc + 2 * kSlot + q0);
+      const int gm = glb ? -1 : 0;
+      gp[j] = make_int4((pr.x & gm) | ((r0 + q0) & ~gm), (pr.y & gm) | ((r0 + q0 + 1) & ~gm),
+                        (pr.z & gm) | ((r0 + q0 + 2) & ~gm), (pr.w & gm) | ((r0 + q0 + 3) & ~gm));
+    };
+    auto read_tr_op = [&] __device__ (int o) __attribute__((always_inline)) {
+      const int m = o % NT, db = m >> 1, hh = m & 1;
+      tr[o] = read_tr(o < NT ? oc : qc, QT::kStride, hh * 16, db, lane);
+    };
+    uint32_t pk[8], dk2[8];
+    auto slice = [&] __device__ (int sl) __attribute__((always_inline)) {
+#pragma unroll
+      for (int c2 = 0; c2 < E / 2; ++c2) {
+        const int c = sl * (E / 2) + c2;  // pair index: elements 2c, 2c+1
+        float pr[2], ds[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int e = 2 * c + i;
+          const int j = e >> 2, w = e & 3;
+          const float l2 = w == 0 ? gl[j].x : w == 1 ? gl[j].y : w == 2 ? gl[j].z : gl[j].w;
+          const float dr = w == 0 ? gd[j].x : w == 1 ? gd[j].y : w == 2 ? gd[j].z : gd[j].w;
+          const int pos = w == 0 ? gp[j].x : w == 1 ? gp[j].y : w == 2 ? gp[j].z : gp[j].w;
+          const bool ok = (uint32_t)(pos - key) < wlim;
+          const float x = __builtin_amdgcn_exp2f(fmaf(s_in[e], p.scale_log2, -l2));
+          pr[i] = ok ? x : 0.0f;
+          ds[i] = pr[i] * (p_in[e] - dr);
+        }
+        pk[c] = pack_bf16x2(pr[0], pr[1]);
+        dk2[c] = pack_bf16x2(ds[0], ds[1]);
+        asm volatile("" : "+v"(pk[c]), "+v"(dk2[c]));
+      }
+    };
+    // prologue reads
+    qa[0] = ld16(qrow);
+    oa[0] = ld16(orow);
+    if (QS > 1) {
+      qa[1] = ld16(qrow + 16);
+      oa[1] = ld16(orow + 16);
     }
-    if (!__builtin_amdgcn_readfirstlane(act)) return;
-    f32x16 sacc = (f32x16){}, pacc = (f32x16){};
-    const uint16_t* qrow = qt + col * QT::kStride + half * 8;
-    const uint16_t* orow = ot + col * QT::kStride + half * 8;
+    read_group(0);
 #pragma unroll
     for (int s = 0; s < QS; ++s) {
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld16(qrow + s * 16), kreg[s], sacc, 0, 0, 0);
-      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld16(orow + s * 16), vreg[s], pacc, 0, 0, 0);
-    }
-    uint32_t pk[8], dk2[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int q0 = j * 8 + half * 4;
-      const float4 l4 = *reinterpret_cast<const float4*>(&lse_s[buf][q0]);
-      const float4 d4 = *reinterpret_cast<const float4*>(&dr_s[buf][q0]);
-      const int4 p4 = *reinterpret_cast<const int4*>(&pos_s[buf][q0]);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-      const int pv[4] = {p4.x, p4.y, p4.z, p4.w};
-      float pr[4], ds[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = j * 4 + i;
-        bool ok = key <= pv[i];
-        if (!d.glb) ok = ok && key >= pv[i] - p.W + 1;
-        pr[i] = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[e], p.scale_log2, -lv[i])) : 0.0f;
-        ds[i] = pr[i] * (pacc[e] - dv[i]);
+      if (s + 2 < QS) {
+        qa[s + 2] = ld16(qrow + (s + 2) * 16);
+        oa[s + 2] = ld16(orow + (s + 2) * 16);
       }
-      pk[2 * j] = pack_bf16x2(pr[0], pr[1]);
-      pk[2 * j + 1] = pack_bf16x2(pr[2], pr[3]);
-      dk2[2 * j] = pack_bf16x2(ds[0], ds[1]);
-      dk2[2 * j + 1] = pack_bf16x2(ds[2], ds[3]);
+#pragma unroll
+      for (int u = 0; u < TPS; ++u) {
+        const int o = s * TPS + u;
+        if (o < 2 * NT) read_tr_op(o);
+      }
+      // the group first used by slice s+1 (run at step s+2)
+      {
+        const int jn = ((s + 1) * E) >> 2;
+        const int jc = (s * E) >> 2;
+        if (s + 1 < QS && jn != jc && jn < 4) read_group(jn);
+      }
+      s_out = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kreg[s], s ? s_out : (f32x16){}, 0,
+                                                      0, 0);
+      p_out = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[s], vreg[s], s ? p_out : (f32x16){}, 0,
+                                                      0, 0);
+      if (s >= 1) slice(s - 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // dV^T += dO^T P, dK^T += Q^T dS for tile t: keys 0..15 of the
+    // contraction (elements 0..7) first, then the last slice, then 16..31
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int hh = 0; hh < 2; ++hh) {
+      if (hh == 1) {
+        slice(QS - 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const bf16x8 pb = __builtin_bit_cast(
+          bf16x8, make_uint4(pk[4 * hh], pk[4 * hh + 1], pk[4 * hh + 2], pk[4 * hh + 3]));
+      const bf16x8 sb = __builtin_bit_cast(
+          bf16x8, make_uint4(dk2[4 * hh], dk2[4 * hh + 1], dk2[4 * hh + 2], dk2[4 * hh + 3]));
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const bf16x8 pb =
-            __builtin_bit_cast(bf16x8, make_uint4(pk[4 * hh], pk[4 * hh + 1], pk[4 * hh + 2],
-                                                  pk[4 * hh + 3]));
-        const bf16x8 sb =
-            __builtin_bit_cast(bf16x8, make_uint4(dk2[4 * hh], dk2[4 * hh + 1], dk2[4 * hh + 2],
-                                                  dk2[4 * hh + 3]));
-        acc_dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            read_tr(ot, QT::kStride, hh * 16, db, lane), pb, acc_dv[db], 0, 0, 0);
-        acc_dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            read_tr(qt, QT::kStride, hh * 16, db, lane), sb, acc_dk[db], 0, 0, 0);
+      for (int db = 0; db < DB; ++db) {
+        acc_dv[db] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr[db * 2 + hh], pb, acc_dv[db], 0, 0, 0);
+        acc_dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr[NT + db * 2 + hh], sb,
+                                                             acc_dk[db], 0, 0, 0);
       }
     }
-  };
-
-  auto step = [&] __device__ (int t, int buf, const uint16_t* qt, const uint16_t* ot,
-                              uint16_t* qn, uint16_t* on) __attribute__((always_inline)) {
-    const bool more = t + 1 < T;
-    if (more) issue(t + 1, qn, on);
-    compute(t, buf, qt, ot);
-    if (more) publish(buf ^ 1);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
   };
 
-  if (T > 0) {
-    issue(0, Q0, O0);
-    publish(0);
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
+  // prologue: tiles 0 and 1 land, S and dP of tile 0
+  f32x16 sA, pA, sB, pB;
+  issue(0, Q0, O0, R0);
+  if (T > 1) issue(1, Q1, O1, R1);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+  {
+    const uint16_t* qrow = Q0 + col * QT::kStride + half * 8;
+    const uint16_t* orow = O0 + col * QT::kStride + half * 8;
+    sA = (f32x16){};
+    pA = (f32x16){};
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      sA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld16(qrow + s * 16), kreg[s], sA, 0, 0, 0);
+      pA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld16(orow + s * 16), vreg[s], pA, 0, 0, 0);
+    }
   }
+  // Three tiles per trip (buffers named at compile time); the products of
+  // tile t+1 in the last iteration read a stale buffer and are never used.
 #pragma unroll 1
-  for (int t = 0; t < T; t += 2) {
-    step(t, 0, Q0, O0, Q1, O1);
-    if (t + 1 < T) step(t + 1, 1, Q1, O1, Q0, O0);
+  for (int t = 0; t < T; t += 3) {
+    iter(t, Q0, O0, R0, Q1, O1, Q2, O2, R2, sA, pA, sB, pB);
+    if (t + 1 < T) iter(t + 1, Q1, O1, R1, Q2, O2, Q0, O0, R0, sB, pB, sA, pA);
+    if (t + 2 < T) {
+      iter(t + 2, Q2, O2, R2, Q0, O0, Q1, O1, R1, sA, pA, sB, pB);
+      sA = sB;
+      pA = pB;
+    }
   }
 
   if (key >= p.n) return;
@@ -613,8 +710,8 @@ hipError_t dkdv_t(const Dims& d, const BwdArgs& a, hipStream_t s) {
   p.qs = static_cast<const uint16_t*>(a.qs);
   p.dog = static_cast<const uint16_t*>(a.dog);
   p.idx = a.idx;
-  p.lse_l = a.lse_l;
-  p.lse_g = a.lse_g;
+  p.L2_l = a.L2_l;
+  p.L2_g = a.L2_g;
   p.D_l = a.D_l;
   p.D_g = a.D_g;
   p.dk = a.dk;

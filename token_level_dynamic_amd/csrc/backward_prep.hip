@@ -8,7 +8,8 @@
 // its probabilities, the scalar <e, o_row> (the probability-weighted mean of
 // <e, v_j>). This file computes those scalars for every row of both
 // branches, gathers the selected rows' queries and gated upstream gradients
-// into dense arrays for the matrix-core kernels, and the gate gradient
+// into dense arrays for the matrix-core kernels (with each row's lse in log2
+// units, as those kernels exponentiate), and the gate gradient
 //   dgate_i = g_i (1 - g_i) sum_h <do_{h,i}, o_global_{h,i}>   (i in S), 0 elsewhere.
 #include "logo_internal.h"
 
@@ -17,6 +18,8 @@ namespace {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   bf16x2 r = __builtin_convertvector((f32x2){a, b}, bf16x2);
@@ -80,6 +83,10 @@ struct PrepParams {
   const float* o_g;
   float* D_l;
   float* D_g;
+  const float* lse_l;
+  const float* lse_g;
+  float* L2_l;
+  float* L2_g;
   void* qs;
   void* dog;
   int Hq, n, ksel;
@@ -130,10 +137,16 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(PrepParams p) {
     dg += __shfl_xor(dg, off, 64);
   }
   if (!live) return;
-  if (c == 0) p.D_l[rr] = dl;
+  if (c == 0) {
+    p.D_l[rr] = dl;
+    p.L2_l[rr] = p.lse_l[rr] * kLog2e;
+  }
   if (rk >= 0) {
     const long long cr = (long long)bh * p.ksel + rk;
-    if (c == 0) p.D_g[cr] = dg;
+    if (c == 0) {
+      p.D_g[cr] = dg;
+      p.L2_g[cr] = p.lse_g[cr] * kLog2e;
+    }
     float qv[8];
     load8<BF16>(p.q, b * p.vq.sb + h * p.vq.sh + (long long)i * p.vq.st + c, qv);
     store8<BF16>(p.qs, cr * D + c, qv);
@@ -197,6 +210,10 @@ hipError_t launch_prep_t(const Dims& d, const BwdArgs& a, hipStream_t s) {
   pp.o_g = a.o_g;
   pp.D_l = a.D_l;
   pp.D_g = a.D_g;
+  pp.lse_l = a.lse_l;
+  pp.lse_g = a.lse_g;
+  pp.L2_l = a.L2_l;
+  pp.L2_g = a.L2_g;
   pp.qs = a.qs;
   pp.dog = a.dog;
   pp.Hq = d.Hq;
@@ -234,7 +251,9 @@ BwdWorkspace bwd_workspace(const Dims& d) {
   BwdWorkspace w;
   w.D_l = 0;
   w.D_g = up((size_t)d.B * d.Hq * d.n * 4);
-  w.qs = w.D_g + up((size_t)d.B * d.Hq * d.k * 4);
+  w.L2_l = w.D_g + up((size_t)d.B * d.Hq * d.k * 4);
+  w.L2_g = w.L2_l + up((size_t)d.B * d.Hq * d.n * 4);
+  w.qs = w.L2_g + up((size_t)d.B * d.Hq * d.k * 4);
   w.dog = w.qs + up((size_t)d.B * d.Hq * d.k * d.d * es);
   w.total = w.dog + up((size_t)d.B * d.Hq * d.k * d.d * es);
   return w;

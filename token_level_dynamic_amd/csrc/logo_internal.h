@@ -70,13 +70,16 @@ struct BwdArgs {
   // workspace
   float* D_l;             // [B][Hq][n]   <do_i, o_local_i>
   float* D_g;             // [B][Hq][k]   g_i <do_i, o_global_i>
+  float* L2_l;            // [B][Hq][n]   lse_local * log2(e)
+  float* L2_g;            // [B][Hq][k]   lse_global * log2(e)
   void* qs;               // [B][Hq][k][d] io dtype: q of the selected rows
   void* dog;              // [B][Hq][k][d] io dtype: g_i do_i of the selected rows
 };
 
-// Backward workspace: offsets (bytes, 256-aligned) of D_l, D_g, qs, dog and the total.
+// Backward workspace: offsets (bytes, 256-aligned) of D_l, D_g, L2_l, L2_g,
+// qs, dog and the total.
 struct BwdWorkspace {
-  size_t D_l, D_g, qs, dog, total;
+  size_t D_l, D_g, L2_l, L2_g, qs, dog, total;
 };
 BwdWorkspace bwd_workspace(const Dims& d);
 
