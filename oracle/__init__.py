@@ -5,10 +5,12 @@ CPU-baseline leg are the only callers allowed. The product (the HIP library
 and its Python binding) never imports it, and it imports nothing from the
 product. See ``oracle/logo.py`` for the forward's definition and the passages
 each step follows, and ``oracle/backward.py`` for its chain rule (gradients
-of q, k, v and the gate, and the statistics a training forward saves).
+of q, k, v and the gate, and the statistics a training forward saves), and
+``oracle/router.py`` for the routed forward (the gate computed from the local
+branch's output).
 
 Parity status: every function here is pinned (tests/test_oracle.py,
-tests/test_oracle_backward.py); none is
+tests/test_oracle_backward.py, tests/test_oracle_router.py); none is
 "parity unpinned" against the mathematics, though the pages themselves print
 no worked numbers for this method.
 """
@@ -27,3 +29,4 @@ from .logo import (  # noqa: F401
     target_count,
 )
 from . import backward  # noqa: F401,E402
+from . import router  # noqa: F401,E402
