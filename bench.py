@@ -42,6 +42,9 @@ sys.path.insert(0, ROOT)
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
 HBM_PEAK_GBS = 8000.0
 METRIC = "effective attn TFLOP/s + ms/layer fwd at 32K ctx, rho=0.2; % of bf16 MFMA peak"
+ROUTED_METRIC = ("effective attn TFLOP/s + ms/layer of the routed forward (local branch, gate "
+                 "from its output, select, global branch) at 32K ctx, rho=0.2; % of bf16 MFMA "
+                 "peak")
 TRAIN_METRIC = ("effective attn TFLOP/s + ms/layer of one training pass (forward with saved "
                 "statistics + backward) at 32K ctx, rho=0.2; % of bf16 MFMA peak")
 KERNEL_SOURCES = ["attn_bf16.hip", "select.hip", "combine.hip", "abi.cpp"]
@@ -248,6 +251,79 @@ def train_bench(args, torch, T, w, inp, p, q, k, v, gate, dev) -> int:
     return 0
 
 
+def routed_bench(args, torch, T, w, inp, p, q, k, v, dev) -> int:
+    """One step = logo_forward_routed (local, router logits, select, global)."""
+    from workloads import make_router
+    rw, rb = make_router(w, args.seed)
+    router_w = torch.from_numpy(rw).to(dev)
+    buf = T.alloc_routed_buffers(p, dev)
+
+    def step():
+        T.logo_forward_routed(p, q, k, v, router_w, rb, buf["gate"], buf["o"], buf["mask"],
+                              buf["idx"], buf["rank"], buf["workspace"])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    T.logo_profile_begin()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    stage_ms, stage_n = T.logo_profile_end()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    per_step = per_step_timing(torch, step, stream, args.steps)
+    idx = buf["idx"].cpu().numpy()
+    F = effective_flops(w, idx)
+    F_router = 2.0 * w.Hq * w.d * w.n * w.B      # one multiply-add per local output element
+    tflops = (F["total"] + F_router) / (ms_per_step * 1e-3) / 1e12
+    avg = {s: (stage_ms[j] / stage_n[j] if stage_n[j] else None)
+           for j, s in enumerate(T.STAGES)}
+    dom = "global" if F["global"] >= F["local"] else "local"
+    dom_ms = avg[dom]
+    achieved = F[dom] / (dom_ms * 1e-3) / 1e12 if dom_ms else None
+    result = {
+        "metric": ROUTED_METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "n": w.n,
+                   "d": w.d, "window": w.window, "rho": w.rho,
+                   "k_sel": int(T.logo_target_count(w.rho, w.n)), "seed": args.seed,
+                   "mode": "routed", "parallelism": "none (1 GPU)"},
+        "pct_of_bf16_peak": round(100.0 * tflops / BF16_PEAK_TFLOPS, 2),
+        "effective_flops": F["total"] + F_router,
+        "stage_ms_avg": {s: round(x, 4) for s, x in avg.items() if x is not None},
+        "per_step_ms": per_step,
+        "roofline": {
+            "kernel": f"attn_bf16_kernel ({dom} branch, routed epilogue)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2) if achieved else None,
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / BF16_PEAK_TFLOPS, 4) if achieved else None,
+            "traffic": None,
+            "algorithmic_flops_per_launch": F[dom],
+            "avg_launch_ms": round(dom_ms, 4) if dom_ms else None,
+        },
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,9 +334,10 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--mode", choices=("forward", "train"), default="forward",
+    ap.add_argument("--mode", choices=("forward", "train", "routed"), default="forward",
                     help="forward: one logo_forward per step (the headline); train: one "
-                         "logo_forward_train + logo_backward per step")
+                         "logo_forward_train + logo_backward per step; routed: one "
+                         "logo_forward_routed per step (gate computed from the local branch)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (read N, write N "
                          "bytes) so HBM counters can be scaled to bytes")
@@ -303,6 +380,8 @@ def main() -> int:
     p = T.make_problem(w.B, w.Hq, w.Hkv, w.n, w.d, w.window, w.rho, dtype=w.dtype)
     if args.mode == "train":
         return train_bench(args, torch, T, w, inp, p, q, k, v, gate, dev)
+    if args.mode == "routed":
+        return routed_bench(args, torch, T, w, inp, p, q, k, v, dev)
     buf = T.alloc_forward_buffers(p, dev)
 
     def step():

@@ -201,6 +201,31 @@ logo_status logo_backward(const logo_problem* p, const void* q, const void* k,
                           float* dq, float* dk, float* dv, float* dgate,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- routed forward: the gate computed from the local branch ----------
+ *
+ * "Learning When to Attend" (section "The Architecture of Conditional
+ * Attention") runs local attention for every token first and then routes
+ * each token; LoGo (abstract) learns the gate. Here the router is a linear
+ * map of the token's local output over all query heads (the pages give no
+ * router architecture; the plainest reading):
+ *   gate[b][i] = router_bias + sum_h <router_w[h], o_local[b][h][i]>
+ * then, as in logo_forward, the top-k selection on those logits, the global
+ * branch for the selected rows and o = o_local + sigmoid(gate) o_global.
+ * Order of work: local -> router -> select -> global, one stream.
+ *   router_w   [Hq][d] float32 (device)
+ *   gate       [B][n]  float32 output: the computed logits (the selection and
+ *              the combine use exactly these values)
+ *   o, mask, idx, rank as logo_forward.
+ * Workspace: logo_routed_workspace_size bytes (the float32 local output of
+ * every row, B*Hq*n*d*4, and B*Hq*n*4 of per-head partial logits).
+ * Errors: as logo_forward; LOGO_ERR_INVALID_ARG for a non-finite bias. */
+logo_status logo_routed_workspace_size(const logo_problem* p, size_t* bytes);
+logo_status logo_forward_routed(const logo_problem* p, const void* q, const void* k,
+                                const void* v, const float* router_w, float router_bias,
+                                float* gate, void* o, uint8_t* mask, int32_t* idx,
+                                int32_t* rank, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 /* Static text for a status code. */
 const char* logo_status_string(logo_status s);
 
@@ -210,10 +235,11 @@ const char* logo_last_error(void);
 /* Kernel timing for measurement. Between logo_profile_begin() and
  * logo_profile_end(), logo_forward records a HIP event pair around each of
  * its kernels on the caller's stream (at most 4096 pairs; later launches go
- * unrecorded); so do logo_forward_train and logo_backward. logo_profile_end()
- * waits for those events and writes, per stage (0 select, 1 local, 2 global,
- * 3 combine, 4 backward row terms and dgate, 5 backward dk/dv, 6 backward
- * dq), the summed milliseconds
+ * unrecorded); so do logo_forward_train, logo_backward and
+ * logo_forward_routed. logo_profile_end() waits for those events and writes,
+ * per stage (0 select, 1 local, 2 global, 3 combine, 4 backward row terms and
+ * dgate, 5 backward dk/dv, 6 backward dq, 7 router logits), the summed
+ * milliseconds
  * and the number of launches into arrays of `n_stages` entries. */
 logo_status logo_profile_begin(void);
 logo_status logo_profile_end(double* stage_ms, int64_t* stage_launches,

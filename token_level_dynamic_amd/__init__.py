@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     LogoError,
     alloc_backward_buffers,
     alloc_forward_buffers,
+    alloc_routed_buffers,
     alloc_train_buffers,
     io_dtype,
     lib,
@@ -18,12 +19,14 @@ from ._lib import (  # noqa: F401
     logo_backward_workspace_size,
     logo_combine,
     logo_forward,
+    logo_forward_routed,
     logo_forward_train,
     logo_global_attn_sparse,
     logo_local_attn,
     logo_problem,
     logo_profile_begin,
     logo_profile_end,
+    logo_routed_workspace_size,
     logo_select_queries,
     logo_target_count,
     logo_workspace_size,

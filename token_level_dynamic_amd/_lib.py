@@ -23,7 +23,8 @@ LOGO_ERR_WORKSPACE = 3
 LOGO_ERR_HIP = 4
 LOGO_F32 = 0
 LOGO_BF16 = 1
-STAGES = ("select", "local", "global", "combine", "bwd_prep", "bwd_dkdv", "bwd_dq")
+STAGES = ("select", "local", "global", "combine", "bwd_prep", "bwd_dkdv", "bwd_dq",
+          "router")
 
 
 class LogoError(RuntimeError):
@@ -88,6 +89,9 @@ _SIGS = {
     "logo_forward_train": (ctypes.c_int, [_PP] + [_P] * 13),
     "logo_backward_workspace_size": (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_size_t)]),
     "logo_backward": (ctypes.c_int, [_PP] + [_P] * 17 + [ctypes.c_size_t, _P]),
+    "logo_routed_workspace_size": (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_size_t)]),
+    "logo_forward_routed": (ctypes.c_int, [_PP, _P, _P, _P, _P, ctypes.c_float] + [_P] * 6 +
+                            [ctypes.c_size_t, _P]),
     "logo_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "logo_last_error": (ctypes.c_char_p, []),
     "logo_profile_begin": (ctypes.c_int, []),
@@ -327,6 +331,46 @@ def alloc_backward_buffers(p: logo_problem, device="cuda") -> dict:
         "dk": torch.empty((p.B, p.Hkv, p.n, p.d), **f32),
         "dv": torch.empty((p.B, p.Hkv, p.n, p.d), **f32),
         "dgate": torch.empty((p.B, p.n), **f32),
+        "workspace": torch.empty((ws,), dtype=torch.uint8, device=device) if ws else None,
+    }
+
+
+def logo_routed_workspace_size(p: logo_problem) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().logo_routed_workspace_size(ctypes.byref(p), ctypes.byref(out)),
+           "logo_routed_workspace_size")
+    return int(out.value)
+
+
+def logo_forward_routed(p: logo_problem, q, k, v, router_w, router_bias: float, gate, o, mask,
+                        idx, rank, workspace, stream=None) -> None:
+    """Routed forward: local branch, router logits (written to `gate`),
+    selection, global branch, combine (see include/logo.h)."""
+    kk = logo_target_count(p.rho, p.n)
+    qp, kp, vp = _qkv(p, q, k, v)
+    _expect(router_w, "router_w", torch.float32, p.Hq * p.d)
+    _expect(gate, "gate", torch.float32, p.B * p.n)
+    op = _io(p, o, "o", p.Hq)
+    _expect(mask, "mask", torch.uint8, p.B * p.n)
+    _expect(idx, "idx", torch.int32, p.B * kk)
+    _expect(rank, "rank", torch.int32, p.B * p.n)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().logo_forward_routed(
+        ctypes.byref(p), qp, kp, vp, _ptr(router_w, "router_w"), float(router_bias),
+        _ptr(gate, "gate"), op, _ptr(mask, "mask"), _ptr(idx, "idx"), _ptr(rank, "rank"),
+        _ptr(workspace, "workspace"), ws_bytes, _stream(stream)), "logo_forward_routed")
+
+
+def alloc_routed_buffers(p: logo_problem, device="cuda") -> dict:
+    """Gate, output, selection and workspace tensors for logo_forward_routed."""
+    kk = logo_target_count(p.rho, p.n)
+    ws = logo_routed_workspace_size(p)
+    return {
+        "gate": torch.empty((p.B, p.n), dtype=torch.float32, device=device),
+        "o": torch.empty((p.B, p.Hq, p.n, p.d), dtype=io_dtype(p), device=device),
+        "mask": torch.empty((p.B, p.n), dtype=torch.uint8, device=device),
+        "idx": torch.empty((p.B, kk), dtype=torch.int32, device=device),
+        "rank": torch.empty((p.B, p.n), dtype=torch.int32, device=device),
         "workspace": torch.empty((ws,), dtype=torch.uint8, device=device) if ws else None,
     }
 

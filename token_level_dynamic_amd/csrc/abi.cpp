@@ -491,6 +491,86 @@ logo_status logo_backward(const logo_problem* p, const void* q, const void* k, c
   return LOGO_OK;
 }
 
+// Routed forward workspace: float32 local outputs of every row, then the
+// per-head router partials.
+size_t routed_local_bytes(const logo::Dims& d) {
+  return ((size_t)d.B * d.Hq * d.n * d.d * sizeof(float) + 255) / 256 * 256;
+}
+size_t routed_bytes(const logo::Dims& d) {
+  return routed_local_bytes(d) + ((size_t)d.B * d.Hq * d.n * sizeof(float) + 255) / 256 * 256;
+}
+
+logo_status logo_routed_workspace_size(const logo_problem* p, size_t* bytes) {
+  logo::Dims d;
+  LOGO_TRY(check_problem(p, &d));
+  if (!bytes) return fail(LOGO_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = empty(d) ? 0 : routed_bytes(d);
+  return LOGO_OK;
+}
+
+logo_status logo_forward_routed(const logo_problem* p, const void* q, const void* k,
+                                const void* v, const float* router_w, float router_bias,
+                                float* gate, void* o, uint8_t* mask, int32_t* idx,
+                                int32_t* rank, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  logo::Dims d;
+  LOGO_TRY(check_problem(p, &d));
+  if (empty(d)) return LOGO_OK;
+  if (!std::isfinite(router_bias))
+    return fail(LOGO_ERR_INVALID_ARG, "router_bias must be finite");
+  LOGO_TRY(need_ptr(q, "q"));
+  LOGO_TRY(need_ptr(k, "k"));
+  LOGO_TRY(need_ptr(v, "v"));
+  LOGO_TRY(need_ptr(router_w, "router_w"));
+  LOGO_TRY(need_ptr(gate, "gate"));
+  LOGO_TRY(need_ptr(o, "o"));
+  LOGO_TRY(need_ptr(mask, "mask"));
+  LOGO_TRY(need_ptr(rank, "rank"));
+  if (d.k > 0) LOGO_TRY(need_ptr(idx, "idx"));
+  const size_t need = routed_bytes(d);
+  if (!workspace || workspace_bytes < need)
+    return fail(LOGO_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(LOGO_ERR_INVALID_ARG, "workspace misaligned");
+  float* o_local = static_cast<float*>(workspace);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + routed_local_bytes(d));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  logo::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.idx = idx;
+  a.rank = rank;
+  a.gate = gate;
+  a.out_f32 = o_local;
+  a.scratch = o_local;
+  a.out_io = o;
+  a.router_w = router_w;
+  a.router_part = part;
+  hipError_t e;
+  {
+    StageTimer tm(1, s);
+    e = run_attn(d, logo::Epi::LocalRouted, a, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "local attention launch");
+  {
+    StageTimer tm(7, s);
+    e = logo::launch_router_sum(d, part, router_bias, gate, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "router launch");
+  {
+    StageTimer tm(0, s);
+    e = logo::launch_select(d, gate, mask, d.k > 0 ? idx : nullptr, rank, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  if (d.k > 0) {
+    StageTimer tm(2, s);
+    e = run_attn(d, logo::Epi::GlobalRouted, a, s);
+    if (e != hipSuccess) return hip_fail(e, "global attention launch");
+  }
+  return LOGO_OK;
+}
+
 logo_status logo_profile_begin(void) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
   g_prof.on = true;

@@ -92,6 +92,8 @@ struct Params {
   View vq, vk, vv, vo;  // element strides of q, k, v, o
   float* lse_out;       // optional per-row log-sum-exp (natural log)
   float* og_out;        // optional f32 o_global rows (fused global)
+  const float* router_w;  // routed local: [Hq][D]
+  float* router_part;     // routed local: [B][Hq][n]
 };
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
@@ -426,11 +428,15 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   if (p.lse_out && half == 0)
     p.lse_out[head_row * R + (GLOBAL ? r_lane : pos)] = (m_run + __log2f(l_tot)) * kLn2;
   uint16_t* const orow = p.out_io + b * p.vo.sb + h * p.vo.sh + (long long)pos * p.vo.st;
-  // EPI: 0 LocalAll, 1 LocalFused, 2 GlobalAll, 3 GlobalFused
+  // EPI: 0 LocalAll, 1 LocalFused, 2 GlobalAll, 3 GlobalFused, 4 LocalRouted,
+  // 5 GlobalRouted
   int rk = -1;
   if (EPI == 1) rk = p.rank[(size_t)b * p.n + pos];
   float sig = 0.0f;
-  if (EPI == 3) sig = 1.0f / (1.0f + expf(-p.gate[(size_t)b * p.n + pos]));
+  if (EPI == 3 || EPI == 5) sig = 1.0f / (1.0f + expf(-p.gate[(size_t)b * p.n + pos]));
+  // routed local: this lane's half of <router_w[h], o_local row>
+  float rdot = 0.0f;
+  const float* rw = EPI == 4 ? p.router_w + (size_t)h * D : nullptr;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -440,6 +446,19 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
                               acc_o[db][j * 4 + 2] * inv, acc_o[db][j * 4 + 3] * inv);
       if (EPI == 0) {
         *reinterpret_cast<float4*>(p.out_f32 + (head_row * p.n + pos) * D + d0) = o4;
+      } else if (EPI == 4) {
+        *reinterpret_cast<float4*>(p.out_f32 + (head_row * p.n + pos) * D + d0) = o4;
+        uint2 w2 = make_uint2(pack_bf16x2(o4.x, o4.y), pack_bf16x2(o4.z, o4.w));
+        *reinterpret_cast<uint2*>(orow + d0) = w2;
+        const float4 w4 = *reinterpret_cast<const float4*>(rw + d0);
+        rdot = fmaf(o4.x, w4.x, fmaf(o4.y, w4.y, fmaf(o4.z, w4.z, fmaf(o4.w, w4.w, rdot))));
+      } else if (EPI == 5) {
+        const float4 l4 =
+            *reinterpret_cast<const float4*>(p.scratch + (head_row * p.n + pos) * D + d0);
+        float4 c4 = make_float4(l4.x + sig * o4.x, l4.y + sig * o4.y, l4.z + sig * o4.z,
+                                l4.w + sig * o4.w);
+        uint2 w2 = make_uint2(pack_bf16x2(c4.x, c4.y), pack_bf16x2(c4.z, c4.w));
+        *reinterpret_cast<uint2*>(orow + d0) = w2;
       } else if (EPI == 2) {
         *reinterpret_cast<float4*>(p.out_f32 + (head_row * p.ksel + r_lane) * D + d0) = o4;
       } else if (EPI == 1) {
@@ -461,10 +480,18 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
       }
     }
   }
+  if (EPI == 4) {
+    // both halves of a query's row are live together (row_ok is per query)
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rdot), __float_as_uint(rdot),
+                                                     false, false);
+    if (half == 0)
+      p.router_part[head_row * p.n + pos] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
 }
 
 template <int D, bool GLOBAL, int EPI>
 hipError_t launch_one(const Params& prm, hipStream_t s) {
+  static_assert(GLOBAL == (EPI == 2 || EPI == 3 || EPI == 5), "epilogue of the other branch");
   const int grid = prm.per_xcd * kNumXcd;
   hipLaunchKernelGGL((attn_bf16_kernel<D, GLOBAL, EPI>), dim3(grid), dim3(kThreads), 0, s,
                      prm);
@@ -478,6 +505,8 @@ hipError_t dispatch_epi(Epi epi, const Params& prm, hipStream_t s) {
     case Epi::LocalFused: return launch_one<D, false, 1>(prm, s);
     case Epi::GlobalAll: return launch_one<D, true, 2>(prm, s);
     case Epi::GlobalFused: return launch_one<D, true, 3>(prm, s);
+    case Epi::LocalRouted: return launch_one<D, false, 4>(prm, s);
+    case Epi::GlobalRouted: return launch_one<D, true, 5>(prm, s);
   }
   return hipErrorInvalidValue;
 }
@@ -485,7 +514,8 @@ hipError_t dispatch_epi(Epi epi, const Params& prm, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attn_bf16(const Dims& d, Epi epi, const AttnArgs& a, hipStream_t s) {
-  const bool global = epi == Epi::GlobalAll || epi == Epi::GlobalFused;
+  const bool global =
+      epi == Epi::GlobalAll || epi == Epi::GlobalFused || epi == Epi::GlobalRouted;
   const int R = global ? d.k : d.n;
   if (d.B == 0 || R == 0) return hipSuccess;
   Params prm;
@@ -517,6 +547,8 @@ hipError_t launch_attn_bf16(const Dims& d, Epi epi, const AttnArgs& a, hipStream
   prm.vo = d.vo;
   prm.lse_out = a.lse_out;
   prm.og_out = a.og_out;
+  prm.router_w = a.router_w;
+  prm.router_part = a.router_part;
   if (d.d == 64) return dispatch_epi<64>(epi, prm, s);
   if (d.d == 128) return dispatch_epi<128>(epi, prm, s);
   return hipErrorInvalidValue;

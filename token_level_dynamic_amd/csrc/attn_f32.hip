@@ -38,6 +38,8 @@ struct Params {
   View vq, vk, vv, vo;  // element strides of q, k, v, o
   float* lse_out;       // optional per-row log-sum-exp (natural log)
   float* og_out;        // optional f32 o_global rows (fused global)
+  const float* router_w;  // routed local: [Hq][D]
+  float* router_part;     // routed local: [B][Hq][n]
 };
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -122,7 +124,8 @@ __global__ __launch_bounds__(kWaves * 64) void attn_f32_kernel(Params p) {
     p.lse_out[head_row * R + (GLOBAL ? r : pos)] = (m_run + log2f(l_run)) * kLn2;
   float* const orow = p.out_io + b * p.vo.sb + h * p.vo.sh + (long long)pos * p.vo.st;
   float sig = 0.0f;
-  if (EPI == 3) sig = 1.0f / (1.0f + expf(-p.gate[(size_t)b * p.n + pos]));
+  if (EPI == 3 || EPI == 5) sig = 1.0f / (1.0f + expf(-p.gate[(size_t)b * p.n + pos]));
+  float rdot = 0.0f;
   int rk = -1;
   if (EPI == 1) rk = p.rank[(size_t)b * p.n + pos];
 #pragma unroll
@@ -131,6 +134,12 @@ __global__ __launch_bounds__(kWaves * 64) void attn_f32_kernel(Params p) {
     const float o = acc[c] * inv;
     if (EPI == 0) {
       p.out_f32[(head_row * p.n + pos) * D + e] = o;
+    } else if (EPI == 4) {
+      p.out_f32[(head_row * p.n + pos) * D + e] = o;
+      orow[e] = o;
+      rdot = fmaf(o, p.router_w[(size_t)h * D + e], rdot);
+    } else if (EPI == 5) {
+      orow[e] = p.scratch[(head_row * p.n + pos) * D + e] + sig * o;
     } else if (EPI == 2) {
       p.out_f32[(head_row * p.ksel + r) * D + e] = o;
     } else if (EPI == 1) {
@@ -141,6 +150,10 @@ __global__ __launch_bounds__(kWaves * 64) void attn_f32_kernel(Params p) {
       if (p.og_out) p.og_out[(head_row * p.ksel + r) * D + e] = o;
       orow[e] = l + sig * o;
     }
+  }
+  if (EPI == 4) {
+    rdot = wave_sum(rdot);
+    if (lane == 0) p.router_part[head_row * p.n + pos] = rdot;
   }
 }
 
@@ -159,6 +172,8 @@ hipError_t dispatch_epi(Epi epi, const Params& prm, hipStream_t s) {
     case Epi::LocalFused: return launch_one<D, false, 1>(prm, s);
     case Epi::GlobalAll: return launch_one<D, true, 2>(prm, s);
     case Epi::GlobalFused: return launch_one<D, true, 3>(prm, s);
+    case Epi::LocalRouted: return launch_one<D, false, 4>(prm, s);
+    case Epi::GlobalRouted: return launch_one<D, true, 5>(prm, s);
   }
   return hipErrorInvalidValue;
 }
@@ -166,7 +181,8 @@ hipError_t dispatch_epi(Epi epi, const Params& prm, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attn_f32(const Dims& d, Epi epi, const AttnArgs& a, hipStream_t s) {
-  const bool global = epi == Epi::GlobalAll || epi == Epi::GlobalFused;
+  const bool global =
+      epi == Epi::GlobalAll || epi == Epi::GlobalFused || epi == Epi::GlobalRouted;
   const int R = global ? d.k : d.n;
   if (d.B == 0 || R == 0) return hipSuccess;
   Params prm;
@@ -193,6 +209,8 @@ hipError_t launch_attn_f32(const Dims& d, Epi epi, const AttnArgs& a, hipStream_
   prm.vo = d.vo;
   prm.lse_out = a.lse_out;
   prm.og_out = a.og_out;
+  prm.router_w = a.router_w;
+  prm.router_part = a.router_part;
   if (d.d == 64) return dispatch_epi<64>(epi, prm, s);
   if (d.d == 128) return dispatch_epi<128>(epi, prm, s);
   return hipErrorInvalidValue;

@@ -29,7 +29,10 @@ enum class Epi : int {
   LocalAll = 0,    // o_local[b][h][i][:] (f32) for every row
   LocalFused = 1,  // rank[i] >= 0: scratch[b][h][rank][:] (f32); else o (io dtype)
   GlobalAll = 2,   // o_global[b][h][r][:] (f32), r = row in idx
-  GlobalFused = 3  // o = scratch[b][h][r] + sigmoid(gate) * o_global (io dtype)
+  GlobalFused = 3,  // o = scratch[b][h][r] + sigmoid(gate) * o_global (io dtype)
+  LocalRouted = 4,  // o_local[b][h][i][:] (f32) and o (io dtype) for every row, and
+                    // router_part[b][h][i] = <router_w[h], o_local row>
+  GlobalRouted = 5  // o = scratch[b][h][i] + sigmoid(gate) * o_global (io dtype)
 };
 
 struct AttnArgs {
@@ -45,6 +48,8 @@ struct AttnArgs {
   float* lse_out;        // optional: natural-log log-sum-exp of each row's
                          // scaled scores (local [B][Hq][n], global [B][Hq][k])
   float* og_out;         // optional, fused global: o_global [B][Hq][k][d] f32
+  const float* router_w; // routed local: [Hq][d] f32
+  float* router_part;    // routed local: [B][Hq][n] f32
 };
 
 // Everything the backward kernels read and write. q, k, v, o and dout are
@@ -97,6 +102,10 @@ hipError_t launch_attn_bf16(const Dims& d, Epi epi, const AttnArgs& a,
 
 hipError_t launch_attn_f32(const Dims& d, Epi epi, const AttnArgs& a,
                            hipStream_t s);
+
+// gate[b][i] = bias + sum_h part[b][h][i] (heads summed in order).
+hipError_t launch_router_sum(const Dims& d, const float* part, float bias, float* gate,
+                             hipStream_t s);
 
 hipError_t launch_combine(const Dims& d, const float* o_local,
                           const float* o_global, const int32_t* rank,

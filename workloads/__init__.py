@@ -202,6 +202,13 @@ def make_dout(w: Workload, seed: int = 0):
     return x, None
 
 
+def make_router(w: Workload, seed: int = 0):
+    """Synthetic router weights for the routed forward: w [Hq, d] with N(0,1)
+    entries from a stream of its own (seed, 0x50), and a bias of 0.25."""
+    rng = np.random.default_rng([seed, 0x50])
+    return rng.standard_normal((w.Hq, w.d), dtype=np.float32), 0.25
+
+
 def _skip_normals(rng: np.random.Generator, count: int, chunk: int = 1 << 24) -> None:
     while count > 0:
         m = min(count, chunk)
