@@ -7,10 +7,11 @@ product. See ``oracle/logo.py`` for the forward's definition and the passages
 each step follows, and ``oracle/backward.py`` for its chain rule (gradients
 of q, k, v and the gate, and the statistics a training forward saves), and
 ``oracle/router.py`` for the routed forward (the gate computed from the local
-branch's output).
+branch's output), and ``oracle/decode.py`` for the threshold budget
+controller and the decode step.
 
 Parity status: every function here is pinned (tests/test_oracle.py,
-tests/test_oracle_backward.py, tests/test_oracle_router.py); none is
+tests/test_oracle_backward.py, tests/test_oracle_router.py, tests/test_oracle_decode.py); none is
 "parity unpinned" against the mathematics, though the pages themselves print
 no worked numbers for this method.
 """
@@ -30,3 +31,4 @@ from .logo import (  # noqa: F401
 )
 from . import backward  # noqa: F401,E402
 from . import router  # noqa: F401,E402
+from . import decode  # noqa: F401,E402
