@@ -324,6 +324,95 @@ def routed_bench(args, torch, T, w, inp, p, q, k, v, dev) -> int:
     return 0
 
 
+def decode_bench(args, torch, T) -> int:
+    """One step = logo_decode_step: controller, chunked decode, reduction."""
+    from workloads import DECODE_WORKLOADS, make_decode_inputs
+    import oracle.decode as DC   # the N(0,1) quantile for the threshold (a number, no kernel)
+    cfg = DECODE_WORKLOADS["decode128k"]
+    B, Hq, Hkv, cap, d, W = (cfg[x] for x in ("B", "Hq", "Hkv", "cap", "d", "window"))
+    tau0 = DC.normal_quantile(1.0 - cfg["rho"])
+    inp = make_decode_inputs(B, Hq, Hkv, cap, d, cfg["dtype"], seed=args.seed,
+                             tau=np.full(B, tau0, np.float32))
+    dev = torch.device("cuda:0")
+
+    def cv(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = cv(inp.bits["q"]), cv(inp.bits["k"]), cv(inp.bits["v"])
+    del inp.k, inp.v, inp.bits
+    lens = torch.from_numpy(inp.lens).to(dev)
+    gate = torch.from_numpy(inp.gate).to(dev)
+    tau = torch.from_numpy(inp.tau).to(dev)
+    # eta = 0: the controller is frozen so every timed step makes the same decisions
+    p = T.make_decode_problem(B, Hq, Hkv, cap, d, W, cfg["rho"], eta=0.0, dtype=cfg["dtype"])
+    o = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev)
+    sel = torch.empty(B, dtype=torch.uint8, device=dev)
+    ws = torch.empty(T.logo_decode_workspace_size(p), dtype=torch.uint8, device=dev)
+
+    def step():
+        T.logo_decode_step(p, q, k, v, lens, gate, tau, o, sel, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    T.logo_profile_begin()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    stage_ms, stage_n = T.logo_profile_end()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    per_step = per_step_timing(torch, step, stream, args.steps)
+    selected = sel.cpu().numpy().astype(bool)
+    nl = inp.lens.astype(np.float64)
+    keys = np.where(selected, nl, np.minimum(W, nl))      # cached keys read per (b, kv head)
+    # algorithmic bytes: each needed cached key and value once (bf16), q and o once
+    algo = float(keys.sum()) * Hkv * d * 2 * 2 + 2.0 * B * Hq * d * 2
+    dec_ms = stage_ms[T.STAGES.index("decode")] / max(stage_n[T.STAGES.index("decode")], 1)
+    gbs = algo / (dec_ms * 1e-3) / 1e9
+    result = {
+        "metric": "decode step of 8 sequences with 128K caches: effective HBM GB/s (cached "
+                  "K/V bytes the step must read over its time), ms per step",
+        "value": round(algo / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic",
+        "config": {"workload": "decode128k", "B": B, "Hq": Hq, "Hkv": Hkv, "cap": cap, "d": d,
+                   "window": W, "rho": cfg["rho"], "tau": round(tau0, 6), "eta": 0.0,
+                   "selected": int(selected.sum()), "seed": args.seed, "mode": "decode",
+                   "parallelism": "none (1 GPU)"},
+        "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
+        "algorithmic_bytes": algo,
+        "stage_ms_avg": {s: round(stage_ms[j] / stage_n[j], 4)
+                         for j, s in enumerate(T.STAGES) if stage_n[j]},
+        "per_step_ms": per_step,
+        "roofline": {
+            "kernel": "decode_partial_kernel + decode_reduce_kernel",
+            "bound": "hbm",
+            "achieved": round(gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": algo,
+            "avg_launch_ms": round(dec_ms, 4),
+        },
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -334,10 +423,12 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--mode", choices=("forward", "train", "routed"), default="forward",
+    ap.add_argument("--mode", choices=("forward", "train", "routed", "decode"),
+                    default="forward",
                     help="forward: one logo_forward per step (the headline); train: one "
                          "logo_forward_train + logo_backward per step; routed: one "
-                         "logo_forward_routed per step (gate computed from the local branch)")
+                         "logo_forward_routed per step (gate computed from the local branch); "
+                         "decode: one logo_decode_step of the 128K decode workload per step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (read N, write N "
                          "bytes) so HBM counters can be scaled to bytes")
@@ -365,6 +456,8 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
 
+    if args.mode == "decode":
+        return decode_bench(args, torch, T)
     w = get_workload(args.workload)
     if args.rho is not None:
         w = w.with_(rho=args.rho)

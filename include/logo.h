@@ -226,6 +226,68 @@ logo_status logo_forward_routed(const logo_problem* p, const void* q, const void
                                 int32_t* rank, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* ---- threshold budget controller and the decode step ------------------
+ *
+ * LoGo (abstract) holds the target global ratio with a threshold-based
+ * budget controller; "Learning When to Attend" (section "Empirical
+ * Validation and System Optimization") reads the full context at decode
+ * time only for tokens routed to it. Readings (the pages give no formulas):
+ * a token is selected iff gate > tau (NaN never); the running controller
+ * moves tau by eta (selected - rho) after each decision, a quantile tracker
+ * whose selected fraction settles at rho using only past tokens. */
+
+/* Calibrated threshold from a prefill's exact top-k selection: tau[b] is the
+ * largest gate[b][i] with mask[b][i] == 0 (NaN excluded), -inf when every
+ * token was selected, so "gate > tau" reproduces the selection on distinct
+ * logits. gate, mask [B][n]; tau [B] float32 out. n >= 1. */
+logo_status logo_calibrate_threshold(const logo_problem* p, const float* gate,
+                                     const uint8_t* mask, float* tau, void* stream);
+
+/* Threshold selection of whole sequences: mask[b][i] = gate[b][i] > tau[b];
+ * idx [B][n] int32 gets the selected positions ascending, then -1;
+ * count [B] int32 the number selected. (The budget is not enforced: the
+ * count follows the logits.) */
+logo_status logo_select_threshold(const logo_problem* p, const float* gate,
+                                  const float* tau, uint8_t* mask, int32_t* idx,
+                                  int32_t* count, void* stream);
+
+/* One decode step per sequence. */
+typedef struct {
+  int64_t B;       /* sequences                                              */
+  int64_t Hq;      /* query heads; Hq / Hkv in {1, 2, 4, 7, 8}               */
+  int64_t Hkv;     /* key/value heads                                        */
+  int64_t cap;     /* cache capacity (positions per sequence and kv head)    */
+  int64_t d;       /* head dimension: 64 or 128                              */
+  int64_t window;  /* W >= 1                                                 */
+  double rho;      /* target global ratio in [0, 1]                          */
+  float eta;       /* controller step >= 0 (0 freezes tau)                   */
+  float scale;     /* score scale; 0 means 1/sqrt(d)                         */
+  int32_t dtype;   /* logo_dtype of q, caches and o                          */
+} logo_decode_problem;
+
+/* Bytes of workspace logo_decode_step needs (per-chunk partial softmax
+ * states: B*Hq*ceil(cap/2048)*2*(d+2)*4). */
+logo_status logo_decode_workspace_size(const logo_decode_problem* p, size_t* bytes);
+
+/* The newest token of each sequence attends over its cache:
+ *   q        [B][Hq][d]           dtype
+ *   k_cache, v_cache [B][Hkv][cap][d] dtype, contiguous; positions
+ *            0 .. lens[b]-1 valid, the newest token's own key/value included
+ *   lens     [B] int32 in [1, cap] (values outside are clamped into it)
+ *   gate     [B] float32 logit of the newest token
+ *   tau      [B] float32 threshold, read then updated in place:
+ *            selected[b] = gate[b] > tau[b]; tau[b] += eta (selected[b] - rho)
+ *   o        [B][Hq][d] dtype: o_local over the last W cached keys, plus
+ *            sigmoid(gate) o_global over the whole cache when selected
+ *   selected [B] uint8 out.
+ * Reads each needed cached key and value once (the kv head's query heads
+ * share it); unselected sequences read only their window. */
+logo_status logo_decode_step(const logo_decode_problem* p, const void* q,
+                             const void* k_cache, const void* v_cache,
+                             const int32_t* lens, const float* gate, float* tau,
+                             void* o, uint8_t* selected, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* logo_status_string(logo_status s);
 
@@ -235,11 +297,11 @@ const char* logo_last_error(void);
 /* Kernel timing for measurement. Between logo_profile_begin() and
  * logo_profile_end(), logo_forward records a HIP event pair around each of
  * its kernels on the caller's stream (at most 4096 pairs; later launches go
- * unrecorded); so do logo_forward_train, logo_backward and
- * logo_forward_routed. logo_profile_end() waits for those events and writes,
+ * unrecorded); so do logo_forward_train, logo_backward,
+ * logo_forward_routed and logo_decode_step. logo_profile_end() waits for those events and writes,
  * per stage (0 select, 1 local, 2 global, 3 combine, 4 backward row terms and
- * dgate, 5 backward dk/dv, 6 backward dq, 7 router logits), the summed
- * milliseconds
+ * dgate, 5 backward dk/dv, 6 backward dq, 7 router logits, 8 decode: chunk
+ * partials and their reduction), the summed milliseconds
  * and the number of launches into arrays of `n_stages` entries. */
 logo_status logo_profile_begin(void);
 logo_status logo_profile_end(double* stage_ms, int64_t* stage_launches,

@@ -17,7 +17,11 @@ from ._lib import (  # noqa: F401
     lib,
     logo_backward,
     logo_backward_workspace_size,
+    logo_calibrate_threshold,
     logo_combine,
+    logo_decode_step,
+    logo_decode_workspace_size,
+    logo_decode_problem,
     logo_forward,
     logo_forward_routed,
     logo_forward_train,
@@ -28,8 +32,10 @@ from ._lib import (  # noqa: F401
     logo_profile_end,
     logo_routed_workspace_size,
     logo_select_queries,
+    logo_select_threshold,
     logo_target_count,
     logo_workspace_size,
+    make_decode_problem,
     make_problem,
     view_strides,
 )

@@ -24,7 +24,7 @@ LOGO_ERR_HIP = 4
 LOGO_F32 = 0
 LOGO_BF16 = 1
 STAGES = ("select", "local", "global", "combine", "bwd_prep", "bwd_dkdv", "bwd_dq",
-          "router")
+          "router", "decode")
 
 
 class LogoError(RuntimeError):
@@ -73,6 +73,29 @@ def view_strides(t: torch.Tensor) -> Tuple[int, int, int]:
     return t.stride(0), t.stride(1), t.stride(2)
 
 
+class logo_decode_problem(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int64),
+        ("Hq", ctypes.c_int64),
+        ("Hkv", ctypes.c_int64),
+        ("cap", ctypes.c_int64),
+        ("d", ctypes.c_int64),
+        ("window", ctypes.c_int64),
+        ("rho", ctypes.c_double),
+        ("eta", ctypes.c_float),
+        ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+def make_decode_problem(B: int, Hq: int, Hkv: int, cap: int, d: int, window: int, rho: float,
+                        eta: float = 0.0, scale: float = 0.0,
+                        dtype: str = "bf16") -> logo_decode_problem:
+    dt = {"bf16": LOGO_BF16, "f32": LOGO_F32}[dtype]
+    return logo_decode_problem(B, Hq, Hkv, cap, d, window, float(rho), float(eta), float(scale),
+                               dt)
+
+
 _lib = None
 _P = ctypes.c_void_p
 _PP = ctypes.POINTER(logo_problem)
@@ -92,6 +115,12 @@ _SIGS = {
     "logo_routed_workspace_size": (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_size_t)]),
     "logo_forward_routed": (ctypes.c_int, [_PP, _P, _P, _P, _P, ctypes.c_float] + [_P] * 6 +
                             [ctypes.c_size_t, _P]),
+    "logo_decode_workspace_size": (ctypes.c_int, [ctypes.POINTER(logo_decode_problem),
+                                                   ctypes.POINTER(ctypes.c_size_t)]),
+    "logo_decode_step": (ctypes.c_int, [ctypes.POINTER(logo_decode_problem)] + [_P] * 9 +
+                         [ctypes.c_size_t, _P]),
+    "logo_calibrate_threshold": (ctypes.c_int, [_PP, _P, _P, _P, _P]),
+    "logo_select_threshold": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P]),
     "logo_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "logo_last_error": (ctypes.c_char_p, []),
     "logo_profile_begin": (ctypes.c_int, []),
@@ -373,6 +402,54 @@ def alloc_routed_buffers(p: logo_problem, device="cuda") -> dict:
         "rank": torch.empty((p.B, p.n), dtype=torch.int32, device=device),
         "workspace": torch.empty((ws,), dtype=torch.uint8, device=device) if ws else None,
     }
+
+
+def logo_decode_workspace_size(p: logo_decode_problem) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().logo_decode_workspace_size(ctypes.byref(p), ctypes.byref(out)),
+           "logo_decode_workspace_size")
+    return int(out.value)
+
+
+def logo_decode_step(p: logo_decode_problem, q, k_cache, v_cache, lens, gate, tau, o, selected,
+                     workspace, stream=None) -> None:
+    """One decode step (see include/logo.h); tau is updated in place."""
+    dt = torch.bfloat16 if p.dtype == LOGO_BF16 else torch.float32
+    _expect(q, "q", dt, p.B * p.Hq * p.d)
+    _expect(k_cache, "k_cache", dt, p.B * p.Hkv * p.cap * p.d)
+    _expect(v_cache, "v_cache", dt, p.B * p.Hkv * p.cap * p.d)
+    _expect(lens, "lens", torch.int32, p.B)
+    _expect(gate, "gate", torch.float32, p.B)
+    _expect(tau, "tau", torch.float32, p.B)
+    _expect(o, "o", dt, p.B * p.Hq * p.d)
+    _expect(selected, "selected", torch.uint8, p.B)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().logo_decode_step(
+        ctypes.byref(p), _ptr(q, "q"), _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache"),
+        _ptr(lens, "lens"), _ptr(gate, "gate"), _ptr(tau, "tau"), _ptr(o, "o"),
+        _ptr(selected, "selected"), _ptr(workspace, "workspace"), ws_bytes, _stream(stream)),
+        "logo_decode_step")
+
+
+def logo_calibrate_threshold(p: logo_problem, gate, mask, tau, stream=None) -> None:
+    _expect(gate, "gate", torch.float32, p.B * p.n)
+    _expect(mask, "mask", torch.uint8, p.B * p.n)
+    _expect(tau, "tau", torch.float32, p.B)
+    _check(lib().logo_calibrate_threshold(ctypes.byref(p), _ptr(gate, "gate"), _ptr(mask, "mask"),
+                                          _ptr(tau, "tau"), _stream(stream)),
+           "logo_calibrate_threshold")
+
+
+def logo_select_threshold(p: logo_problem, gate, tau, mask, idx, count, stream=None) -> None:
+    _expect(gate, "gate", torch.float32, p.B * p.n)
+    _expect(tau, "tau", torch.float32, p.B)
+    _expect(mask, "mask", torch.uint8, p.B * p.n)
+    _expect(idx, "idx", torch.int32, p.B * p.n)
+    _expect(count, "count", torch.int32, p.B)
+    _check(lib().logo_select_threshold(ctypes.byref(p), _ptr(gate, "gate"), _ptr(tau, "tau"),
+                                       _ptr(mask, "mask"), _ptr(idx, "idx"),
+                                       _ptr(count, "count"), _stream(stream)),
+           "logo_select_threshold")
 
 
 def logo_profile_begin() -> None:

@@ -22,7 +22,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblogo.so")
 
 SOURCES = ["abi.cpp", "select.hip", "attn_bf16.hip", "attn_f32.hip", "combine.hip",
-           "backward_prep.hip", "backward_bf16.hip", "backward_f32.hip", "router.hip"]
+           "backward_prep.hip", "backward_bf16.hip", "backward_f32.hip", "router.hip",
+           "decode.hip"]
 ARCH = "gfx950"
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -571,6 +571,120 @@ logo_status logo_forward_routed(const logo_problem* p, const void* q, const void
   return LOGO_OK;
 }
 
+logo_status check_decode(const logo_decode_problem* p, logo::DecodeDims* out) {
+  if (!p) return fail(LOGO_ERR_INVALID_ARG, "problem is NULL");
+  if (p->B < 0) return fail(LOGO_ERR_INVALID_ARG, "B must be >= 0");
+  if (p->Hq < 1 || p->Hkv < 1 || p->Hq % p->Hkv != 0)
+    return fail(LOGO_ERR_INVALID_ARG, "Hq must be a positive multiple of Hkv");
+  if (p->cap < 1) return fail(LOGO_ERR_INVALID_ARG, "cache capacity must be >= 1");
+  if (p->window < 1) return fail(LOGO_ERR_INVALID_ARG, "window must be >= 1");
+  if (std::isnan(p->rho) || p->rho < 0.0 || p->rho > 1.0)
+    return fail(LOGO_ERR_INVALID_ARG, "rho must be in [0, 1]");
+  if (!std::isfinite(p->eta) || p->eta < 0.0f)
+    return fail(LOGO_ERR_INVALID_ARG, "eta must be finite and >= 0");
+  if (!std::isfinite(p->scale) || p->scale < 0.0f)
+    return fail(LOGO_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if (p->dtype != LOGO_F32 && p->dtype != LOGO_BF16)
+    return fail(LOGO_ERR_INVALID_ARG, "dtype must be LOGO_F32 or LOGO_BF16");
+  if (p->d != 64 && p->d != 128)
+    return fail(LOGO_ERR_UNSUPPORTED, "head dimension %lld not supported (64 or 128)",
+                (long long)p->d);
+  if (!logo::decode_group_supported((int)(p->Hq / p->Hkv)))
+    return fail(LOGO_ERR_UNSUPPORTED, "query heads per kv head %lld not built (1, 2, 4, 7, 8)",
+                (long long)(p->Hq / p->Hkv));
+  if (p->cap >= (int64_t(1) << 30) || p->B >= (int64_t(1) << 20) || p->Hq >= (int64_t(1) << 16))
+    return fail(LOGO_ERR_UNSUPPORTED, "sizes beyond the supported range");
+  out->B = (int)p->B;
+  out->Hq = (int)p->Hq;
+  out->Hkv = (int)p->Hkv;
+  out->cap = (int)p->cap;
+  out->d = (int)p->d;
+  out->window = (int)std::min<int64_t>(p->window, int64_t(1) << 30);
+  out->rho = p->rho;
+  out->eta = p->eta;
+  out->scale = p->scale == 0.0f ? (float)(1.0 / std::sqrt((double)p->d)) : p->scale;
+  out->dtype = p->dtype;
+  return LOGO_OK;
+}
+
+logo_status logo_decode_workspace_size(const logo_decode_problem* p, size_t* bytes) {
+  logo::DecodeDims d;
+  LOGO_TRY(check_decode(p, &d));
+  if (!bytes) return fail(LOGO_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = d.B == 0 ? 0 : logo::decode_partial_bytes(d);
+  return LOGO_OK;
+}
+
+logo_status logo_decode_step(const logo_decode_problem* p, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* lens, const float* gate,
+                             float* tau, void* o, uint8_t* selected, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  logo::DecodeDims d;
+  LOGO_TRY(check_decode(p, &d));
+  if (d.B == 0) return LOGO_OK;
+  LOGO_TRY(need_ptr(q, "q"));
+  LOGO_TRY(need_ptr(k_cache, "k_cache"));
+  LOGO_TRY(need_ptr(v_cache, "v_cache"));
+  LOGO_TRY(need_ptr(lens, "lens"));
+  LOGO_TRY(need_ptr(gate, "gate"));
+  LOGO_TRY(need_ptr(tau, "tau"));
+  LOGO_TRY(need_ptr(o, "o"));
+  LOGO_TRY(need_ptr(selected, "selected"));
+  const size_t need = logo::decode_partial_bytes(d);
+  if (!workspace || workspace_bytes < need)
+    return fail(LOGO_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(LOGO_ERR_INVALID_ARG, "workspace misaligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = logo::launch_decode_ctrl(d, gate, tau, selected, s);
+  if (e != hipSuccess) return hip_fail(e, "controller launch");
+  logo::DecodeArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.lens = lens;
+  a.gate = gate;
+  a.selected = selected;
+  a.part = static_cast<float*>(workspace);
+  a.o = o;
+  {
+    StageTimer tm(8, s);
+    e = logo::launch_decode(d, a, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return LOGO_OK;
+}
+
+logo_status logo_calibrate_threshold(const logo_problem* p, const float* gate,
+                                     const uint8_t* mask, float* tau, void* stream) {
+  logo::Dims d;
+  LOGO_TRY(check_problem(p, &d));
+  if (d.B == 0) return LOGO_OK;
+  LOGO_TRY(need_ptr(gate, "gate"));
+  LOGO_TRY(need_ptr(mask, "mask"));
+  LOGO_TRY(need_ptr(tau, "tau"));
+  if (d.n == 0) return fail(LOGO_ERR_INVALID_ARG, "n must be >= 1 to calibrate");
+  hipError_t e = logo::launch_calibrate(d, gate, mask, tau, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "calibrate launch");
+  return LOGO_OK;
+}
+
+logo_status logo_select_threshold(const logo_problem* p, const float* gate, const float* tau,
+                                  uint8_t* mask, int32_t* idx, int32_t* count, void* stream) {
+  logo::Dims d;
+  LOGO_TRY(check_problem(p, &d));
+  if (empty(d)) return LOGO_OK;
+  LOGO_TRY(need_ptr(gate, "gate"));
+  LOGO_TRY(need_ptr(tau, "tau"));
+  LOGO_TRY(need_ptr(mask, "mask"));
+  LOGO_TRY(need_ptr(idx, "idx"));
+  LOGO_TRY(need_ptr(count, "count"));
+  hipError_t e = logo::launch_select_threshold(d, gate, tau, mask, idx, count,
+                                               static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "threshold select launch");
+  return LOGO_OK;
+}
+
 logo_status logo_profile_begin(void) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
   g_prof.on = true;

@@ -107,6 +107,34 @@ hipError_t launch_attn_f32(const Dims& d, Epi epi, const AttnArgs& a,
 hipError_t launch_router_sum(const Dims& d, const float* part, float bias, float* gate,
                              hipStream_t s);
 
+// ---- threshold controller and decode step --------------------------------
+struct DecodeDims {
+  int B, Hq, Hkv, cap, d, window;
+  double rho;
+  float eta;
+  float scale;
+  int dtype;
+};
+struct DecodeArgs {
+  const void* q;          // [B][Hq][d]
+  const void* k_cache;    // [B][Hkv][cap][d]
+  const void* v_cache;
+  const int32_t* lens;    // [B]
+  const float* gate;      // [B]
+  const uint8_t* selected;
+  float* part;            // workspace: chunk partials
+  void* o;                // [B][Hq][d]
+};
+bool decode_group_supported(int G);
+size_t decode_partial_bytes(const DecodeDims& d);
+hipError_t launch_decode_ctrl(const DecodeDims& d, const float* gate, float* tau,
+                              uint8_t* selected, hipStream_t s);
+hipError_t launch_decode(const DecodeDims& d, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_calibrate(const Dims& d, const float* gate, const uint8_t* mask, float* tau,
+                            hipStream_t s);
+hipError_t launch_select_threshold(const Dims& d, const float* gate, const float* tau,
+                                   uint8_t* mask, int32_t* idx, int32_t* count, hipStream_t s);
+
 hipError_t launch_combine(const Dims& d, const float* o_local,
                           const float* o_global, const int32_t* rank,
                           const float* gate, void* o, hipStream_t s);

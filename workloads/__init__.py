@@ -209,6 +209,44 @@ def make_router(w: Workload, seed: int = 0):
     return rng.standard_normal((w.Hq, w.d), dtype=np.float32), 0.25
 
 
+@dataclasses.dataclass
+class DecodeInputs:
+    q: np.ndarray          # [B, Hq, d] values (bf16-exact for bf16)
+    k: np.ndarray          # [B, Hkv, cap, d]
+    v: np.ndarray
+    lens: np.ndarray       # [B] int32
+    gate: np.ndarray       # [B] float32
+    tau: np.ndarray        # [B] float32
+    bits: dict             # bf16 bit patterns of q, k, v (bf16 only)
+
+
+DECODE_WORKLOADS = {
+    # one decode step of the 128K GQA layer: 8 sequences with full caches;
+    # gates N(0,1), threshold at the N(0,1) quantile of 1 - rho, controller frozen
+    "decode128k": dict(B=8, Hq=28, Hkv=4, cap=131072, d=128, window=4096, rho=0.25,
+                       dtype="bf16"),
+}
+
+
+def make_decode_inputs(B, Hq, Hkv, cap, d, dtype="bf16", seed=0, lens=None, tau=None):
+    """Seeded decode-step inputs: N(0,1) q, caches and gates (stream (seed, 0xDEC)),
+    lens = cap unless given, tau = 0 unless given."""
+    rng = np.random.default_rng([seed, 0xDEC])
+    q = rng.standard_normal((B, Hq, d), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, cap, d), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, cap, d), dtype=np.float32)
+    gate = rng.standard_normal(B, dtype=np.float32)
+    bits = {}
+    if dtype == "bf16":
+        for name in ("q", "k", "v"):
+            x = {"q": q, "k": k, "v": v}[name]
+            bits[name] = bf16_bits(x)
+        q, k, v = (bits_to_f32(bits[x]) for x in ("q", "k", "v"))
+    lens = np.full(B, cap, np.int32) if lens is None else np.asarray(lens, np.int32)
+    tau = np.zeros(B, np.float32) if tau is None else np.asarray(tau, np.float32)
+    return DecodeInputs(q, k, v, lens, gate, tau, bits)
+
+
 def _skip_normals(rng: np.random.Generator, count: int, chunk: int = 1 << 24) -> None:
     while count > 0:
         m = min(count, chunk)
