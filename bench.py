@@ -326,11 +326,12 @@ def routed_bench(args, torch, T, w, inp, p, q, k, v, dev) -> int:
 
 def decode_bench(args, torch, T) -> int:
     """One step = logo_decode_step: controller, chunked decode, reduction."""
+    from statistics import NormalDist
     from workloads import DECODE_WORKLOADS, make_decode_inputs
-    import oracle.decode as DC   # the N(0,1) quantile for the threshold (a number, no kernel)
     cfg = DECODE_WORKLOADS["decode128k"]
     B, Hq, Hkv, cap, d, W = (cfg[x] for x in ("B", "Hq", "Hkv", "cap", "d", "window"))
-    tau0 = DC.normal_quantile(1.0 - cfg["rho"])
+    # threshold at the N(0,1) quantile the logits exceed with probability rho
+    tau0 = NormalDist().inv_cdf(1.0 - cfg["rho"])
     inp = make_decode_inputs(B, Hq, Hkv, cap, d, cfg["dtype"], seed=args.seed,
                              tau=np.full(B, tau0, np.float32))
     dev = torch.device("cuda:0")
