@@ -24,7 +24,7 @@
 namespace logo {
 namespace {
 
-constexpr int kChunk = 2048;      // keys per workgroup
+constexpr int kChunk = 256;       // keys per workgroup
 constexpr int kSub = 64;          // keys per wave step (one per lane)
 constexpr int kDecWaves = 4;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -38,19 +38,38 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-template <bool BF16>
-__device__ __forceinline__ float ld_io(const void* base, long long i) {
-  if (BF16) return __uint_as_float((uint32_t)static_cast<const uint16_t*>(base)[i] << 16);
-  return static_cast<const float*>(base)[i];
+// Wave-wide max / sum without LDS permutes: rotations within each 16-lane
+// DPP row, then the row pairs and the wave halves exchanged with
+// v_permlane16_swap / v_permlane32_swap; every lane gets the result.
+template <int N>  // rotate right by N lanes within each 16-lane row
+__device__ __forceinline__ float dpp_ror(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               0x120 + N, 0xf, 0xf, false));
 }
-
+#define LOGO_DPP_ROR(x, n) dpp_ror<(n)>(x)
 __device__ __forceinline__ float wmax(float x) {
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-  return x;
+  x = fmaxf(x, LOGO_DPP_ROR(x, 8));
+  x = fmaxf(x, LOGO_DPP_ROR(x, 4));
+  x = fmaxf(x, LOGO_DPP_ROR(x, 2));
+  x = fmaxf(x, LOGO_DPP_ROR(x, 1));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 __device__ __forceinline__ float wsum(float x) {
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
+  x += LOGO_DPP_ROR(x, 8);
+  x += LOGO_DPP_ROR(x, 4);
+  x += LOGO_DPP_ROR(x, 2);
+  x += LOGO_DPP_ROR(x, 1);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
 __device__ __forceinline__ int clamp_len(int len, int cap) { return min(max(len, 1), cap); }
@@ -77,125 +96,210 @@ struct DecParams {
   float scale_log2;
 };
 
+// Sum over the 16 lanes of a DPP row (rotations by 8, 4, 2, 1 within the
+// row): every lane of the row gets the row's total.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += LOGO_DPP_ROR(x, 8);
+  x += LOGO_DPP_ROR(x, 4);
+  x += LOGO_DPP_ROR(x, 2);
+  x += LOGO_DPP_ROR(x, 1);
+  return x;
+}
+
+// EPL consecutive elements of an I/O-dtype row as float (16 B for bf16 x 8,
+// 8 B for bf16 x 4, two or one float4 for float32).
+template <int EPL, bool BF16>
+__device__ __forceinline__ void load_seg(const void* base, long long off, float (&x)[EPL]) {
+  if (EPL == 1) {
+    x[0] = BF16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(base)[off] << 16)
+                : static_cast<const float*>(base)[off];
+    return;
+  }
+  if (BF16) {
+    const uint16_t* pp = static_cast<const uint16_t*>(base) + off;
+    uint32_t w[EPL / 2 > 0 ? EPL / 2 : 1];
+    if (EPL == 8) {
+      const uint4 u = *reinterpret_cast<const uint4*>(pp);
+      w[0] = u.x; w[1] = u.y; w[2 % (EPL / 2)] = u.z; w[3 % (EPL / 2)] = u.w;
+    } else {
+      const uint2 u = *reinterpret_cast<const uint2*>(pp);
+      w[0] = u.x; w[1] = u.y;
+    }
+#pragma unroll
+    for (int t = 0; t < EPL / 2; ++t) {
+      x[(2 * t) % EPL] = __uint_as_float(w[t] << 16);
+      x[(2 * t + 1) % EPL] = __uint_as_float(w[t] & 0xffff0000u);
+    }
+  } else {
+    const float4* f = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+#pragma unroll
+    for (int t = 0; t < EPL / 4; ++t) {
+      const float4 a = f[t];
+      x[(4 * t) % EPL] = a.x;
+      x[(4 * t + 1) % EPL] = a.y;
+      x[(4 * t + 2) % EPL] = a.z;
+      x[(4 * t + 3) % EPL] = a.w;
+    }
+  }
+}
+
 // One workgroup per (b, kv head, chunk); waves take 64-key steps of the chunk
-// in turn, lane = key for the scores, lane = d column pair for the values.
+// in turn. Within a step the 16 lanes of each DPP row share one key at a
+// time (4 keys per wave instruction): lane (row r, position s) holds
+// elements [s*EPL, s*EPL + EPL) of the G queries in registers, loads the same
+// slice of the key row (coalesced 16-lane loads), and the row sums its
+// partial dot products with DPP rotates. The values use the same key
+// assignment, each lane accumulating its EPL output elements. Loads are
+// issued kBatch iterations at a time, so each wave keeps kBatch rows of
+// 16 lanes in flight.
+//
+// Each workgroup does one branch of one chunk: the first B*Hkv*nchunk
+// workgroups the local branch (chunks that overlap the window), the rest the
+// global branch (every chunk of a selected sequence), all in one launch and
+// with one set of accumulators (the window's keys are read twice for a
+// selected sequence: a few percent more bytes for twice the occupancy).
+// Workgroups with nothing to do exit at once.
+constexpr int kBatch = 4;
+
 template <int D, int G, bool BF16>
 __global__ __launch_bounds__(kDecWaves * 64) void decode_partial_kernel(DecParams p) {
-  constexpr int NC = D / 64;  // d columns per lane
-  __shared__ float qs[G][D];
-  __shared__ float pw[kDecWaves][2][G][kSub];  // probabilities of a wave step
-  __shared__ float red[kDecWaves][2][G][D + 2];
-  const int c = blockIdx.x % p.nchunk;
-  const int bk = blockIdx.x / p.nchunk;
+  constexpr int EPL = D / 16;   // elements per lane
+  constexpr int NB = 1;
+  __shared__ __attribute__((aligned(16))) float qsh[G][D];  // the G queries
+  __shared__ float sbuf[kDecWaves][G][kSub];       // scores of a wave step
+  __shared__ float pw[kDecWaves][NB][G][kSub];     // probabilities of a wave step
+  __shared__ float red[kDecWaves][NB][G][D + 2];
+  const int per_kind = p.B * p.Hkv * p.nchunk;
+  const bool loc = (int)blockIdx.x < per_kind;  // uniform: local or global branch
+  const int wid = loc ? (int)blockIdx.x : (int)blockIdx.x - per_kind;
+  const int c = wid % p.nchunk;
+  const int bk = wid / p.nchunk;
   const int b = bk / p.Hkv, hk = bk % p.Hkv;
   const int i = clamp_len(p.lens[b], p.cap) - 1;
   const int lo = max(0, i - p.W + 1);
   const bool sel = p.selected[b] != 0;
   const int c0 = c * kChunk, c1 = min(c0 + kChunk, i + 1);  // keys [c0, c1)
-  const bool do_loc = c0 <= i && c1 > lo;
-  const bool do_glb = sel && c0 <= i;
-  if (!do_loc && !do_glb) return;  // uniform over the workgroup: no barrier is skipped
+  const bool in_win = c0 <= i && c1 > lo;
+  // uniform over the workgroup: no barrier is skipped
+  if (loc ? !in_win : (!sel || c0 > i)) return;
+  const bool act[1] = {true};
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  for (int e = tid; e < G * D; e += kDecWaves * 64)
-    qs[e / D][e % D] = ld_io<BF16>(p.q, ((long long)b * p.Hq + hk * G + e / D) * D + e % D);
+  const int grp = lane >> 4, seg = lane & 15;
+  for (int e = tid; e < G * D; e += kDecWaves * 64) {
+    float x[1];
+    load_seg<1, BF16>(p.q, ((long long)b * p.Hq + hk * G) * D + e, x);
+    qsh[e / D][e % D] = x[0];
+  }
   __syncthreads();
   const long long kvb = ((long long)b * p.Hkv + hk) * p.cap;
-  // online state per head and branch (0 local, 1 global)
-  float m[2][G], l[2][G], acc[2][G][NC];
+  float m[NB][G], l[NB][G], acc[NB][G][EPL];
 #pragma unroll
-  for (int br = 0; br < 2; ++br)
+  for (int br = 0; br < NB; ++br)
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       m[br][g] = kNeg;
       l[br][g] = 0.0f;
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) acc[br][g][cc] = 0.0f;
+      for (int t = 0; t < EPL; ++t) acc[br][g][t] = 0.0f;
     }
   for (int j0 = c0 + wave * kSub; j0 < c1; j0 += kDecWaves * kSub) {
+    // scores: kSub/4 iterations of 4 keys, loads kBatch iterations ahead
+#pragma unroll
+    for (int i0 = 0; i0 < kSub / 4; i0 += kBatch) {
+      float kv[kBatch][EPL];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int j = min(j0 + (i0 + u) * 4 + grp, c1 - 1);  // past the chunk: masked below
+        load_seg<EPL, BF16>(p.kc, (kvb + j) * D + seg * EPL, kv[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int jl = (i0 + u) * 4 + grp;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float sg = 0.0f;
+          const float* qg = &qsh[g][seg * EPL];
+#pragma unroll
+          for (int t = 0; t < EPL; ++t) sg = fmaf(qg[t], kv[u][t], sg);
+          sg = row16_sum(sg);
+          if (seg == 0) sbuf[wave][g][jl] = sg;
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    // online softmax, lane = key of the step
     const int j = j0 + lane;
     const bool valid = j < c1;
     const bool inwin = valid && j >= lo;
-    float s[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) s[g] = 0.0f;
-    if (valid) {
-      const long long kr = (kvb + j) * D;
-      for (int e = 0; e < D; e += 8) {
-        float kv[8];
-        if (BF16) {
-          const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.kc) + kr + e);
-          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            kv[2 * t] = __uint_as_float(w[t] << 16);
-            kv[2 * t + 1] = __uint_as_float(w[t] & 0xffff0000u);
-          }
-        } else {
-          const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(p.kc) + kr + e);
-          const float4 bq = *reinterpret_cast<const float4*>(static_cast<const float*>(p.kc) + kr + e + 4);
-          kv[0] = a.x; kv[1] = a.y; kv[2] = a.z; kv[3] = a.w;
-          kv[4] = bq.x; kv[5] = bq.y; kv[6] = bq.z; kv[7] = bq.w;
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int t = 0; t < 8; ++t) s[g] = fmaf(qs[g][e + t], kv[t], s[g]);
-      }
-    }
-    // per head: new maxima, probabilities of this step, rescale
-#pragma unroll
-    for (int br = 0; br < 2; ++br) {
-      if (br == 0 ? !do_loc : !do_glb) continue;
+    for (int br = 0; br < NB; ++br) {
+      if (!act[br]) continue;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const bool in = br == 0 ? inwin : valid;
-        const float x = in ? s[g] * p.scale_log2 : kNeg;
+        const bool in = loc ? inwin : valid;
+        const float x = in ? sbuf[wave][g][lane] * p.scale_log2 : kNeg;
         const float mn = fmaxf(m[br][g], wmax(x));
         const float alpha = exp2f(m[br][g] - mn);
         const float pr = in ? exp2f(x - mn) : 0.0f;
         l[br][g] = l[br][g] * alpha + wsum(pr);
         m[br][g] = mn;
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) acc[br][g][cc] *= alpha;
+        for (int t = 0; t < EPL; ++t) acc[br][g][t] *= alpha;
         pw[wave][br][g][lane] = pr;
       }
     }
     __builtin_amdgcn_wave_barrier();
-    // values: lane owns d columns lane + 64 cc
+    // values: same 4-keys-per-instruction assignment
     const int cnt = min(kSub, c1 - j0);
-    for (int jj = 0; jj < cnt; ++jj) {
-      const long long vr = (kvb + j0 + jj) * D;
-      float vv[NC];
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) vv[cc] = ld_io<BF16>(p.vc, vr + lane + 64 * cc);
+    for (int i0 = 0; i0 < kSub / 4; i0 += kBatch) {
+      if (i0 * 4 >= cnt) break;  // uniform
+      float vv[kBatch][EPL];
 #pragma unroll
-      for (int br = 0; br < 2; ++br) {
-        if (br == 0 ? !do_loc : !do_glb) continue;
+      for (int u = 0; u < kBatch; ++u) {
+        const int jj = min((i0 + u) * 4 + grp, cnt - 1);
+        load_seg<EPL, BF16>(p.vc, (kvb + j0 + jj) * D + seg * EPL, vv[u]);
+      }
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float pr = pw[wave][br][g][jj];
+      for (int u = 0; u < kBatch; ++u) {
+        const int jl = (i0 + u) * 4 + grp;
+        const bool live = jl < cnt;
 #pragma unroll
-          for (int cc = 0; cc < NC; ++cc) acc[br][g][cc] = fmaf(pr, vv[cc], acc[br][g][cc]);
+        for (int br = 0; br < NB; ++br) {
+          if (!act[br]) continue;
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float pr = live ? pw[wave][br][g][jl] : 0.0f;
+#pragma unroll
+            for (int t = 0; t < EPL; ++t) acc[br][g][t] = fmaf(pr, vv[u][t], acc[br][g][t]);
+          }
         }
       }
     }
     __builtin_amdgcn_wave_barrier();
   }
-  // merge the four waves' states, then write this chunk's partial
+  // add the four rows' partial sums (same elements, different keys), then
+  // merge the four waves' states and write this chunk's partial
 #pragma unroll
-  for (int br = 0; br < 2; ++br)
+  for (int br = 0; br < NB; ++br)
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) red[wave][br][g][lane + 64 * cc] = acc[br][g][cc];
+      for (int t = 0; t < EPL; ++t) {
+        float x = acc[br][g][t];
+        x += __shfl_xor(x, 16, 64);
+        x += __shfl_xor(x, 32, 64);
+        if (grp == 0) red[wave][br][g][seg * EPL + t] = x;
+      }
       if (lane == 0) {
         red[wave][br][g][D] = m[br][g];
         red[wave][br][g][D + 1] = l[br][g];
       }
     }
   __syncthreads();
-  for (int e = tid; e < 2 * G * D; e += kDecWaves * 64) {
+  for (int e = tid; e < NB * G * D; e += kDecWaves * 64) {
     const int br = e / (G * D), g = (e / D) % G, dd = e % D;
+    if (!act[br]) continue;
     float mx = kNeg;
     for (int w = 0; w < kDecWaves; ++w) mx = fmaxf(mx, red[w][br][g][D]);
     float a = 0.0f, ls = 0.0f;
@@ -204,7 +308,9 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_partial_kernel(DecParam
       a = fmaf(f, red[w][br][g][dd], a);
       ls = fmaf(f, red[w][br][g][D + 1], ls);
     }
-    float* out = p.part + ((((long long)b * p.Hq + hk * G + g) * p.nchunk + c) * 2 + br) * (D + 2);
+    const int slot = loc ? 0 : 1;  // partial slot: 0 local, 1 global
+    float* out =
+        p.part + ((((long long)b * p.Hq + hk * G + g) * p.nchunk + c) * 2 + slot) * (D + 2);
     out[dd] = a;
     if (dd == 0) {
       out[D] = mx;
@@ -222,14 +328,16 @@ struct RedParams {
   int B, Hq, cap, W, nchunk;
 };
 
-// One wave per (b, query head): merge the chunk partials of each branch in
-// chunk order (deterministic) and combine.
+// One workgroup per (b, query head): the four waves take every fourth chunk
+// of a branch (lanes over d) and merge their sums through LDS in wave order
+// (deterministic), then combine the branches.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(RedParams p) {
   constexpr int NC = D / 64;
-  const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (w >= (long long)p.B * p.Hq) return;
+  __shared__ float wpart[4][D + 1];
+  __shared__ float wmx[4];
+  const long long w = blockIdx.x;  // b * Hq + h
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int b = (int)(w / p.Hq);
   const int i = clamp_len(p.lens[b], p.cap) - 1;
   const int lo = max(0, i - p.W + 1);
@@ -238,26 +346,44 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(RedParams p) {
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc) out[cc] = 0.0f;
   for (int br = 0; br < 2; ++br) {
-    if (br == 1 && !sel) break;
+    if (br == 1 && !sel) break;  // uniform
     const int cfirst = br == 0 ? lo / kChunk : 0;
     const int clast = i / kChunk;
+    // this wave's max over its chunks, then the workgroup's
+    // lanes over chunks for the maxima
     float mx = kNeg;
-    for (int c = cfirst; c <= clast; ++c)
+    for (int c = cfirst + threadIdx.x; c <= clast; c += 256)
       mx = fmaxf(mx, p.part[((w * p.nchunk + c) * 2 + br) * (D + 2) + D]);
+    mx = wmax(mx);
+    if (lane == 0) wmx[wave] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(wmx[0], wmx[1]), fmaxf(wmx[2], wmx[3]));
     float a[NC], ls = 0.0f;
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) a[cc] = 0.0f;
-    for (int c = cfirst; c <= clast; ++c) {
+#pragma unroll 8
+    for (int c = cfirst + wave; c <= clast; c += 4) {
       const float* pt = p.part + ((w * p.nchunk + c) * 2 + br) * (D + 2);
       const float f = exp2f(pt[D] - mx);
       ls = fmaf(f, pt[D + 1], ls);
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) a[cc] = fmaf(f, pt[lane + 64 * cc], a[cc]);
     }
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) wpart[wave][lane + 64 * cc] = a[cc];
+    if (lane == 0) wpart[wave][D] = ls;
+    __syncthreads();
+    const float tot = wpart[0][D] + wpart[1][D] + wpart[2][D] + wpart[3][D];
     const float wgt = br == 0 ? 1.0f : 1.0f / (1.0f + expf(-p.gate[b]));
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) out[cc] = fmaf(wgt, a[cc] / ls, out[cc]);
+    for (int cc = 0; cc < NC; ++cc) {
+      const int dd = lane + 64 * cc;
+      const float sum = wpart[0][dd] + wpart[1][dd] + wpart[2][dd] + wpart[3][dd];
+      out[cc] = fmaf(wgt, sum / tot, out[cc]);
+    }
+    __syncthreads();
   }
+  if (wave != 0) return;
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc) {
     const long long e = w * D + lane + 64 * cc;
@@ -335,9 +461,8 @@ hipError_t decode_t(const DecodeDims& d, const DecodeArgs& a, hipStream_t s) {
   p.W = d.window;
   p.nchunk = (d.cap + kChunk - 1) / kChunk;
   p.scale_log2 = d.scale * kLog2e;
-  hipLaunchKernelGGL((decode_partial_kernel<D, G, BF16>),
-                     dim3((unsigned)((long long)d.B * d.Hkv * p.nchunk)), dim3(kDecWaves * 64), 0,
-                     s, p);
+  const dim3 grid((unsigned)(2LL * d.B * d.Hkv * p.nchunk));
+  hipLaunchKernelGGL((decode_partial_kernel<D, G, BF16>), grid, dim3(kDecWaves * 64), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   RedParams r;
@@ -351,8 +476,8 @@ hipError_t decode_t(const DecodeDims& d, const DecodeArgs& a, hipStream_t s) {
   r.cap = d.cap;
   r.W = d.window;
   r.nchunk = p.nchunk;
-  hipLaunchKernelGGL((decode_reduce_kernel<D, BF16>),
-                     dim3((unsigned)(((long long)d.B * d.Hq + 3) / 4)), dim3(256), 0, s, r);
+  hipLaunchKernelGGL((decode_reduce_kernel<D, BF16>), dim3((unsigned)((long long)d.B * d.Hq)),
+                     dim3(256), 0, s, r);
   return hipGetLastError();
 }
 
