@@ -414,6 +414,97 @@ def decode_bench(args, torch, T) -> int:
     return 0
 
 
+def varlen_bench(args, torch, T) -> int:
+    """One step = logo_forward_varlen over the packed varlen64k batch."""
+    from workloads import VARLEN_WORKLOADS, make_varlen_inputs
+    cfg = VARLEN_WORKLOADS["varlen64k"]
+    lens, Hq, Hkv, d, W, rho = (cfg[x] for x in ("lens", "Hq", "Hkv", "d", "window", "rho"))
+    inp = make_varlen_inputs(lens, Hq, Hkv, d, cfg["dtype"], seed=args.seed)
+    dev = torch.device("cuda:0")
+
+    def cv(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)[None]
+    q, k, v = cv(inp["bits"]["q"]), cv(inp["bits"]["k"]), cv(inp["bits"]["v"])
+    Tn = int(inp["cu"][-1])
+    p = T.make_problem(1, Hq, Hkv, Tn, d, W, rho)
+    K = T.logo_varlen_selected_count(rho, inp["cu"])
+    cu = torch.from_numpy(inp["cu"]).to(dev)
+    gate = torch.from_numpy(inp["gate"]).to(dev)
+    o = torch.empty((1, Hq, Tn, d), dtype=torch.bfloat16, device=dev)
+    mask = torch.empty(Tn, dtype=torch.uint8, device=dev)
+    idx = torch.empty(K, dtype=torch.int32, device=dev)
+    rank = torch.empty(Tn, dtype=torch.int32, device=dev)
+    ws = torch.empty(T.logo_varlen_workspace_size(p, len(lens), K), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        T.logo_forward_varlen(p, cu, K, q, k, v, gate, o, mask, idx, rank, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    T.logo_profile_begin()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    stage_ms, stage_n = T.logo_profile_end()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    per_step = per_step_timing(torch, step, stream, args.steps)
+    # effective FLOPs: 4 d per (query, key) pair of each example's band and
+    # of its selected rows' prefixes (positions relative to the example)
+    sel = idx.cpu().numpy().astype(np.int64)
+    cu_h = inp["cu"].astype(np.int64)
+    ex = np.searchsorted(cu_h, sel, side="right") - 1
+    glob_pairs = float((sel - cu_h[ex] + 1).sum())
+    band_pairs = float(sum(np.minimum(W, np.arange(n, dtype=np.float64) + 1).sum() for n in lens))
+    F_loc, F_glb = 4.0 * d * Hq * band_pairs, 4.0 * d * Hq * glob_pairs
+    tflops = (F_loc + F_glb) / (ms_per_step * 1e-3) / 1e12
+    avg = {s: (stage_ms[j] / stage_n[j] if stage_n[j] else None) for j, s in enumerate(T.STAGES)}
+    dom, dF = ("global", F_glb) if F_glb >= F_loc else ("local", F_loc)
+    achieved = dF / (avg[dom] * 1e-3) / 1e12 if avg[dom] else None
+    result = {
+        "metric": "effective attn TFLOP/s + ms/layer fwd over a packed batch of 65536 tokens "
+                  "(9 examples, 32K down to 256), rho=0.2; % of bf16 MFMA peak",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "varlen64k", "lens": lens, "Hq": Hq, "Hkv": Hkv, "d": d,
+                   "window": W, "rho": rho, "k_sel": K, "seed": args.seed, "mode": "varlen",
+                   "parallelism": "none (1 GPU)"},
+        "pct_of_bf16_peak": round(100.0 * tflops / BF16_PEAK_TFLOPS, 2),
+        "effective_flops": F_loc + F_glb,
+        "stage_ms_avg": {s: round(x, 4) for s, x in avg.items() if x is not None},
+        "per_step_ms": per_step,
+        "roofline": {
+            "kernel": f"attn_bf16_kernel ({dom} branch, packed examples)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2) if achieved else None,
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / BF16_PEAK_TFLOPS, 4) if achieved else None,
+            "traffic": None,
+            "algorithmic_flops_per_launch": dF,
+            "avg_launch_ms": round(avg[dom], 4) if avg[dom] else None,
+        },
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -424,12 +515,13 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--mode", choices=("forward", "train", "routed", "decode"),
+    ap.add_argument("--mode", choices=("forward", "train", "routed", "decode", "varlen"),
                     default="forward",
                     help="forward: one logo_forward per step (the headline); train: one "
                          "logo_forward_train + logo_backward per step; routed: one "
                          "logo_forward_routed per step (gate computed from the local branch); "
-                         "decode: one logo_decode_step of the 128K decode workload per step")
+                         "decode: one logo_decode_step of the 128K decode workload per step; "
+                         "varlen: one logo_forward_varlen over a packed 64K-token batch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (read N, write N "
                          "bytes) so HBM counters can be scaled to bytes")
@@ -459,6 +551,8 @@ def main() -> int:
 
     if args.mode == "decode":
         return decode_bench(args, torch, T)
+    if args.mode == "varlen":
+        return varlen_bench(args, torch, T)
     w = get_workload(args.workload)
     if args.rho is not None:
         w = w.with_(rho=args.rho)

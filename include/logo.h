@@ -288,6 +288,41 @@ logo_status logo_decode_step(const logo_decode_problem* p, const void* q,
                              void* o, uint8_t* selected, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* ---- packed variable-length batches --------------------------------------
+ *
+ * Several examples packed into one token stream ("Local-global attention",
+ * implementation-sketch notes: packing needs per-example boundaries so no
+ * token attends across them). The problem has B = 1 and n = T, the total
+ * number of tokens; cu_seqlens [E+1] (ascending, cu[0] = 0, cu[E] = T)
+ * splits the stream into examples. Every example is its own sequence: the
+ * local window and the global prefix stop at its first token, and its
+ * budget is k_e = ceil(rho * n_e) of its own gate logits (ties to the lower
+ * position). q, o [1][Hq][T][d] and k, v [1][Hkv][T][d] with the problem's
+ * strides (a token-major [T][H][d] layout is a strided view); gate, mask,
+ * rank [T]; idx [K] with K = logo_varlen_selected_count: the examples'
+ * selections concatenated, absolute token positions (ascending); rank is a
+ * token's index in idx or -1. Inconsistent cu_seqlens on the device (not
+ * what logo_varlen_selected_count was given) give undefined results but no
+ * access outside the buffers: idx writes past K are dropped. */
+
+/* K = sum over examples of ceil(rho * (cu[e+1] - cu[e])), from a host copy of
+ * cu_seqlens; -1 for a bad ratio, cu[0] != 0 or decreasing offsets. */
+int64_t logo_varlen_selected_count(double rho, const int32_t* cu_seqlens_host,
+                                   int64_t n_examples);
+
+/* Workspace of logo_forward_varlen: 16 B per example, 4 B per token and the
+ * float32 local outputs of the selected rows (Hq*K*d*4), each 256-aligned. */
+logo_status logo_varlen_workspace_size(const logo_problem* p, int64_t n_examples,
+                                       int64_t total_selected, size_t* bytes);
+
+/* The forward over a packed batch (cu_seqlens is a device pointer). */
+logo_status logo_forward_varlen(const logo_problem* p, const int32_t* cu_seqlens,
+                                int64_t n_examples, int64_t total_selected,
+                                const void* q, const void* k, const void* v,
+                                const float* gate, void* o, uint8_t* mask,
+                                int32_t* idx, int32_t* rank, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* logo_status_string(logo_status s);
 

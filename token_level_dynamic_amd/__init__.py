@@ -34,6 +34,9 @@ from ._lib import (  # noqa: F401
     logo_select_queries,
     logo_select_threshold,
     logo_target_count,
+    logo_varlen_selected_count,
+    logo_varlen_workspace_size,
+    logo_forward_varlen,
     logo_workspace_size,
     make_decode_problem,
     make_problem,

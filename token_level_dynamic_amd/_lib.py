@@ -121,6 +121,11 @@ _SIGS = {
                          [ctypes.c_size_t, _P]),
     "logo_calibrate_threshold": (ctypes.c_int, [_PP, _P, _P, _P, _P]),
     "logo_select_threshold": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P]),
+    "logo_varlen_selected_count": (ctypes.c_int64, [ctypes.c_double, _P, ctypes.c_int64]),
+    "logo_varlen_workspace_size": (ctypes.c_int, [_PP, ctypes.c_int64, ctypes.c_int64,
+                                                   ctypes.POINTER(ctypes.c_size_t)]),
+    "logo_forward_varlen": (ctypes.c_int, [_PP, _P, ctypes.c_int64, ctypes.c_int64] + [_P] * 9 +
+                            [ctypes.c_size_t, _P]),
     "logo_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "logo_last_error": (ctypes.c_char_p, []),
     "logo_profile_begin": (ctypes.c_int, []),
@@ -450,6 +455,39 @@ def logo_select_threshold(p: logo_problem, gate, tau, mask, idx, count, stream=N
                                        _ptr(mask, "mask"), _ptr(idx, "idx"),
                                        _ptr(count, "count"), _stream(stream)),
            "logo_select_threshold")
+
+
+def logo_varlen_selected_count(rho: float, cu_seqlens) -> int:
+    """K = sum of ceil(rho * n_e) over the examples of host offsets cu_seqlens."""
+    import numpy as np
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    return int(lib().logo_varlen_selected_count(float(rho), cu.ctypes.data, cu.size - 1))
+
+
+def logo_varlen_workspace_size(p: logo_problem, n_examples: int, total_selected: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().logo_varlen_workspace_size(ctypes.byref(p), int(n_examples), int(total_selected),
+                                            ctypes.byref(out)), "logo_varlen_workspace_size")
+    return int(out.value)
+
+
+def logo_forward_varlen(p: logo_problem, cu_seqlens, total_selected: int, q, k, v, gate, o, mask,
+                        idx, rank, workspace, stream=None) -> None:
+    """Forward over a packed batch (B = 1, n = total tokens); cu_seqlens is a
+    device int32 tensor of E+1 offsets (see include/logo.h)."""
+    E = cu_seqlens.numel() - 1
+    _expect(cu_seqlens, "cu_seqlens", torch.int32, E + 1)
+    qp, kp, vp = _qkv(p, q, k, v)
+    _expect(gate, "gate", torch.float32, p.n)
+    op = _io(p, o, "o", p.Hq)
+    _expect(mask, "mask", torch.uint8, p.n)
+    _expect(idx, "idx", torch.int32, total_selected)
+    _expect(rank, "rank", torch.int32, p.n)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().logo_forward_varlen(
+        ctypes.byref(p), _ptr(cu_seqlens, "cu_seqlens"), E, int(total_selected), qp, kp, vp,
+        _ptr(gate, "gate"), op, _ptr(mask, "mask"), _ptr(idx, "idx"), _ptr(rank, "rank"),
+        _ptr(workspace, "workspace"), ws_bytes, _stream(stream)), "logo_forward_varlen")
 
 
 def logo_profile_begin() -> None:

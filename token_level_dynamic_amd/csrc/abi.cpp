@@ -685,6 +685,113 @@ logo_status logo_select_threshold(const logo_problem* p, const float* gate, cons
   return LOGO_OK;
 }
 
+// Packed examples: the per-example table, per-token example starts and the
+// float32 local outputs of the selected rows.
+struct VarlenWs {
+  size_t seg, seg_start, scratch, total;
+};
+VarlenWs varlen_ws(const logo::Dims& d, int64_t E, int64_t K) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  VarlenWs w;
+  w.seg = 0;
+  w.seg_start = up((size_t)E * 16);
+  w.scratch = w.seg_start + up((size_t)d.n * 4);
+  w.total = w.scratch + up((size_t)d.Hq * (size_t)K * d.d * sizeof(float));
+  return w;
+}
+
+logo_status check_varlen(const logo_problem* p, int64_t E, int64_t K, logo::Dims* d) {
+  LOGO_TRY(check_problem(p, d));
+  if (p->B != 1)
+    return fail(LOGO_ERR_INVALID_ARG, "packed batches are one token stream: B must be 1");
+  if (E < 1 || E > (int64_t(1) << 30))
+    return fail(LOGO_ERR_INVALID_ARG, "n_examples must be >= 1");
+  if (K < 0 || K > p->n)
+    return fail(LOGO_ERR_INVALID_ARG, "total_selected must be in [0, n]");
+  d->k = (int)K;
+  return LOGO_OK;
+}
+
+int64_t logo_varlen_selected_count(double rho, const int32_t* cu, int64_t E) {
+  if (std::isnan(rho) || rho < 0.0 || rho > 1.0 || !cu || E < 1) return -1;
+  if (cu[0] != 0) return -1;
+  int64_t K = 0;
+  for (int64_t e = 0; e < E; ++e) {
+    if (cu[e + 1] < cu[e]) return -1;
+    K += target_count(rho, (int64_t)cu[e + 1] - cu[e]);
+  }
+  return K;
+}
+
+logo_status logo_varlen_workspace_size(const logo_problem* p, int64_t n_examples,
+                                       int64_t total_selected, size_t* bytes) {
+  logo::Dims d;
+  LOGO_TRY(check_varlen(p, n_examples, total_selected, &d));
+  if (!bytes) return fail(LOGO_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = d.n == 0 ? 0 : varlen_ws(d, n_examples, total_selected).total;
+  return LOGO_OK;
+}
+
+logo_status logo_forward_varlen(const logo_problem* p, const int32_t* cu_seqlens,
+                                int64_t n_examples, int64_t total_selected, const void* q,
+                                const void* k, const void* v, const float* gate, void* o,
+                                uint8_t* mask, int32_t* idx, int32_t* rank, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  logo::Dims d;
+  LOGO_TRY(check_varlen(p, n_examples, total_selected, &d));
+  if (d.n == 0) return LOGO_OK;
+  LOGO_TRY(need_ptr(cu_seqlens, "cu_seqlens"));
+  LOGO_TRY(need_ptr(q, "q"));
+  LOGO_TRY(need_ptr(k, "k"));
+  LOGO_TRY(need_ptr(v, "v"));
+  LOGO_TRY(need_ptr(gate, "gate"));
+  LOGO_TRY(need_ptr(o, "o"));
+  LOGO_TRY(need_ptr(mask, "mask"));
+  LOGO_TRY(need_ptr(rank, "rank"));
+  if (d.k > 0) LOGO_TRY(need_ptr(idx, "idx"));
+  const VarlenWs ws = varlen_ws(d, n_examples, total_selected);
+  if (!workspace || workspace_bytes < ws.total)
+    return fail(LOGO_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(LOGO_ERR_INVALID_ARG, "workspace misaligned");
+  char* w = static_cast<char*>(workspace);
+  int4* seg = reinterpret_cast<int4*>(w + ws.seg);
+  int32_t* seg_start = reinterpret_cast<int32_t*>(w + ws.seg_start);
+  float* scratch = reinterpret_cast<float*>(w + ws.scratch);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  {
+    StageTimer tm(0, s);
+    e = logo::launch_varlen_prep(cu_seqlens, (int)n_examples, d.n, p->rho, seg, seg_start, s);
+    if (e == hipSuccess)
+      e = logo::launch_select_segments((int)n_examples, seg, gate, mask, d.k > 0 ? idx : nullptr,
+                                       rank, d.k, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  logo::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.idx = idx;
+  a.rank = rank;
+  a.gate = gate;
+  a.out_f32 = scratch;
+  a.scratch = scratch;
+  a.out_io = o;
+  a.seg_start = seg_start;
+  {
+    StageTimer tm(1, s);
+    e = run_attn(d, logo::Epi::LocalFused, a, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "local attention launch");
+  if (d.k > 0) {
+    StageTimer tm(2, s);
+    e = run_attn(d, logo::Epi::GlobalFused, a, s);
+    if (e != hipSuccess) return hip_fail(e, "global attention launch");
+  }
+  return LOGO_OK;
+}
+
 logo_status logo_profile_begin(void) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
   g_prof.on = true;

@@ -94,6 +94,7 @@ struct Params {
   float* og_out;        // optional f32 o_global rows (fused global)
   const float* router_w;  // routed local: [Hq][D]
   float* router_part;     // routed local: [B][Hq][n]
+  const int32_t* seg_start;  // packed examples: [n] first token of the example, or NULL
 };
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
@@ -167,7 +168,8 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   const int h = hk * G + (wave_on ? u : u_last) % G;
 
   auto row_pos = [&] __device__ (int r) __attribute__((always_inline)) {
-    return GLOBAL ? p.idx[(size_t)b * p.ksel + r] : r;
+    // positions read from idx are clamped into the sequence (defensive)
+    return GLOBAL ? min(max(p.idx[(size_t)b * p.ksel + r], 0), p.n - 1) : r;
   };
   // Row of this lane and the wave's / workgroup's key range.
   const int r_lane = pb * kRows + col;
@@ -175,11 +177,19 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   const int pos = r_lane < R ? row_pos(r_lane) : -1;
   const int wpos_lo = row_pos(pb * kRows);                 // rows ascend
   const int wpos_hi = row_pos(min(pb * kRows + kRows, R) - 1);
-  const int wkey_lo = GLOBAL ? 0 : max(0, wpos_lo - p.W + 1);
+  // Packed examples: keys before a row's example start are not read; the
+  // starts do not decrease along the rows.
+  auto seg0 = [&] __device__ (int pos_) __attribute__((always_inline)) {
+    return p.seg_start ? p.seg_start[pos_] : 0;
+  };
+  const int ss = pos >= 0 ? seg0(pos) : 0;
+  const int wss_lo = seg0(wpos_lo), wss_hi = seg0(wpos_hi);
+  const int wkey_lo = GLOBAL ? wss_lo : max(wss_lo, wpos_lo - p.W + 1);
   const int wkey_hi = wpos_hi;
   const int gpos_lo = row_pos((u_first / G) * kRows);
   const int gpos_hi = row_pos(min((u_last / G) * kRows + kRows, R) - 1);
-  const int t_lo = (GLOBAL ? 0 : max(0, gpos_lo - p.W + 1)) / kKeys;
+  const int gss_lo = seg0(gpos_lo);
+  const int t_lo = (GLOBAL ? gss_lo : max(gss_lo, gpos_lo - p.W + 1)) / kKeys;
   const int t_hi = gpos_hi / kKeys;
 
   // This (b, kv head)'s K and V, read through bounds-checked buffer loads:
@@ -257,6 +267,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   };
   auto is_full = [&] __device__ (int t) __attribute__((always_inline)) {
     const int key0 = t * kKeys;
+    if (key0 < wss_hi) return false;  // some row's example starts inside or after the tile
     if (GLOBAL) return key0 + kKeys - 1 <= wpos_lo;
     return key0 >= wpos_hi - p.W + 1 && key0 + kKeys - 1 <= wpos_lo;
   };
@@ -306,7 +317,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int key = key0 + (e >> 2) * 8 + half * 4 + (e & 3);
-      bool ok = key <= pos;
+      bool ok = key <= pos && key >= ss;
       if (!GLOBAL) ok = ok && key >= pos - p.W + 1;
       s[e] = ok ? s[e] : -INFINITY;
     }
@@ -431,7 +442,10 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   // EPI: 0 LocalAll, 1 LocalFused, 2 GlobalAll, 3 GlobalFused, 4 LocalRouted,
   // 5 GlobalRouted
   int rk = -1;
-  if (EPI == 1) rk = p.rank[(size_t)b * p.n + pos];
+  if (EPI == 1) {
+    rk = p.rank[(size_t)b * p.n + pos];
+    if (rk >= p.ksel) rk = -1;  // defensive: never address past the scratch rows
+  }
   float sig = 0.0f;
   if (EPI == 3 || EPI == 5) sig = 1.0f / (1.0f + expf(-p.gate[(size_t)b * p.n + pos]));
   // routed local: this lane's half of <router_w[h], o_local row>
@@ -549,6 +563,7 @@ hipError_t launch_attn_bf16(const Dims& d, Epi epi, const AttnArgs& a, hipStream
   prm.og_out = a.og_out;
   prm.router_w = a.router_w;
   prm.router_part = a.router_part;
+  prm.seg_start = a.seg_start;
   if (d.d == 64) return dispatch_epi<64>(epi, prm, s);
   if (d.d == 128) return dispatch_epi<128>(epi, prm, s);
   return hipErrorInvalidValue;

@@ -40,6 +40,7 @@ struct Params {
   float* og_out;        // optional f32 o_global rows (fused global)
   const float* router_w;  // routed local: [Hq][D]
   float* router_part;     // routed local: [B][Hq][n]
+  const int32_t* seg_start;  // packed examples: [n] first token of the example, or NULL
 };
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -67,8 +68,9 @@ __global__ __launch_bounds__(kWaves * 64) void attn_f32_kernel(Params p) {
   const int b = bh / p.Hq;
   const int h = bh % p.Hq;
   const int hk = h / (p.Hq / p.Hkv);
-  const int pos = GLOBAL ? p.idx[(size_t)b * p.ksel + r] : r;
-  const int lo = GLOBAL ? 0 : max(0, pos - p.W + 1);
+  const int pos = GLOBAL ? min(max(p.idx[(size_t)b * p.ksel + r], 0), p.n - 1) : r;
+  const int ss = p.seg_start ? p.seg_start[pos] : 0;  // packed examples: example start
+  const int lo = GLOBAL ? ss : max(ss, pos - p.W + 1);
   const int hi = pos;
 
   const float* qrow = p.q + b * p.vq.sb + h * p.vq.sh + (long long)pos * p.vq.st;
@@ -127,7 +129,10 @@ __global__ __launch_bounds__(kWaves * 64) void attn_f32_kernel(Params p) {
   if (EPI == 3 || EPI == 5) sig = 1.0f / (1.0f + expf(-p.gate[(size_t)b * p.n + pos]));
   float rdot = 0.0f;
   int rk = -1;
-  if (EPI == 1) rk = p.rank[(size_t)b * p.n + pos];
+  if (EPI == 1) {
+    rk = p.rank[(size_t)b * p.n + pos];
+    if (rk >= p.ksel) rk = -1;  // defensive: never address past the scratch rows
+  }
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int e = lane + 64 * c;
@@ -211,6 +216,7 @@ hipError_t launch_attn_f32(const Dims& d, Epi epi, const AttnArgs& a, hipStream_
   prm.og_out = a.og_out;
   prm.router_w = a.router_w;
   prm.router_part = a.router_part;
+  prm.seg_start = a.seg_start;
   if (d.d == 64) return dispatch_epi<64>(epi, prm, s);
   if (d.d == 128) return dispatch_epi<128>(epi, prm, s);
   return hipErrorInvalidValue;

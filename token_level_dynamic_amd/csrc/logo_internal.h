@@ -50,6 +50,8 @@ struct AttnArgs {
   float* og_out;         // optional, fused global: o_global [B][Hq][k][d] f32
   const float* router_w; // routed local: [Hq][d] f32
   float* router_part;    // routed local: [B][Hq][n] f32
+  const int32_t* seg_start;  // packed examples: first token of each token's
+                             // example (keys before it are masked); or NULL
 };
 
 // Everything the backward kernels read and write. q, k, v, o and dout are
@@ -96,6 +98,14 @@ hipError_t launch_bwd_dq_f32(const Dims& d, bool global, const BwdArgs& a, hipSt
 
 hipError_t launch_select(const Dims& d, const float* gate, uint8_t* mask,
                          int32_t* idx, int32_t* rank, hipStream_t s);
+
+// Packed examples: select per example (see select.hip) and build the
+// per-example table and per-token example starts from cu_seqlens.
+hipError_t launch_select_segments(int n_segments, const int4* seg, const float* gate,
+                                  uint8_t* mask, int32_t* idx, int32_t* rank, int idx_cap,
+                                  hipStream_t s);
+hipError_t launch_varlen_prep(const int32_t* cu, int E, int T, double rho, int4* seg,
+                              int32_t* seg_start, hipStream_t s);
 
 hipError_t launch_attn_bf16(const Dims& d, Epi epi, const AttnArgs& a,
                             hipStream_t s);

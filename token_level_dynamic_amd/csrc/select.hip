@@ -65,19 +65,43 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* w
   return r;
 }
 
+// One workgroup per sequence. Batched rows (SEG == false): row b holds
+// gate[b*n .. b*n + n), writes idx[b*k ..] with positions within the row and
+// rank = index in the row's list. Packed examples (SEG == true): example e
+// is seg[e] = {start, length, k_e, offset}; positions written to idx (at
+// idx[offset ..]) are absolute token positions and rank is the index in the
+// concatenated list; writes past `idx_cap` are dropped.
+template <bool SEG>
 __global__ __launch_bounds__(kThreads) void select_kernel(
-    const float* __restrict__ gate, int n, int k, uint8_t* __restrict__ mask,
-    int32_t* __restrict__ idx, int32_t* __restrict__ rank) {
+    const float* __restrict__ gate, int n_rows, int k_rows, uint8_t* __restrict__ mask,
+    int32_t* __restrict__ idx, int32_t* __restrict__ rank, const int4* __restrict__ seg,
+    int idx_cap) {
   __shared__ uint32_t hist[4096];
   __shared__ uint32_t scan_ws[kWaves + 1];
   __shared__ uint32_t s_digit, s_before;
 
   const int b = blockIdx.x;
   const int t = threadIdx.x;
-  const float* g = gate + (size_t)b * n;
-  uint8_t* mrow = mask + (size_t)b * n;
-  int32_t* rrow = rank + (size_t)b * n;
-  int32_t* irow = idx ? idx + (size_t)b * k : nullptr;
+  int start, n, k, koff;
+  if (SEG) {
+    const int4 sg = seg[b];
+    start = sg.x;
+    n = sg.y;
+    k = sg.z;
+    koff = sg.w;
+  } else {
+    start = b * n_rows;
+    n = n_rows;
+    k = k_rows;
+    koff = b * k_rows;
+  }
+  const int pos_add = SEG ? start : 0;    // idx values: absolute or within the row
+  const int rank_add = SEG ? koff : 0;    // rank values: into the concatenation or the row
+  const float* g = gate + (size_t)start;
+  uint8_t* mrow = mask + (size_t)start;
+  int32_t* rrow = rank + (size_t)start;
+  int32_t* irow = idx ? idx + (size_t)koff : nullptr;
+  const int icap = SEG ? idx_cap - koff : k;  // entries of irow that may be written
 
   uint32_t T;        // threshold image
   uint32_t need;     // ties at T to take
@@ -125,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
 
   // Compaction in position order.
   uint32_t carry_gt = 0, carry_tie = 0;
-  const bool vec = (n % 4) == 0;
+  const bool vec = (n % 4) == 0 && (start % 4) == 0;
 #pragma unroll 1
   for (int base = 0; base < n; base += kChunk) {
     const int p0 = base + t * kItems;
@@ -162,8 +186,8 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       const bool sel = gt || (tie && tie_before < need);
       const uint32_t r = gt_before + (tie_before < need ? tie_before : need);
       mv[j] = sel ? 1 : 0;
-      rv[j] = sel ? (int32_t)r : -1;
-      if (sel && p0 + j < n) irow[r] = p0 + j;
+      rv[j] = sel ? (int32_t)r + rank_add : -1;
+      if (sel && p0 + j < n && (int)r < icap) irow[r] = p0 + j + pos_add;
       gt_before += gt ? 1u : 0u;
       tie_before += tie ? 1u : 0u;
     }
@@ -194,8 +218,62 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
 hipError_t launch_select(const Dims& d, const float* gate, uint8_t* mask,
                          int32_t* idx, int32_t* rank, hipStream_t s) {
   if (d.B == 0 || d.n == 0) return hipSuccess;
-  hipLaunchKernelGGL(select_kernel, dim3(d.B), dim3(kThreads), 0, s, gate, d.n,
-                     d.k, mask, idx, rank);
+  hipLaunchKernelGGL(select_kernel<false>, dim3(d.B), dim3(kThreads), 0, s, gate, d.n, d.k, mask,
+                     idx, rank, nullptr, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_segments(int n_segments, const int4* seg, const float* gate,
+                                  uint8_t* mask, int32_t* idx, int32_t* rank, int idx_cap,
+                                  hipStream_t s) {
+  if (n_segments == 0) return hipSuccess;
+  hipLaunchKernelGGL(select_kernel<true>, dim3(n_segments), dim3(kThreads), 0, s, gate, 0, 0,
+                     mask, idx, rank, seg, idx_cap);
+  return hipGetLastError();
+}
+
+namespace {
+
+// Per-example table {start, length, k_e = ceil(rho * length), offset of the
+// example's selection} from cu_seqlens, and every token's example start.
+// One workgroup scans the examples in order (offsets need a prefix sum);
+// tokens are filled by every thread.
+// Offsets are clamped into [0, T] (each at or after the previous one), so
+// inconsistent offsets cannot address outside the token arrays.
+__global__ __launch_bounds__(kThreads) void varlen_prep_kernel(const int32_t* __restrict__ cu,
+                                                               int E, int T, double rho,
+                                                               int4* __restrict__ seg,
+                                                               int32_t* __restrict__ seg_start) {
+  __shared__ uint32_t scan_ws[kWaves + 1];
+  const int t = threadIdx.x;
+  uint32_t carry = 0;
+  for (int base = 0; base < E; base += kThreads) {
+    const int e = base + t;
+    int a = 0, len = 0, k = 0;
+    if (e < E) {
+      a = min(max(cu[e], 0), T);
+      len = min(max(cu[e + 1], a), T) - a;
+      const double kk = ceil(rho * (double)len);
+      k = (int)min(max(kk, 0.0), (double)len);
+    }
+    uint32_t tot;
+    const uint32_t before = block_exclusive_scan((uint32_t)k, scan_ws, &tot);
+    if (e < E) seg[e] = make_int4(a, len, k, (int)(carry + before));
+    carry += tot;
+    for (int e2 = base; e2 < min(base + kThreads, E); ++e2) {
+      const int a2 = min(max(cu[e2], 0), T), b2 = min(max(cu[e2 + 1], a2), T);
+      for (int i = a2 + t; i < b2; i += kThreads) seg_start[i] = a2;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_varlen_prep(const int32_t* cu, int E, int T, double rho, int4* seg,
+                              int32_t* seg_start, hipStream_t s) {
+  if (E == 0) return hipSuccess;
+  hipLaunchKernelGGL(varlen_prep_kernel, dim3(1), dim3(kThreads), 0, s, cu, E, T, rho, seg,
+                     seg_start);
   return hipGetLastError();
 }
 

@@ -189,6 +189,33 @@ def make_inputs(w: Workload, seed: int = 0, *, gate: Optional[np.ndarray] = None
     return inp
 
 
+# A packed batch of 65536 tokens: examples of 32K, 16K, 8K, 4K, 2K, 1K, 512,
+# 256 and 256 tokens (a length mix halving per example), otherwise the 32K GQA
+# layer's shape.
+VARLEN_WORKLOADS = {
+    "varlen64k": dict(lens=[32768, 16384, 8192, 4096, 2048, 1024, 512, 256, 256], Hq=16, Hkv=4,
+                      d=128, window=1024, rho=0.2, dtype="bf16"),
+}
+
+
+def make_varlen_inputs(lens, Hq, Hkv, d, dtype="bf16", seed=0):
+    """Seeded packed-batch inputs (stream (seed, 0x7A)): q [Hq, T, d], k, v
+    [Hkv, T, d] N(0,1), gate [T] N(0,1); cu_seqlens from the lengths."""
+    rng = np.random.default_rng([seed, 0x7A])
+    T = int(sum(lens))
+    q = rng.standard_normal((Hq, T, d), dtype=np.float32)
+    k = rng.standard_normal((Hkv, T, d), dtype=np.float32)
+    v = rng.standard_normal((Hkv, T, d), dtype=np.float32)
+    gate = rng.standard_normal(T, dtype=np.float32)
+    bits = {}
+    if dtype == "bf16":
+        for name, x in (("q", q), ("k", k), ("v", v)):
+            bits[name] = bf16_bits(x)
+        q, k, v = (bits_to_f32(bits[x]) for x in ("q", "k", "v"))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return {"q": q, "k": k, "v": v, "gate": gate, "cu": cu, "bits": bits}
+
+
 def make_dout(w: Workload, seed: int = 0):
     """Upstream gradient of the layer output for the backward: N(0,1) entries
     of shape [B, Hq, n, d] from a stream of its own (seed, 0xD0), rounded to
