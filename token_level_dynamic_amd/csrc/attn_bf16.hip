@@ -130,7 +130,12 @@ __device__ __forceinline__ void issue_tile(const uint16_t* base, int nbytes, uin
   }
 }
 
-template <int D, bool GLOBAL, int EPI>
+// SEG: packed examples (p.seg_start set): keys before a row's example start
+// are masked and tile ranges start at the example; positions read from idx
+// are clamped and ranks beyond the scratch rows ignored, so inconsistent
+// example offsets cannot address outside the buffers. Compiled separately so
+// the plain path carries none of it.
+template <int D, bool GLOBAL, int EPI, bool SEG>
 __global__ __launch_bounds__(kThreads, 2)
 __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   using SM = Smem<D>;
@@ -168,8 +173,9 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   const int h = hk * G + (wave_on ? u : u_last) % G;
 
   auto row_pos = [&] __device__ (int r) __attribute__((always_inline)) {
-    // positions read from idx are clamped into the sequence (defensive)
-    return GLOBAL ? min(max(p.idx[(size_t)b * p.ksel + r], 0), p.n - 1) : r;
+    if (!GLOBAL) return r;
+    const int ix = p.idx[(size_t)b * p.ksel + r];
+    return SEG ? min(max(ix, 0), p.n - 1) : ix;
   };
   // Row of this lane and the wave's / workgroup's key range.
   const int r_lane = pb * kRows + col;
@@ -180,7 +186,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   // Packed examples: keys before a row's example start are not read; the
   // starts do not decrease along the rows.
   auto seg0 = [&] __device__ (int pos_) __attribute__((always_inline)) {
-    return p.seg_start ? p.seg_start[pos_] : 0;
+    return SEG ? p.seg_start[pos_] : 0;
   };
   const int ss = pos >= 0 ? seg0(pos) : 0;
   const int wss_lo = seg0(wpos_lo), wss_hi = seg0(wpos_hi);
@@ -267,7 +273,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   };
   auto is_full = [&] __device__ (int t) __attribute__((always_inline)) {
     const int key0 = t * kKeys;
-    if (key0 < wss_hi) return false;  // some row's example starts inside or after the tile
+    if (SEG && key0 < wss_hi) return false;  // a row's example starts inside or after the tile
     if (GLOBAL) return key0 + kKeys - 1 <= wpos_lo;
     return key0 >= wpos_hi - p.W + 1 && key0 + kKeys - 1 <= wpos_lo;
   };
@@ -317,7 +323,8 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int key = key0 + (e >> 2) * 8 + half * 4 + (e & 3);
-      bool ok = key <= pos && key >= ss;
+      bool ok = key <= pos;
+      if (SEG) ok = ok && key >= ss;
       if (!GLOBAL) ok = ok && key >= pos - p.W + 1;
       s[e] = ok ? s[e] : -INFINITY;
     }
@@ -444,7 +451,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   int rk = -1;
   if (EPI == 1) {
     rk = p.rank[(size_t)b * p.n + pos];
-    if (rk >= p.ksel) rk = -1;  // defensive: never address past the scratch rows
+    if (SEG && rk >= p.ksel) rk = -1;  // never address past the scratch rows
   }
   float sig = 0.0f;
   if (EPI == 3 || EPI == 5) sig = 1.0f / (1.0f + expf(-p.gate[(size_t)b * p.n + pos]));
@@ -503,17 +510,22 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   }
 }
 
-template <int D, bool GLOBAL, int EPI>
+template <int D, bool GLOBAL, int EPI, bool SEG = false>
 hipError_t launch_one(const Params& prm, hipStream_t s) {
   static_assert(GLOBAL == (EPI == 2 || EPI == 3 || EPI == 5), "epilogue of the other branch");
   const int grid = prm.per_xcd * kNumXcd;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, GLOBAL, EPI>), dim3(grid), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((attn_bf16_kernel<D, GLOBAL, EPI, SEG>), dim3(grid), dim3(kThreads), 0, s,
                      prm);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t dispatch_epi(Epi epi, const Params& prm, hipStream_t s) {
+  if (prm.seg_start) {  // packed examples: the fused forward only
+    if (epi == Epi::LocalFused) return launch_one<D, false, 1, true>(prm, s);
+    if (epi == Epi::GlobalFused) return launch_one<D, true, 3, true>(prm, s);
+    return hipErrorInvalidValue;
+  }
   switch (epi) {
     case Epi::LocalAll: return launch_one<D, false, 0>(prm, s);
     case Epi::LocalFused: return launch_one<D, false, 1>(prm, s);

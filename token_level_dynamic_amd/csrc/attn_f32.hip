@@ -68,7 +68,8 @@ __global__ __launch_bounds__(kWaves * 64) void attn_f32_kernel(Params p) {
   const int b = bh / p.Hq;
   const int h = bh % p.Hq;
   const int hk = h / (p.Hq / p.Hkv);
-  const int pos = GLOBAL ? min(max(p.idx[(size_t)b * p.ksel + r], 0), p.n - 1) : r;
+  int pos = GLOBAL ? p.idx[(size_t)b * p.ksel + r] : r;
+  if (GLOBAL && p.seg_start) pos = min(max(pos, 0), p.n - 1);  // packed: defensive clamp
   const int ss = p.seg_start ? p.seg_start[pos] : 0;  // packed examples: example start
   const int lo = GLOBAL ? ss : max(ss, pos - p.W + 1);
   const int hi = pos;
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_f32_kernel(Params p) {
   int rk = -1;
   if (EPI == 1) {
     rk = p.rank[(size_t)b * p.n + pos];
-    if (rk >= p.ksel) rk = -1;  // defensive: never address past the scratch rows
+    if (rk >= p.ksel) rk = -1;  // never address past the scratch rows
   }
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
