@@ -130,6 +130,36 @@ def copy_calibration(torch) -> int:
     return 0
 
 
+def gemm_ceiling(torch) -> int:
+    """Sustained bf16 matrix-core rate of a plain library GEMM on this part,
+    on random N(0,1) operands and on zero operands. The published dense peak
+    assumes the top clock; under a full matrix-core load the clock is set by
+    power, which depends on the data, so this is the practical ceiling that
+    the attention kernels' rates can be read against."""
+    out = {}
+    for n in (8192, 16384):
+        a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+        z = torch.zeros_like(a)
+        reps = 20 if n == 8192 else 5
+        for name, (x, y) in (("random", (a, b)), ("zero", (z, z))):
+            for _ in range(3):
+                torch.matmul(x, y)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                torch.matmul(x, y)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            out[f"{n}^3 {name}"] = {"ms": round(ms, 4), "TFLOP/s": round(2 * n ** 3 / ms / 1e9, 1)}
+    print(json.dumps({"gemm_ceiling": out, "kernel": "torch.matmul bf16 (hipBLASLt)",
+                      "published_dense_peak_TFLOP/s": BF16_PEAK_TFLOPS}))
+    return 0
+
+
 def per_step_timing(torch, step, stream, steps: int) -> dict:
     """Each forward timed on its own: warm (back to back) and cold (a 1 GiB
     device write before each forward evicts L2 and the MALL), median/min/max.
@@ -399,7 +429,7 @@ def decode_bench(args, torch, T) -> int:
                          for j, s in enumerate(T.STAGES) if stage_n[j]},
         "per_step_ms": per_step,
         "roofline": {
-            "kernel": "decode_partial_kernel + decode_reduce_kernel",
+            "kernel": "decode_stream_kernel + decode_reduce_kernel",
             "bound": "hbm",
             "achieved": round(gbs, 2),
             "peak": HBM_PEAK_GBS,
@@ -522,6 +552,8 @@ def main() -> int:
                          "logo_forward_routed per step (gate computed from the local branch); "
                          "decode: one logo_decode_step of the 128K decode workload per step; "
                          "varlen: one logo_forward_varlen over a packed 64K-token batch")
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="time a plain bf16 GEMM on random and on zero operands and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (read N, write N "
                          "bytes) so HBM counters can be scaled to bytes")
@@ -539,6 +571,8 @@ def main() -> int:
 
     if args.copy_calibration:
         return copy_calibration(torch)
+    if args.gemm_ceiling:
+        return gemm_ceiling(torch)
 
     from token_level_dynamic_amd._lib import LIB_PATH
     if not os.path.exists(LIB_PATH):

@@ -86,6 +86,25 @@ def test_decode_matches_oracle(name):
     assert err <= TOL[cfg["dtype"]]
 
 
+def test_decode_many_sequences():
+    """More sequences than the streaming kernel's item table holds: the
+    chunked kernel serves the step (bf16), with the same results."""
+    cfg = dict(B=1030, Hq=2, Hkv=1, cap=300, d=64, window=40, rho=0.3, dtype="bf16")
+    r = np.random.default_rng(11)
+    lens = r.integers(1, cfg["cap"] + 1, size=cfg["B"]).astype(np.int32)
+    inp = make_decode_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["cap"], cfg["d"], "bf16",
+                             seed=5, lens=lens)
+    inp.tau = (inp.gate + np.where(r.random(cfg["B"]) < 0.3, -0.5, 0.5)).astype(np.float32)
+    say(f"[decode] many sequences B={cfg['B']}")
+    got = run_decode(cfg, inp, eta=0.0)
+    ref = DC.decode_step(inp.q, inp.k, inp.v, inp.lens, inp.gate, inp.tau, cfg["window"],
+                         cfg["rho"], 0.0)
+    assert np.array_equal(got["selected"], ref["selected"])
+    err = float(np.abs(got["o"] - ref["o"]).max())
+    say(f"  o max_abs={err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 def test_decode_is_deterministic_and_tau_accumulates():
     cfg = CASES["bf16_g2_chunks"]
     inp = make_decode_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["cap"], cfg["d"], "bf16",

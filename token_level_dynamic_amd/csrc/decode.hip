@@ -319,6 +319,415 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_partial_kernel(DecParam
   }
 }
 
+// ---- bf16 decode as a persistent stream ------------------------------------
+//
+// One workgroup per compute unit walks a balanced, contiguous range of work
+// items, an item being (b, branch, kv head, chunk of kChunk keys) with at
+// least one key to read: local items cover the chunks that overlap the
+// window, global items every chunk of a selected sequence. Items are
+// numbered sequence-major, branch, kv head, chunk, so a range streams
+// through consecutive chunks of one cache. The item numbering (a prefix sum
+// over (b, branch) of kv heads x chunks) and each sequence's last position
+// are built in LDS at the start, so looking up an item reads no global memory.
+//
+// K/V tiles of kStKeys keys stream into LDS by bounds-checked buffer loads
+// with kStStages buffers, across item boundaries, so three tiles are in
+// flight while one is consumed. Each tile is computed with the matrix cores
+// as in the attention kernels: S^T = K Q^T with the kv head's G query heads
+// as the 32 columns (columns G..31 are zero), online softmax per column,
+// O^T += V^T P^T with V^T from the transposing LDS read. Every wave computes
+// the (cheap) scores and softmax; wave w accumulates only d block w of the
+// output, so no cross-wave merge is needed and each wave writes its own
+// slice of the item's partial (max, sum, weighted values) when the item ends.
+constexpr int kStWaves = 4;
+constexpr int kStStages = 4;
+constexpr int kStKeys = 64;
+constexpr int kStPlan = 2048;    // plan entries in LDS: 2B + 1, so B <= 1023
+constexpr int kStMaxB = (kStPlan - 1) / 2;
+constexpr int kWaitLgkm0 = 0xC07F; // s_waitcnt lgkmcnt(0), vmcnt/expcnt untouched
+// s_waitcnt immediate for vmcnt(N), expcnt and lgkmcnt untouched (gfx9
+// encoding: vmcnt bits 3:0 at 3:0, bits 5:4 at 15:14)
+template <int N>
+constexpr int vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  return 0x0F70 | (N & 15) | ((N >> 4) << 14);
+}
+constexpr float kLazy = 8.0f;      // log2 headroom before the running max moves
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int D>
+struct StSmem {
+  // row-major tiles with padded rows (conflict-free 16-byte K reads and
+  // transposing V reads), filled 1 KiB per buffer-load instruction
+  static constexpr int kChunks = D / 8 + 1;
+  static constexpr int vChunks = D / 8 + 2;
+  static constexpr int kStride = kChunks * 8;
+  static constexpr int vStride = vChunks * 8;
+  static constexpr int kElems = kStKeys * kStride;
+  static constexpr int vElems = kStKeys * vStride;
+};
+
+struct StParams {
+  const uint16_t* q;   // [B][Hq][D] bf16
+  const uint16_t* kc;  // [B][Hkv][cap][D]
+  const uint16_t* vc;
+  const int32_t* lens;
+  const uint8_t* selected;
+  float* part;         // as DecParams::part
+  int B, Hq, Hkv, cap, W, nchunk, nwg;
+  float scale_log2;
+};
+
+// Wave w issues instructions j = w, w+4, ... of the NCH that fill one tile;
+// lane l of instruction j moves 16 bytes at byte offset voff[i] of the
+// buffer [base, base + nbytes) to LDS byte 1024*j + 16*l of dst; offsets at
+// or past nbytes read as zero. The resource type is device-only, so it is
+// built here and not in the kernel's lambdas.
+template <int NJ, int NCH>
+__device__ __forceinline__ void st_issue(const uint16_t* base, int nbytes, uint16_t* dst,
+                                         const uint32_t* voff, int wave) {
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(base), (short)0, nbytes, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < NJ; ++i) {
+    const int j = wave + kStWaves * i;
+    if (j < NCH)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)(dst + j * 512), 16, voff[i], 0, 0,
+                                               0);
+  }
+}
+
+__device__ __forceinline__ uint32_t st_pack(float a, float b) { return pack_bf16x2(a, b); }
+
+template <int D>
+__global__ __launch_bounds__(kStWaves * 64, 1) void decode_stream_kernel(StParams p) {
+  using SM = StSmem<D>;
+  constexpr int QS = D / 16;   // 16-wide k steps along d
+  constexpr int DB = D / 32;   // 32-wide d blocks (one per wave)
+  // one LDS object per stage (K tile, then V tile): the compiler tells the
+  // stage being read from the stages whose loads are in flight only when
+  // they are distinct objects, and it tracks few of them
+  __shared__ __attribute__((aligned(16))) uint16_t T0[SM::kElems + SM::vElems];
+  __shared__ __attribute__((aligned(16))) uint16_t T1[SM::kElems + SM::vElems];
+  __shared__ __attribute__((aligned(16))) uint16_t T2[SM::kElems + SM::vElems];
+  __shared__ __attribute__((aligned(16))) uint16_t T3[SM::kElems + SM::vElems];
+  __shared__ int plan[kStPlan];     // plan[s]: first item of segment s = 2b + branch
+  __shared__ int last[kStMaxB];     // last position (lens - 1) of each sequence
+  __shared__ int wtot[kStWaves];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int G = p.Hq / p.Hkv;
+  const int S = 2 * p.B;
+
+  // ---- item numbering -----------------------------------------------------
+  {
+    constexpr int PER = kStPlan / (kStWaves * 64);
+    int cnt[PER], sum = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int s = tid * PER + j;
+      int c = 0;
+      if (s < S) {
+        const int b = s >> 1;
+        const int i = clamp_len(p.lens[b], p.cap) - 1;
+        if ((s & 1) == 0) {
+          last[b] = i;
+          c = i / kChunk - max(0, i - p.W + 1) / kChunk + 1;
+        } else {
+          c = p.selected[b] ? i / kChunk + 1 : 0;
+        }
+        c *= p.Hkv;
+      }
+      cnt[j] = c;
+      sum += c;
+    }
+    // inclusive scan of the per-thread sums: within the wave, then across
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) wtot[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += wtot[w];
+    int ex = base + incl - sum;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      plan[tid * PER + j] = ex;   // past S: the total
+      ex += cnt[j];
+    }
+    __syncthreads();
+  }
+  const int N = plan[S];  // S < kStPlan; plan[S] = total items
+  const int k0 = (int)((long long)N * blockIdx.x / p.nwg);
+  const int k1 = (int)((long long)N * (blockIdx.x + 1) / p.nwg);
+  if (k0 >= k1) return;
+
+  // An item's description; every field is uniform over the workgroup.
+  struct Item {
+    int k, s, b, br, hk, c, ks, ke, t, tb;
+  };
+  auto load_item = [&] __device__ (Item& it, int k) __attribute__((always_inline)) {
+    int s = it.s;
+    while (__builtin_amdgcn_readfirstlane(plan[s + 1]) <= k) ++s;
+    it.k = k;
+    it.s = s;
+    it.b = s >> 1;
+    it.br = s & 1;
+    const int i = __builtin_amdgcn_readfirstlane(last[it.b]);
+    const int lo = max(0, i - p.W + 1);
+    const int cf = it.br == 0 ? lo / kChunk : 0;
+    const int nch = i / kChunk - cf + 1;
+    const int r = k - __builtin_amdgcn_readfirstlane(plan[s]);
+    it.hk = r / nch;
+    it.c = cf + r % nch;
+    it.ks = max(it.c * kChunk, it.br == 0 ? lo : 0);
+    it.ke = min(it.c * kChunk + kChunk, i + 1);
+    it.t = it.ks / kStKeys;
+    it.tb = (it.ke - 1) / kStKeys;
+  };
+  auto advance = [&] __device__ (Item& it) __attribute__((always_inline)) {
+    // next tile; false when the range is done
+    if (it.t < it.tb) {
+      ++it.t;
+      return true;
+    }
+    if (it.k + 1 >= k1) return false;
+    load_item(it, it.k + 1);
+    return true;
+  };
+
+  // ---- tile staging ----------------------------------------------------------
+  constexpr int KJ = (SM::kChunks + kStWaves - 1) / kStWaves;
+  constexpr int VJ = (SM::vChunks + kStWaves - 1) / kStWaves;
+  constexpr uint32_t kPadOff = 0x40000000u;  // past every tile: reads zero
+  uint32_t k_voff[KJ], v_voff[VJ];
+#pragma unroll
+  for (int i = 0; i < KJ; ++i) {
+    const int slot = (wave + kStWaves * i) * 64 + lane;
+    const int row = slot / SM::kChunks, chunk = slot % SM::kChunks;
+    k_voff[i] = chunk < D / 8 ? (uint32_t)(row * D * 2 + chunk * 16) : kPadOff;
+  }
+#pragma unroll
+  for (int i = 0; i < VJ; ++i) {
+    const int slot = (wave + kStWaves * i) * 64 + lane;
+    const int row = slot / SM::vChunks, chunk = slot % SM::vChunks;
+    v_voff[i] = chunk < D / 8 ? (uint32_t)(row * D * 2 + chunk * 16) : kPadOff;
+  }
+  // tile t of (b, kv head): keys t*64 .. of the cache; keys past the last
+  // position read as zero (the range ends there)
+  auto issue = [&] __device__ (const Item& it, uint16_t* kdst, uint16_t* vdst)
+      __attribute__((always_inline)) {
+    const int key0 = it.t * kStKeys;
+    const int i = __builtin_amdgcn_readfirstlane(last[it.b]);
+    const int nbytes = min(i + 1 - key0, kStKeys) * D * 2;
+    const size_t row0 = ((size_t)it.b * p.Hkv + it.hk) * p.cap + key0;
+    st_issue<KJ, SM::kChunks>(p.kc + row0 * D, nbytes, kdst, k_voff, wave);
+    st_issue<VJ, SM::vChunks>(p.vc + row0 * D, nbytes, vdst, v_voff, wave);
+  };
+  const int n_issue = __builtin_amdgcn_readfirstlane(
+      (SM::kChunks - wave + kStWaves - 1) / kStWaves + (SM::vChunks - wave + kStWaves - 1) / kStWaves);
+  // wait until at most `ahead` newer tiles' loads of this wave are in flight
+  // (waiting for fewer is always safe)
+  auto wait_tiles = [&] __device__ (int ahead) __attribute__((always_inline)) {
+    const int c = ahead * n_issue;
+    if (c <= 0) __builtin_amdgcn_s_waitcnt(vm_wait<0>());
+    else if (c < 8) __builtin_amdgcn_s_waitcnt(vm_wait<4>());
+    else if (c < 12) __builtin_amdgcn_s_waitcnt(vm_wait<8>());
+    else if (c < 16) __builtin_amdgcn_s_waitcnt(vm_wait<12>());
+    else if (c < 20) __builtin_amdgcn_s_waitcnt(vm_wait<16>());
+    else __builtin_amdgcn_s_waitcnt(vm_wait<20>());
+  };
+
+  // ---- per-item state ----------------------------------------------------------
+  bf16x8 qreg[QS];
+  auto load_q = [&] __device__ (const Item& it) __attribute__((always_inline)) {
+    const bool ok = col < G;
+    const uint16_t* qrow = p.q + ((size_t)it.b * p.Hq + it.hk * G + (ok ? col : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      const uint4 x = ok ? *reinterpret_cast<const uint4*>(qrow + s * 16 + half * 8)
+                         : make_uint4(0, 0, 0, 0);
+      qreg[s] = __builtin_bit_cast(bf16x8, x);
+    }
+  };
+  f32x16 acc = (f32x16){};
+  float m_run = -1.0e30f, l_run = 0.0f;
+
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
+  // LDS reads take one integer offset from the stage object itself: a
+  // pointer derived through several steps loses the alias information that
+  // tells the compiler this stage is not the one whose loads are in flight,
+  // and every such read then waits for all of them
+  auto read_vf = [&] __device__ (const uint16_t* tb, int kb, int hh)
+      __attribute__((always_inline)) {
+    const int kbase = kb * 32 + hh * 16 + half * 4 + tr_row;
+    const int o0 = SM::kElems + kbase * SM::vStride + wave * 32 + tr_col;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(tb + o0));
+    const v4i16 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(tb + (o0 + 8 * SM::vStride)));
+    const uint2 l2 = __builtin_bit_cast(uint2, lo);
+    const uint2 h2 = __builtin_bit_cast(uint2, hi);
+    return __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+  };
+
+  // one tile of the current item: scores of both 32-key blocks, online
+  // softmax per query column, this wave's d block of P V
+  auto compute = [&] __device__ (const Item& it, const uint16_t* tb)
+      __attribute__((always_inline)) {
+    const int key0 = it.t * kStKeys;
+    const bool full = key0 >= it.ks && key0 + kStKeys <= it.ke;
+    f32x16 sc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int krow = (kb * 32 + col) * SM::kStride + half * 8;
+      bf16x8 kf[QS];
+#pragma unroll
+      for (int s = 0; s < QS; ++s)
+        kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(tb + (krow + s * 16)));
+#pragma unroll
+      for (int s = 0; s < QS; ++s)
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qreg[s],
+                                                         s ? sc[kb] : (f32x16){}, 0, 0, 0);
+    }
+    if (!full) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = key0 + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+          sc[kb][e] = key >= it.ks && key < it.ke ? sc[kb][e] : -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                      false, false);
+    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * p.scale_log2;
+    const float m_new = mx > m_run + kLazy ? mx : m_run;
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) acc *= alpha;
+    uint32_t pk[2][8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][2 * c], p.scale_log2, -m_run));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][2 * c + 1], p.scale_log2, -m_run));
+        l_run += p0 + p1;
+        pk[kb][c] = st_pack(p0, p1);
+      }
+    if (wave < DB) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 v0 = read_vf(tb, kb, 0);
+        const bf16x8 v1 = read_vf(tb, kb, 1);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            v0, __builtin_bit_cast(bf16x8, make_uint4(pk[kb][0], pk[kb][1], pk[kb][2], pk[kb][3])),
+            acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            v1, __builtin_bit_cast(bf16x8, make_uint4(pk[kb][4], pk[kb][5], pk[kb][6], pk[kb][7])),
+            acc, 0, 0, 0);
+      }
+    }
+  };
+  // the item's partial: this wave's d block for query heads < G; wave 0 adds
+  // the max and the sum
+  auto flush = [&] __device__ (const Item& it) __attribute__((always_inline)) {
+    const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
+                                                       __float_as_uint(l_run), false, false);
+    const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
+    if (col < G) {
+      float* out = p.part + ((((size_t)it.b * p.Hq + it.hk * G + col) * p.nchunk + it.c) * 2 +
+                             it.br) * (D + 2);
+      if (wave < DB) {
+        // slots are (D + 2) floats: 4-byte aligned only, so scalar stores
+#pragma unroll
+        for (int e = 0; e < 16; ++e) out[wave * 32 + (e >> 2) * 8 + half * 4 + (e & 3)] = acc[e];
+      }
+      if (wave == 0 && half == 0) {
+        out[D] = m_run;
+        out[D + 1] = l_tot;
+      }
+    }
+    acc = (f32x16){};
+    m_run = -1.0e30f;
+    l_run = 0.0f;
+  };
+
+  // ---- the stream ------------------------------------------------------------
+  // Tile number q (counted from 0 over this workgroup's range) lives in
+  // buffer q % 4; the steps are unrolled four times so every LDS access
+  // names its buffer at compile time.
+  Item ci, ii;  // the tile being computed, the next tile to issue
+  ci.s = 0;
+  load_item(ci, k0);
+  ii = ci;
+  bool more = true;  // ii names a tile not yet issued
+  int issued = 0, done = 0;
+  auto prime = [&] __device__ (uint16_t* td) __attribute__((always_inline)) {
+    if (more) {
+      issue(ii, td, td + SM::kElems);
+      ++issued;
+      more = advance(ii);
+    }
+  };
+  prime(T0);
+  prime(T1);
+  prime(T2);
+  // Q of the first item; the explicit wait keeps the loop free of pending
+  // register loads (a reload happens only when (b, kv head) changes)
+  auto reload_q = [&] __device__ () __attribute__((always_inline)) {
+    load_q(ci);
+    __builtin_amdgcn_s_waitcnt(vm_wait<0>());
+  };
+  reload_q();
+  int qb = ci.b, qh = ci.hk;
+  bool live = true;
+  auto step = [&] __device__ (const uint16_t* tc, uint16_t* tn) __attribute__((always_inline)) {
+    wait_tiles(issued - done - 1);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    if (more) {
+      issue(ii, tn, tn + SM::kElems);
+      ++issued;
+      more = advance(ii);
+    }
+    compute(ci, tc);
+    ++done;
+    const bool item_end = ci.t == ci.tb;
+    if (item_end) flush(ci);
+    live = advance(ci);
+    if (live && item_end && (ci.b != qb || ci.hk != qh)) {
+      reload_q();
+      qb = ci.b;
+      qh = ci.hk;
+    }
+  };
+#pragma unroll 1
+  while (live) {
+    step(T0, T3);
+    if (live) step(T1, T0);
+    if (live) step(T2, T1);
+    if (live) step(T3, T2);
+  }
+  __builtin_amdgcn_s_waitcnt(vm_wait<0>());
+}
+
 struct RedParams {
   const float* part;
   const int32_t* lens;
@@ -445,6 +854,16 @@ __global__ __launch_bounds__(1024) void select_threshold_kernel(const float* gat
   if (t == 0) count[b] = total;
 }
 
+// compute units of the current device (the stream kernel runs one
+// workgroup on each)
+int compute_units() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return 256;
+  return n;
+}
+
 template <int D, int G, bool BF16>
 hipError_t decode_t(const DecodeDims& d, const DecodeArgs& a, hipStream_t s) {
   DecParams p;
@@ -461,8 +880,28 @@ hipError_t decode_t(const DecodeDims& d, const DecodeArgs& a, hipStream_t s) {
   p.W = d.window;
   p.nchunk = (d.cap + kChunk - 1) / kChunk;
   p.scale_log2 = d.scale * kLog2e;
-  const dim3 grid((unsigned)(2LL * d.B * d.Hkv * p.nchunk));
-  hipLaunchKernelGGL((decode_partial_kernel<D, G, BF16>), grid, dim3(kDecWaves * 64), 0, s, p);
+  if (BF16 && d.B <= kStMaxB) {
+    StParams sp;
+    sp.q = static_cast<const uint16_t*>(a.q);
+    sp.kc = static_cast<const uint16_t*>(a.k_cache);
+    sp.vc = static_cast<const uint16_t*>(a.v_cache);
+    sp.lens = a.lens;
+    sp.selected = a.selected;
+    sp.part = a.part;
+    sp.B = d.B;
+    sp.Hq = d.Hq;
+    sp.Hkv = d.Hkv;
+    sp.cap = d.cap;
+    sp.W = d.window;
+    sp.nchunk = p.nchunk;
+    sp.nwg = compute_units();
+    sp.scale_log2 = p.scale_log2;
+    hipLaunchKernelGGL((decode_stream_kernel<D>), dim3((unsigned)sp.nwg),
+                       dim3(kStWaves * 64), 0, s, sp);
+  } else {
+    const dim3 grid((unsigned)(2LL * d.B * d.Hkv * p.nchunk));
+    hipLaunchKernelGGL((decode_partial_kernel<D, G, BF16>), grid, dim3(kDecWaves * 64), 0, s, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   RedParams r;
