@@ -321,27 +321,32 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_partial_kernel(DecParam
 
 // ---- bf16 decode as a persistent stream ------------------------------------
 //
-// One workgroup per compute unit walks a balanced, contiguous range of work
-// items, an item being (b, branch, kv head, chunk of kChunk keys) with at
-// least one key to read: local items cover the chunks that overlap the
-// window, global items every chunk of a selected sequence. Items are
-// numbered sequence-major, branch, kv head, chunk, so a range streams
-// through consecutive chunks of one cache. The item numbering (a prefix sum
-// over (b, branch) of kv heads x chunks) and each sequence's last position
-// are built in LDS at the start, so looking up an item reads no global memory.
+// One workgroup per compute unit takes every nwg-th work item, an item
+// being (b, branch, kv head, chunk of kChunk keys) with at least one key to
+// read: local items cover the chunks that overlap the window, global items
+// every chunk of a selected sequence. Items are numbered sequence-major,
+// branch, kv head, chunk, so at any moment the workgroups read neighbouring
+// chunks of the same caches (HBM serves such a sweep measurably faster than
+// as many separate streams). The item numbering (a prefix sum over
+// (b, branch) of kv heads x chunks) and each sequence's last position are
+// built in LDS at the start, so looking up an item reads no global memory.
 //
-// K/V tiles of kStKeys keys stream into LDS by bounds-checked buffer loads
-// with kStStages buffers, across item boundaries, so three tiles are in
-// flight while one is consumed. Each tile is computed with the matrix cores
-// as in the attention kernels: S^T = K Q^T with the kv head's G query heads
-// as the 32 columns (columns G..31 are zero), online softmax per column,
-// O^T += V^T P^T with V^T from the transposing LDS read. Every wave computes
-// the (cheap) scores and softmax; wave w accumulates only d block w of the
-// output, so no cross-wave merge is needed and each wave writes its own
-// slice of the item's partial (max, sum, weighted values) when the item ends.
+// K/V tiles of kStKeys keys, with the item's query rows, stream into LDS by
+// bounds-checked buffer loads with kStStages buffers, across item
+// boundaries: three tiles are always in flight while one is consumed (past
+// the end of the range, loads of an empty range keep the count, so every
+// wait is the same). Each tile is computed on
+// the matrix cores with the kv head's G query heads as 16 columns (columns
+// G..15 are zero): S^T = K Q^T (16x16x32 steps), online softmax per column,
+// O^T += V^T P^T (16x16x16 steps, V^T from the transposing LDS read). Every
+// wave computes the scores and the softmax; wave w accumulates only its
+// share of the d blocks, so no cross-wave merge is needed and each wave
+// writes its own slice of the item's partial (max, sum, weighted values)
+// when the item ends.
 constexpr int kStWaves = 4;
 constexpr int kStStages = 4;
 constexpr int kStKeys = 64;
+constexpr int kStCols = 16;      // query heads per kv head the kernel takes
 constexpr int kStPlan = 2048;    // plan entries in LDS: 2B + 1, so B <= 1023
 constexpr int kStMaxB = (kStPlan - 1) / 2;
 constexpr int kWaitLgkm0 = 0xC07F; // s_waitcnt lgkmcnt(0), vmcnt/expcnt untouched
@@ -355,18 +360,26 @@ constexpr int vm_wait() {
 constexpr float kLazy = 8.0f;      // log2 headroom before the running max moves
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Tiles are row-major without padding (a K tile then a V tile per stage);
+// bank conflicts are avoided by storing 16-byte chunk c of row r at chunk
+// c ^ f(r): for K reads (16 consecutive rows, one chunk) f spreads the rows
+// over all banks; for the transposing V reads (8 rows, two adjacent chunks)
+// f moves whole chunk pairs.
 template <int D>
-struct StSmem {
-  // row-major tiles with padded rows (conflict-free 16-byte K reads and
-  // transposing V reads), filled 1 KiB per buffer-load instruction
-  static constexpr int kChunks = D / 8 + 1;
-  static constexpr int vChunks = D / 8 + 2;
-  static constexpr int kStride = kChunks * 8;
-  static constexpr int vStride = vChunks * 8;
-  static constexpr int kElems = kStKeys * kStride;
-  static constexpr int vElems = kStKeys * vStride;
+struct StTile {
+  static constexpr int kCpr = D / 8;                  // 16-byte chunks per row
+  static constexpr int kElems = kStKeys * D;          // one K or V tile
+  // the item's query rows, padded to one load per wave (rows past G, and
+  // the padding, read as zero)
+  static constexpr int qElems = kStCols * D > 2048 ? kStCols * D : 2048;
+  static constexpr int kStage = 2 * kElems + qElems;  // K tile, V tile, query rows
+  static constexpr int kInstr = kCpr / kStWaves;      // buffer loads per wave per tile
+  static constexpr int qInstr = qElems / 512 / kStWaves;  // ... and per query block
+  __device__ static int fk(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static int fv(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
 };
 
 struct StParams {
@@ -380,46 +393,41 @@ struct StParams {
   float scale_log2;
 };
 
-// Wave w issues instructions j = w, w+4, ... of the NCH that fill one tile;
-// lane l of instruction j moves 16 bytes at byte offset voff[i] of the
+// Wave w issues instructions j = w, w+4, ... (NJ of them) that fill one
+// tile: lane l of instruction j moves 16 bytes at byte offset voff[i] of the
 // buffer [base, base + nbytes) to LDS byte 1024*j + 16*l of dst; offsets at
-// or past nbytes read as zero. The resource type is device-only, so it is
-// built here and not in the kernel's lambdas.
-template <int NJ, int NCH>
-__device__ __forceinline__ void st_issue(const uint16_t* base, int nbytes, uint16_t* dst,
+// or past nbytes read as zero (nbytes = 0: the whole tile). The resource
+// type is device-only, so it is built here and not in the kernel's lambdas.
+template <int NJ>
+__device__ __forceinline__ void st_issue(const void* base, int nbytes, uint16_t* dst,
                                          const uint32_t* voff, int wave) {
   typedef __attribute__((address_space(3))) void* lds_ptr;
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(base), (short)0, nbytes, 0x00020000);
+      const_cast<void*>(base), (short)0, nbytes, 0x00020000);
 #pragma unroll
-  for (int i = 0; i < NJ; ++i) {
-    const int j = wave + kStWaves * i;
-    if (j < NCH)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)(dst + j * 512), 16, voff[i], 0, 0,
-                                               0);
-  }
+  for (int i = 0; i < NJ; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)(dst + (wave + kStWaves * i) * 512),
+                                             16, voff[i], 0, 0, 0);
 }
-
-__device__ __forceinline__ uint32_t st_pack(float a, float b) { return pack_bf16x2(a, b); }
 
 template <int D>
 __global__ __launch_bounds__(kStWaves * 64, 1) void decode_stream_kernel(StParams p) {
-  using SM = StSmem<D>;
-  constexpr int QS = D / 16;   // 16-wide k steps along d
-  constexpr int DB = D / 32;   // 32-wide d blocks (one per wave)
-  // one LDS object per stage (K tile, then V tile): the compiler tells the
-  // stage being read from the stages whose loads are in flight only when
-  // they are distinct objects, and it tracks few of them
-  __shared__ __attribute__((aligned(16))) uint16_t T0[SM::kElems + SM::vElems];
-  __shared__ __attribute__((aligned(16))) uint16_t T1[SM::kElems + SM::vElems];
-  __shared__ __attribute__((aligned(16))) uint16_t T2[SM::kElems + SM::vElems];
-  __shared__ __attribute__((aligned(16))) uint16_t T3[SM::kElems + SM::vElems];
+  using TL = StTile<D>;
+  constexpr int QS = D / 32;            // 32-wide k steps of the scores
+  constexpr int DBW = D / 16 / kStWaves;  // 16-wide d blocks per wave
+  // one LDS object per stage (K tile, V tile, query rows): the compiler
+  // tells the stage being read from the stages whose loads are in flight
+  // only when they are distinct objects
+  __shared__ __attribute__((aligned(16))) uint16_t T0[TL::kStage];
+  __shared__ __attribute__((aligned(16))) uint16_t T1[TL::kStage];
+  __shared__ __attribute__((aligned(16))) uint16_t T2[TL::kStage];
+  __shared__ __attribute__((aligned(16))) uint16_t T3[TL::kStage];
   __shared__ int plan[kStPlan];     // plan[s]: first item of segment s = 2b + branch
   __shared__ int last[kStMaxB];     // last position (lens - 1) of each sequence
   __shared__ int wtot[kStWaves];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int col = lane & 31, half = lane >> 5;
+  const int col = lane & 15, grp = lane >> 4;
   const int G = p.Hq / p.Hkv;
   const int S = 2 * p.B;
 
@@ -465,9 +473,8 @@ __global__ __launch_bounds__(kStWaves * 64, 1) void decode_stream_kernel(StParam
     __syncthreads();
   }
   const int N = plan[S];  // S < kStPlan; plan[S] = total items
-  const int k0 = (int)((long long)N * blockIdx.x / p.nwg);
-  const int k1 = (int)((long long)N * (blockIdx.x + 1) / p.nwg);
-  if (k0 >= k1) return;
+  const int k0 = blockIdx.x;  // items k0, k0 + nwg, ... below N
+  if (k0 >= N) return;
 
   // An item's description; every field is uniform over the workgroup.
   struct Item {
@@ -498,179 +505,175 @@ __global__ __launch_bounds__(kStWaves * 64, 1) void decode_stream_kernel(StParam
       ++it.t;
       return true;
     }
-    if (it.k + 1 >= k1) return false;
-    load_item(it, it.k + 1);
+    if (it.k + p.nwg >= N) return false;
+    load_item(it, it.k + p.nwg);
     return true;
   };
 
   // ---- tile staging ----------------------------------------------------------
-  constexpr int KJ = (SM::kChunks + kStWaves - 1) / kStWaves;
-  constexpr int VJ = (SM::vChunks + kStWaves - 1) / kStWaves;
-  constexpr uint32_t kPadOff = 0x40000000u;  // past every tile: reads zero
-  uint32_t k_voff[KJ], v_voff[VJ];
+  uint32_t k_voff[TL::kInstr], v_voff[TL::kInstr], q_voff[TL::qInstr];
 #pragma unroll
-  for (int i = 0; i < KJ; ++i) {
-    const int slot = (wave + kStWaves * i) * 64 + lane;
-    const int row = slot / SM::kChunks, chunk = slot % SM::kChunks;
-    k_voff[i] = chunk < D / 8 ? (uint32_t)(row * D * 2 + chunk * 16) : kPadOff;
+  for (int i = 0; i < TL::kInstr; ++i) {
+    const int byte = (wave + kStWaves * i) * 1024 + lane * 16;
+    const int r = byte / (2 * D), q = (byte % (2 * D)) / 16;
+    k_voff[i] = (uint32_t)(r * 2 * D + (q ^ TL::fk(r)) * 16);
+    v_voff[i] = (uint32_t)(r * 2 * D + (q ^ TL::fv(r)) * 16);
   }
 #pragma unroll
-  for (int i = 0; i < VJ; ++i) {
-    const int slot = (wave + kStWaves * i) * 64 + lane;
-    const int row = slot / SM::vChunks, chunk = slot % SM::vChunks;
-    v_voff[i] = chunk < D / 8 ? (uint32_t)(row * D * 2 + chunk * 16) : kPadOff;
+  for (int i = 0; i < TL::qInstr; ++i) {
+    const int byte = (wave + kStWaves * i) * 1024 + lane * 16;
+    const int r = byte / (2 * D), q = (byte % (2 * D)) / 16;
+    q_voff[i] = (uint32_t)(r * 2 * D + (q ^ TL::fk(r)) * 16);
   }
   // tile t of (b, kv head): keys t*64 .. of the cache; keys past the last
-  // position read as zero (the range ends there)
-  auto issue = [&] __device__ (const Item& it, uint16_t* kdst, uint16_t* vdst)
+  // position read as zero (the range ends there); `real` false: an empty
+  // range (no memory is read) that only keeps the count of loads
+  auto issue = [&] __device__ (const Item& it, bool real, uint16_t* dst)
       __attribute__((always_inline)) {
     const int key0 = it.t * kStKeys;
     const int i = __builtin_amdgcn_readfirstlane(last[it.b]);
-    const int nbytes = min(i + 1 - key0, kStKeys) * D * 2;
+    const int nbytes = real ? min(i + 1 - key0, kStKeys) * D * 2 : 0;
     const size_t row0 = ((size_t)it.b * p.Hkv + it.hk) * p.cap + key0;
-    st_issue<KJ, SM::kChunks>(p.kc + row0 * D, nbytes, kdst, k_voff, wave);
-    st_issue<VJ, SM::vChunks>(p.vc + row0 * D, nbytes, vdst, v_voff, wave);
-  };
-  const int n_issue = __builtin_amdgcn_readfirstlane(
-      (SM::kChunks - wave + kStWaves - 1) / kStWaves + (SM::vChunks - wave + kStWaves - 1) / kStWaves);
-  // wait until at most `ahead` newer tiles' loads of this wave are in flight
-  // (waiting for fewer is always safe)
-  auto wait_tiles = [&] __device__ (int ahead) __attribute__((always_inline)) {
-    const int c = ahead * n_issue;
-    if (c <= 0) __builtin_amdgcn_s_waitcnt(vm_wait<0>());
-    else if (c < 8) __builtin_amdgcn_s_waitcnt(vm_wait<4>());
-    else if (c < 12) __builtin_amdgcn_s_waitcnt(vm_wait<8>());
-    else if (c < 16) __builtin_amdgcn_s_waitcnt(vm_wait<12>());
-    else if (c < 20) __builtin_amdgcn_s_waitcnt(vm_wait<16>());
-    else __builtin_amdgcn_s_waitcnt(vm_wait<20>());
+    st_issue<TL::kInstr>(p.kc + row0 * D, nbytes, dst, k_voff, wave);
+    st_issue<TL::kInstr>(p.vc + row0 * D, nbytes, dst + TL::kElems, v_voff, wave);
+    // the G query rows of (b, kv head); rows G.. read as zero
+    st_issue<TL::qInstr>(p.q + ((size_t)it.b * p.Hq + it.hk * G) * D, real ? G * D * 2 : 0,
+                         dst + 2 * TL::kElems, q_voff, wave);
   };
 
   // ---- per-item state ----------------------------------------------------------
-  bf16x8 qreg[QS];
-  auto load_q = [&] __device__ (const Item& it) __attribute__((always_inline)) {
-    const bool ok = col < G;
-    const uint16_t* qrow = p.q + ((size_t)it.b * p.Hq + it.hk * G + (ok ? col : 0)) * D;
+  f32x4 acc[DBW];
 #pragma unroll
-    for (int s = 0; s < QS; ++s) {
-      const uint4 x = ok ? *reinterpret_cast<const uint4*>(qrow + s * 16 + half * 8)
-                         : make_uint4(0, 0, 0, 0);
-      qreg[s] = __builtin_bit_cast(bf16x8, x);
-    }
-  };
-  f32x16 acc = (f32x16){};
+  for (int j = 0; j < DBW; ++j) acc[j] = (f32x4){};
   float m_run = -1.0e30f, l_run = 0.0f;
 
-  const int tr_row = (lane & 15) >> 2;
-  const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
   typedef short v4i16 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
   // LDS reads take one integer offset from the stage object itself: a
   // pointer derived through several steps loses the alias information that
-  // tells the compiler this stage is not the one whose loads are in flight,
-  // and every such read then waits for all of them
-  auto read_vf = [&] __device__ (const uint16_t* tb, int kb, int hh)
+  // tells the compiler this stage is not one whose loads are in flight, and
+  // every such read then waits for all of them.
+  //
+  // K fragment (A of 16x16x32): key kb*16 + col, d chunk 4 s + grp
+  auto read_k = [&] __device__ (const uint16_t* tb, int kb, int s)
       __attribute__((always_inline)) {
-    const int kbase = kb * 32 + hh * 16 + half * 4 + tr_row;
-    const int o0 = SM::kElems + kbase * SM::vStride + wave * 32 + tr_col;
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(tb + o0));
-    const v4i16 hi =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(tb + (o0 + 8 * SM::vStride)));
-    const uint2 l2 = __builtin_bit_cast(uint2, lo);
-    const uint2 h2 = __builtin_bit_cast(uint2, hi);
-    return __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+    const int r = kb * 16 + col;
+    const int off = r * D + (((4 * s + grp) ^ TL::fk(r)) * 8);
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(tb + off));
+  };
+  // Q^T fragment (B of 16x16x32): query head `col`, d chunk 4 s + grp
+  auto read_q = [&] __device__ (const uint16_t* tb, int s) __attribute__((always_inline)) {
+    const int off = 2 * TL::kElems + col * D + (((4 * s + grp) ^ TL::fk(col)) * 8);
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(tb + off));
+  };
+  // V^T fragment (A of 16x16x16) through the transposing read: within each
+  // 16-lane group, source lane s addresses key row 4*grp + s/4 and d columns
+  // 16*db + 4*(s%4); the destination lane then holds d = 16*db + col for
+  // keys kb*16 + 4*grp + [0, 4)
+  auto read_v = [&] __device__ (const uint16_t* tb, int kb, int db)
+      __attribute__((always_inline)) {
+    const int r = kb * 16 + 4 * grp + (col >> 2);
+    const int cc = 2 * db + ((col & 3) >> 1);
+    const int off = TL::kElems + r * D + ((cc ^ TL::fv(r)) * 8) + 4 * (col & 1);
+    return __builtin_bit_cast(
+        bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(tb + off)));
   };
 
-  // one tile of the current item: scores of both 32-key blocks, online
-  // softmax per query column, this wave's d block of P V
+  // one tile of the current item: scores of the four 16-key blocks, online
+  // softmax per query column, this wave's d blocks of P V
   auto compute = [&] __device__ (const Item& it, const uint16_t* tb)
       __attribute__((always_inline)) {
     const int key0 = it.t * kStKeys;
     const bool full = key0 >= it.ks && key0 + kStKeys <= it.ke;
-    f32x16 sc[2];
+    bf16x8 qf[QS];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int krow = (kb * 32 + col) * SM::kStride + half * 8;
+    for (int s = 0; s < QS; ++s) qf[s] = read_q(tb, s);
+    f32x4 sc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
       bf16x8 kf[QS];
 #pragma unroll
-      for (int s = 0; s < QS; ++s)
-        kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(tb + (krow + s * 16)));
+      for (int s = 0; s < QS; ++s) kf[s] = read_k(tb, kb, s);
 #pragma unroll
       for (int s = 0; s < QS; ++s)
-        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qreg[s],
-                                                         s ? sc[kb] : (f32x16){}, 0, 0, 0);
+        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[s], s ? sc[kb] : (f32x4){},
+                                                         0, 0, 0);
     }
     if (!full) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = key0 + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+        for (int e = 0; e < 4; ++e) {
+          const int key = key0 + kb * 16 + 4 * grp + e;
           sc[kb][e] = key >= it.ks && key < it.ke ? sc[kb][e] : -INFINITY;
         }
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sc[kb][e]);
+    // the column's max over its four lanes (col, col+16, col+32, col+48)
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                       false, false);
-    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * p.scale_log2;
+    mx = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                      false, false);
+    mx = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1])) * p.scale_log2;
     const float m_new = mx > m_run + kLazy ? mx : m_run;
     const float alpha = exp2f(m_run - m_new);
     m_run = m_new;
     l_run *= alpha;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) acc *= alpha;
-    uint32_t pk[2][8];
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int j = 0; j < DBW; ++j) acc[j] *= alpha;
+    }
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][2 * c], p.scale_log2, -m_run));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][2 * c + 1], p.scale_log2, -m_run));
-        l_run += p0 + p1;
-        pk[kb][c] = st_pack(p0, p1);
+    for (int kb = 0; kb < 4; ++kb) {
+      float pr[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pr[e] = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], p.scale_log2, -m_run));
+        l_run += pr[e];
       }
-    if (wave < DB) {
+      const bf16x4 pt = __builtin_bit_cast(
+          bf16x4, make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])));
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 v0 = read_vf(tb, kb, 0);
-        const bf16x8 v1 = read_vf(tb, kb, 1);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            v0, __builtin_bit_cast(bf16x8, make_uint4(pk[kb][0], pk[kb][1], pk[kb][2], pk[kb][3])),
-            acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            v1, __builtin_bit_cast(bf16x8, make_uint4(pk[kb][4], pk[kb][5], pk[kb][6], pk[kb][7])),
-            acc, 0, 0, 0);
-      }
+      for (int j = 0; j < DBW; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(read_v(tb, kb, wave * DBW + j), pt,
+                                                           acc[j], 0, 0, 0);
     }
   };
-  // the item's partial: this wave's d block for query heads < G; wave 0 adds
-  // the max and the sum
+  // the item's partial: this wave's d blocks for query heads < G; wave 0
+  // adds the max and the sum
   auto flush = [&] __device__ (const Item& it) __attribute__((always_inline)) {
-    const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
-                                                       __float_as_uint(l_run), false, false);
-    const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(l_run),
+                                                      __float_as_uint(l_run), false, false);
+    float l_tot = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_tot),
+                                                      __float_as_uint(l_tot), false, false);
+    l_tot = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
     if (col < G) {
       float* out = p.part + ((((size_t)it.b * p.Hq + it.hk * G + col) * p.nchunk + it.c) * 2 +
                              it.br) * (D + 2);
-      if (wave < DB) {
-        // slots are (D + 2) floats: 4-byte aligned only, so scalar stores
+      // slots are (D + 2) floats: 4-byte aligned only, so scalar stores
 #pragma unroll
-        for (int e = 0; e < 16; ++e) out[wave * 32 + (e >> 2) * 8 + half * 4 + (e & 3)] = acc[e];
-      }
-      if (wave == 0 && half == 0) {
+      for (int j = 0; j < DBW; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[(wave * DBW + j) * 16 + 4 * grp + e] = acc[j][e];
+      if (wave == 0 && grp == 0) {
         out[D] = m_run;
         out[D + 1] = l_tot;
       }
     }
-    acc = (f32x16){};
+#pragma unroll
+    for (int j = 0; j < DBW; ++j) acc[j] = (f32x4){};
     m_run = -1.0e30f;
     l_run = 0.0f;
   };
 
   // ---- the stream ------------------------------------------------------------
-  // Tile number q (counted from 0 over this workgroup's range) lives in
+  // Tile number q (counted from 0 over this workgroup's items) lives in
   // buffer q % 4; the steps are unrolled four times so every LDS access
   // names its buffer at compile time.
   Item ci, ii;  // the tile being computed, the next tile to issue
@@ -678,45 +681,25 @@ __global__ __launch_bounds__(kStWaves * 64, 1) void decode_stream_kernel(StParam
   load_item(ci, k0);
   ii = ci;
   bool more = true;  // ii names a tile not yet issued
-  int issued = 0, done = 0;
-  auto prime = [&] __device__ (uint16_t* td) __attribute__((always_inline)) {
-    if (more) {
-      issue(ii, td, td + SM::kElems);
-      ++issued;
-      more = advance(ii);
-    }
+  auto put = [&] __device__ (uint16_t* dst) __attribute__((always_inline)) {
+    issue(ii, more, dst);
+    if (more) more = advance(ii);
   };
-  prime(T0);
-  prime(T1);
-  prime(T2);
-  // Q of the first item; the explicit wait keeps the loop free of pending
-  // register loads (a reload happens only when (b, kv head) changes)
-  auto reload_q = [&] __device__ () __attribute__((always_inline)) {
-    load_q(ci);
-    __builtin_amdgcn_s_waitcnt(vm_wait<0>());
-  };
-  reload_q();
-  int qb = ci.b, qh = ci.hk;
+  put(T0);
+  put(T1);
+  put(T2);
   bool live = true;
   auto step = [&] __device__ (const uint16_t* tc, uint16_t* tn) __attribute__((always_inline)) {
-    wait_tiles(issued - done - 1);
+    // three tiles are in flight: the oldest (this one) has landed once at
+    // most two tiles' loads remain
+    __builtin_amdgcn_s_waitcnt(vm_wait<2 * (2 * TL::kInstr + TL::qInstr)>());
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
-    if (more) {
-      issue(ii, tn, tn + SM::kElems);
-      ++issued;
-      more = advance(ii);
-    }
+    put(tn);
     compute(ci, tc);
-    ++done;
     const bool item_end = ci.t == ci.tb;
     if (item_end) flush(ci);
     live = advance(ci);
-    if (live && item_end && (ci.b != qb || ci.hk != qh)) {
-      reload_q();
-      qb = ci.b;
-      qh = ci.hk;
-    }
   };
 #pragma unroll 1
   while (live) {
@@ -737,14 +720,18 @@ struct RedParams {
   int B, Hq, cap, W, nchunk;
 };
 
-// One workgroup per (b, query head): the four waves take every fourth chunk
-// of a branch (lanes over d) and merge their sums through LDS in wave order
-// (deterministic), then combine the branches.
+// One workgroup per (b, query head): for each branch the kRedWaves waves
+// take every kRedWaves-th chunk partial, kRedBatch of them in flight at a
+// time, and keep an online merge (running max, rescaled sum and weighted
+// values); the waves' states are then merged through LDS in wave order
+// (deterministic) and the branches combined.
+constexpr int kRedWaves = 8;
+constexpr int kRedBatch = 16;
+
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void decode_reduce_kernel(RedParams p) {
-  constexpr int NC = D / 64;
-  __shared__ float wpart[4][D + 1];
-  __shared__ float wmx[4];
+__global__ __launch_bounds__(kRedWaves * 64) void decode_reduce_kernel(RedParams p) {
+  constexpr int NC = D / 64;   // d elements per lane
+  __shared__ float wpart[kRedWaves][D + 2];
   const long long w = blockIdx.x;  // b * Hq + h
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int b = (int)(w / p.Hq);
@@ -758,37 +745,60 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(RedParams p) {
     if (br == 1 && !sel) break;  // uniform
     const int cfirst = br == 0 ? lo / kChunk : 0;
     const int clast = i / kChunk;
-    // this wave's max over its chunks, then the workgroup's
-    // lanes over chunks for the maxima
-    float mx = kNeg;
-    for (int c = cfirst + threadIdx.x; c <= clast; c += 256)
-      mx = fmaxf(mx, p.part[((w * p.nchunk + c) * 2 + br) * (D + 2) + D]);
-    mx = wmax(mx);
-    if (lane == 0) wmx[wave] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(wmx[0], wmx[1]), fmaxf(wmx[2], wmx[3]));
-    float a[NC], ls = 0.0f;
+    float m = kNeg, l = 0.0f, a[NC];
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) a[cc] = 0.0f;
-#pragma unroll 8
-    for (int c = cfirst + wave; c <= clast; c += 4) {
-      const float* pt = p.part + ((w * p.nchunk + c) * 2 + br) * (D + 2);
-      const float f = exp2f(pt[D] - mx);
-      ls = fmaf(f, pt[D + 1], ls);
+    for (int c0 = cfirst + wave; c0 <= clast; c0 += kRedWaves * kRedBatch) {
+      float pm[kRedBatch], pl[kRedBatch], pa[kRedBatch][NC];
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) a[cc] = fmaf(f, pt[lane + 64 * cc], a[cc]);
+      for (int u = 0; u < kRedBatch; ++u) {
+        const int c = c0 + u * kRedWaves;
+        const bool ok = c <= clast;
+        const float* pt = p.part + ((w * p.nchunk + (ok ? c : cfirst)) * 2 + br) * (D + 2);
+        pm[u] = ok ? pt[D] : kNeg;
+        pl[u] = ok ? pt[D + 1] : 0.0f;
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) pa[u][cc] = ok ? pt[lane + 64 * cc] : 0.0f;
+      }
+      float mx = m;
+#pragma unroll
+      for (int u = 0; u < kRedBatch; ++u) mx = fmaxf(mx, pm[u]);
+      const float f0 = exp2f(m - mx);
+      l *= f0;
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) a[cc] *= f0;
+#pragma unroll
+      for (int u = 0; u < kRedBatch; ++u) {
+        const float f = exp2f(pm[u] - mx);
+        l = fmaf(f, pl[u], l);
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) a[cc] = fmaf(f, pa[u][cc], a[cc]);
+      }
+      m = mx;
     }
+    // merge the waves' states in wave order
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) wpart[wave][lane + 64 * cc] = a[cc];
-    if (lane == 0) wpart[wave][D] = ls;
+    if (lane == 0) {
+      wpart[wave][D] = m;
+      wpart[wave][D + 1] = l;
+    }
     __syncthreads();
-    const float tot = wpart[0][D] + wpart[1][D] + wpart[2][D] + wpart[3][D];
-    const float wgt = br == 0 ? 1.0f : 1.0f / (1.0f + expf(-p.gate[b]));
+    if (wave == 0) {
+      float mx = kNeg;
+      for (int v = 0; v < kRedWaves; ++v) mx = fmaxf(mx, wpart[v][D]);
+      float tot = 0.0f, sum[NC];
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
-      const int dd = lane + 64 * cc;
-      const float sum = wpart[0][dd] + wpart[1][dd] + wpart[2][dd] + wpart[3][dd];
-      out[cc] = fmaf(wgt, sum / tot, out[cc]);
+      for (int cc = 0; cc < NC; ++cc) sum[cc] = 0.0f;
+      for (int v = 0; v < kRedWaves; ++v) {
+        const float f = exp2f(wpart[v][D] - mx);
+        tot = fmaf(f, wpart[v][D + 1], tot);
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) sum[cc] = fmaf(f, wpart[v][lane + 64 * cc], sum[cc]);
+      }
+      const float wgt = br == 0 ? 1.0f : 1.0f / (1.0f + expf(-p.gate[b]));
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) out[cc] = fmaf(wgt, sum[cc] / tot, out[cc]);
     }
     __syncthreads();
   }
@@ -916,7 +926,7 @@ hipError_t decode_t(const DecodeDims& d, const DecodeArgs& a, hipStream_t s) {
   r.W = d.window;
   r.nchunk = p.nchunk;
   hipLaunchKernelGGL((decode_reduce_kernel<D, BF16>), dim3((unsigned)((long long)d.B * d.Hq)),
-                     dim3(256), 0, s, r);
+                     dim3(kRedWaves * 64), 0, s, r);
   return hipGetLastError();
 }
 
