@@ -91,7 +91,7 @@ struct DecParams {
   const void* vc;
   const int32_t* lens;
   const uint8_t* selected;
-  float* part;         // [B][Hq][nchunk][2][D + 2]: acc[D], max (log2 units), sum
+  float* part;         // [B][Hkv][nchunk][2][G][D + 4]: acc[D], max (log2 units), sum, 2 pad
   int B, Hq, Hkv, cap, W, nchunk;
   float scale_log2;
 };
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_partial_kernel(DecParam
     }
     const int slot = loc ? 0 : 1;  // partial slot: 0 local, 1 global
     float* out =
-        p.part + ((((long long)b * p.Hq + hk * G + g) * p.nchunk + c) * 2 + slot) * (D + 2);
+        p.part + ((((long long)b * p.Hkv + hk) * p.nchunk + c) * 2 + slot) * G * (D + 4) + g * (D + 4);
     out[dd] = a;
     if (dd == 0) {
       out[D] = mx;
@@ -408,6 +408,23 @@ __device__ __forceinline__ void st_issue(const void* base, int nbytes, uint16_t*
   for (int i = 0; i < NJ; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)(dst + (wave + kStWaves * i) * 512),
                                              16, voff[i], 0, 0, 0);
+}
+
+// Partial records of one item: the lane stores NB 16-byte blocks at byte
+// offsets off[k] of the buffer [base, base + nbytes), then (max, sum, 0, 0)
+// at off_ml; offsets at or past nbytes are dropped by the buffer range
+// check (lanes with nothing to write).
+template <int NB>
+__device__ __forceinline__ void st_store(float* base, int nbytes, const f32x4 (&v)[NB],
+                                         const int (&off)[NB], int off_ml, float m, float l) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(base, (short)0, nbytes, 0x00020000);
+#pragma unroll
+  for (int k = 0; k < NB; ++k)
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[k]), rsrc, off[k], 0, 0);
+  const u32x4 ml = {__float_as_uint(m), __float_as_uint(l), 0u, 0u};
+  __builtin_amdgcn_raw_buffer_store_b128(ml, rsrc, off_ml, 0, 0);
 }
 
 template <int D>
@@ -646,6 +663,7 @@ __global__ __launch_bounds__(kStWaves * 64, 1) void decode_stream_kernel(StParam
   };
   // the item's partial: this wave's d blocks for query heads < G; wave 0
   // adds the max and the sum
+  constexpr int kDrop = 0x40000000;  // past every record group: dropped
   auto flush = [&] __device__ (const Item& it) __attribute__((always_inline)) {
     const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(l_run),
                                                       __float_as_uint(l_run), false, false);
@@ -653,19 +671,17 @@ __global__ __launch_bounds__(kStWaves * 64, 1) void decode_stream_kernel(StParam
     const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_tot),
                                                       __float_as_uint(l_tot), false, false);
     l_tot = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
-    if (col < G) {
-      float* out = p.part + ((((size_t)it.b * p.Hq + it.hk * G + col) * p.nchunk + it.c) * 2 +
-                             it.br) * (D + 2);
-      // slots are (D + 2) floats: 4-byte aligned only, so scalar stores
+    // record group of (b, kv head, chunk, branch): G records of D + 4
+    // floats (16-byte aligned)
+    float* grp_base = p.part + ((((size_t)it.b * p.Hkv + it.hk) * p.nchunk + it.c) * 2 + it.br) *
+                                   G * (D + 4);
+    const bool mine = col < G;
+    int off[DBW];
 #pragma unroll
-      for (int j = 0; j < DBW; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) out[(wave * DBW + j) * 16 + 4 * grp + e] = acc[j][e];
-      if (wave == 0 && grp == 0) {
-        out[D] = m_run;
-        out[D + 1] = l_tot;
-      }
-    }
+    for (int j = 0; j < DBW; ++j)
+      off[j] = mine ? (col * (D + 4) + (wave * DBW + j) * 16 + 4 * grp) * 4 : kDrop;
+    const int off_ml = mine && wave == 0 && grp == 0 ? (col * (D + 4) + D) * 4 : kDrop;
+    st_store<DBW>(grp_base, G * (D + 4) * 4, acc, off, off_ml, m_run, l_tot);
 #pragma unroll
     for (int j = 0; j < DBW; ++j) acc[j] = (f32x4){};
     m_run = -1.0e30f;
@@ -685,20 +701,23 @@ __global__ __launch_bounds__(kStWaves * 64, 1) void decode_stream_kernel(StParam
     issue(ii, more, dst);
     if (more) more = advance(ii);
   };
+  // each tile's loads are followed by one group of (here dropped) stores,
+  // as in every step, so the first waits count the same way
   put(T0);
   put(T1);
   put(T2);
   bool live = true;
   auto step = [&] __device__ (const uint16_t* tc, uint16_t* tn) __attribute__((always_inline)) {
-    // three tiles are in flight: the oldest (this one) has landed once at
-    // most two tiles' loads remain
+    // Three tiles are in flight and loads complete in issue order, so this
+    // tile's loads have landed once no more than the two newer tiles' loads
+    // are outstanding. Partial stores issued in between only add to the
+    // count: the wait may last longer, never too short.
     __builtin_amdgcn_s_waitcnt(vm_wait<2 * (2 * TL::kInstr + TL::qInstr)>());
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
     put(tn);
     compute(ci, tc);
-    const bool item_end = ci.t == ci.tb;
-    if (item_end) flush(ci);
+    if (ci.t == ci.tb) flush(ci);
     live = advance(ci);
   };
 #pragma unroll 1
@@ -712,12 +731,12 @@ __global__ __launch_bounds__(kStWaves * 64, 1) void decode_stream_kernel(StParam
 }
 
 struct RedParams {
-  const float* part;
+  const float* part;   // as DecParams::part
   const int32_t* lens;
   const uint8_t* selected;
   const float* gate;
   void* o;             // [B][Hq][D]
-  int B, Hq, cap, W, nchunk;
+  int B, Hq, Hkv, cap, W, nchunk;
 };
 
 // One workgroup per (b, query head): for each branch the kRedWaves waves
@@ -735,6 +754,9 @@ __global__ __launch_bounds__(kRedWaves * 64) void decode_reduce_kernel(RedParams
   const long long w = blockIdx.x;  // b * Hq + h
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int b = (int)(w / p.Hq);
+  const int G = p.Hq / p.Hkv;
+  const int hk = (int)(w % p.Hq) / G, g = (int)(w % p.Hq) % G;
+  const long long row0 = (long long)b * p.Hkv + hk;
   const int i = clamp_len(p.lens[b], p.cap) - 1;
   const int lo = max(0, i - p.W + 1);
   const bool sel = p.selected[b] != 0;
@@ -754,7 +776,8 @@ __global__ __launch_bounds__(kRedWaves * 64) void decode_reduce_kernel(RedParams
       for (int u = 0; u < kRedBatch; ++u) {
         const int c = c0 + u * kRedWaves;
         const bool ok = c <= clast;
-        const float* pt = p.part + ((w * p.nchunk + (ok ? c : cfirst)) * 2 + br) * (D + 2);
+        const float* pt =
+            p.part + ((row0 * p.nchunk + (ok ? c : cfirst)) * 2 + br) * G * (D + 4) + g * (D + 4);
         pm[u] = ok ? pt[D] : kNeg;
         pl[u] = ok ? pt[D + 1] : 0.0f;
 #pragma unroll
@@ -922,6 +945,7 @@ hipError_t decode_t(const DecodeDims& d, const DecodeArgs& a, hipStream_t s) {
   r.o = a.o;
   r.B = d.B;
   r.Hq = d.Hq;
+  r.Hkv = d.Hkv;
   r.cap = d.cap;
   r.W = d.window;
   r.nchunk = p.nchunk;
@@ -948,7 +972,7 @@ bool decode_group_supported(int G) { return G == 1 || G == 2 || G == 4 || G == 7
 
 size_t decode_partial_bytes(const DecodeDims& d) {
   const size_t nchunk = (d.cap + kChunk - 1) / kChunk;
-  return ((size_t)d.B * d.Hq * nchunk * 2 * (d.d + 2) * sizeof(float) + 255) / 256 * 256;
+  return ((size_t)d.B * d.Hq * nchunk * 2 * (d.d + 4) * sizeof(float) + 255) / 256 * 256;
 }
 
 hipError_t launch_decode_ctrl(const DecodeDims& d, const float* gate, float* tau,
