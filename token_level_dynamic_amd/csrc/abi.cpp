@@ -685,10 +685,11 @@ logo_status logo_select_threshold(const logo_problem* p, const float* gate, cons
   return LOGO_OK;
 }
 
-// Packed examples: the per-example table, per-token example starts and the
-// float32 local outputs of the selected rows.
+// Packed examples: the per-example table, per-token example starts, the
+// float32 local outputs of the selected rows and the global branch's
+// workgroup order.
 struct VarlenWs {
-  size_t seg, seg_start, scratch, total;
+  size_t seg, seg_start, scratch, sched, total;
 };
 VarlenWs varlen_ws(const logo::Dims& d, int64_t E, int64_t K) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -696,7 +697,10 @@ VarlenWs varlen_ws(const logo::Dims& d, int64_t E, int64_t K) {
   w.seg = 0;
   w.seg_start = up((size_t)E * 16);
   w.scratch = w.seg_start + up((size_t)d.n * 4);
-  w.total = w.scratch + up((size_t)d.Hq * (size_t)K * d.d * sizeof(float));
+  w.sched = w.scratch + up((size_t)d.Hq * (size_t)K * d.d * sizeof(float));
+  logo::Dims dk = d;
+  dk.k = (int)K;
+  w.total = w.sched + up(logo::attn_bf16_sched_ints(dk) * sizeof(int32_t));
   return w;
 }
 
@@ -779,6 +783,7 @@ logo_status logo_forward_varlen(const logo_problem* p, const int32_t* cu_seqlens
   a.scratch = scratch;
   a.out_io = o;
   a.seg_start = seg_start;
+  a.sched = d.dtype == LOGO_BF16 ? reinterpret_cast<int32_t*>(w + ws.sched) : nullptr;
   {
     StageTimer tm(1, s);
     e = run_attn(d, logo::Epi::LocalFused, a, s);

@@ -95,6 +95,9 @@ struct Params {
   const float* router_w;  // routed local: [Hq][D]
   float* router_part;     // routed local: [B][Hq][n]
   const int32_t* seg_start;  // packed examples: [n] first token of the example, or NULL
+  const int32_t* sched_perm; // packed global: workgroup slots by work, heaviest first
+  int32_t* sched_count;      // packed global: per (b, kv head) next rank; zeroed by the
+                             // schedule kernel
 };
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
@@ -152,7 +155,17 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   if (L >= p.total_wg) return;
   const int unit_bh = L / p.wg_per_unit;       // b * Hkv + kv head
   int w = L % p.wg_per_unit;
-  if (GLOBAL) w = p.wg_per_unit - 1 - w;        // longest prefix first
+  if (GLOBAL && SEG && p.sched_perm) {
+    // packed examples: the prefix lengths do not follow the row order, so
+    // the workgroups of a unit (on whichever XCDs hold it) take slots from
+    // a shared queue ordered heaviest first
+    __shared__ int slot;
+    if (threadIdx.x == 0) slot = p.sched_perm[atomicAdd(p.sched_count + unit_bh, 1)];
+    __syncthreads();
+    w = slot;
+  } else if (GLOBAL) {
+    w = p.wg_per_unit - 1 - w;                  // longest prefix first
+  }
   const int b = unit_bh / p.Hkv;
   const int hk = unit_bh % p.Hkv;
   const int G = p.Hq / p.Hkv;
@@ -510,6 +523,52 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   }
 }
 
+// Work order of the global branch's workgroups over packed examples: the
+// keys a workgroup streams (from its first row's example start to its last
+// row) estimate its work; slots are bucketed by that estimate (1024 buckets,
+// heaviest first; order within a bucket is arbitrary, which changes only
+// the timing, never a result) into perm, and the per-unit counters the
+// workgroups take ranks from are zeroed. One 1024-thread workgroup.
+__global__ __launch_bounds__(1024) void global_sched_kernel(const int32_t* __restrict__ idx,
+                                                            const int32_t* __restrict__ seg_start,
+                                                            int n, int K, int G, int units,
+                                                            int wpu, int n_count,
+                                                            int32_t* __restrict__ perm,
+                                                            int32_t* __restrict__ count) {
+  __shared__ int bins[1024];
+  __shared__ int wmax[16];
+  const int t = threadIdx.x;
+  for (int i = t; i < n_count; i += 1024) count[i] = 0;
+  auto work = [&](int w) {
+    const int u0 = w * kWaves, u1 = min(u0 + kWaves, units) - 1;
+    const int r0 = (u0 / G) * kRows, r1 = min((u1 / G) * kRows + kRows, K) - 1;
+    const int p0 = min(max(idx[r0], 0), n - 1), p1 = min(max(idx[r1], 0), n - 1);
+    return max(p1 - seg_start[p0] + 1, 1);
+  };
+  int mx = 1;
+  for (int w = t; w < wpu; w += 1024) mx = max(mx, work(w));
+  for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off, 64));
+  if ((t & 63) == 0) wmax[t >> 6] = mx;
+  bins[t] = 0;
+  __syncthreads();
+  mx = 1;
+  for (int i = 0; i < 16; ++i) mx = max(mx, wmax[i]);
+  // bucket 0 = heaviest
+  auto bucket = [&](int wk) { return 1023 - (int)((long long)wk * 1023 / mx); };
+  for (int w = t; w < wpu; w += 1024) atomicAdd(&bins[bucket(work(w))], 1);
+  __syncthreads();
+  if (t == 0) {  // exclusive scan of 1024 counts (once per launch)
+    int run = 0;
+    for (int i = 0; i < 1024; ++i) {
+      const int c = bins[i];
+      bins[i] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  for (int w = t; w < wpu; w += 1024) perm[atomicAdd(&bins[bucket(work(w))], 1)] = w;
+}
+
 template <int D, bool GLOBAL, int EPI, bool SEG = false>
 hipError_t launch_one(const Params& prm, hipStream_t s) {
   static_assert(GLOBAL == (EPI == 2 || EPI == 3 || EPI == 5), "epilogue of the other branch");
@@ -538,6 +597,12 @@ hipError_t dispatch_epi(Epi epi, const Params& prm, hipStream_t s) {
 }
 
 }  // namespace
+
+size_t attn_bf16_sched_ints(const Dims& d) {
+  const size_t npb = ((size_t)d.k + kRows - 1) / kRows;
+  const size_t units = npb * (size_t)(d.Hq / d.Hkv);
+  return (units + kWaves - 1) / kWaves + (size_t)d.B * d.Hkv;
+}
 
 hipError_t launch_attn_bf16(const Dims& d, Epi epi, const AttnArgs& a, hipStream_t s) {
   const bool global =
@@ -576,6 +641,18 @@ hipError_t launch_attn_bf16(const Dims& d, Epi epi, const AttnArgs& a, hipStream
   prm.router_w = a.router_w;
   prm.router_part = a.router_part;
   prm.seg_start = a.seg_start;
+  prm.sched_perm = nullptr;
+  prm.sched_count = nullptr;
+  if (global && a.seg_start && a.sched) {
+    int32_t* perm = a.sched;
+    int32_t* count = a.sched + prm.wg_per_unit;
+    hipLaunchKernelGGL(global_sched_kernel, dim3(1), dim3(1024), 0, s, a.idx, a.seg_start, d.n,
+                       d.k, G, prm.units, prm.wg_per_unit, d.B * d.Hkv, perm, count);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    prm.sched_perm = perm;
+    prm.sched_count = count;
+  }
   if (d.d == 64) return dispatch_epi<64>(epi, prm, s);
   if (d.d == 128) return dispatch_epi<128>(epi, prm, s);
   return hipErrorInvalidValue;
