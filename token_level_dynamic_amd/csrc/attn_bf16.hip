@@ -557,13 +557,18 @@ __global__ __launch_bounds__(1024) void global_sched_kernel(const int32_t* __res
   auto bucket = [&](int wk) { return 1023 - (int)((long long)wk * 1023 / mx); };
   for (int w = t; w < wpu; w += 1024) atomicAdd(&bins[bucket(work(w))], 1);
   __syncthreads();
-  if (t == 0) {  // exclusive scan of 1024 counts (once per launch)
-    int run = 0;
-    for (int i = 0; i < 1024; ++i) {
-      const int c = bins[i];
-      bins[i] = run;
-      run += c;
+  {  // exclusive scan of the 1024 counts: within each wave, then across
+    const int c = bins[t];
+    int incl = c;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if ((t & 63) >= off) incl += y;
     }
+    if ((t & 63) == 63) wmax[t >> 6] = incl;  // wave totals (the maxima are consumed)
+    __syncthreads();
+    int base = 0;
+    for (int i = 0; i < (t >> 6); ++i) base += wmax[i];
+    bins[t] = base + incl - c;
   }
   __syncthreads();
   for (int w = t; w < wpu; w += 1024) perm[atomicAdd(&bins[bucket(work(w))], 1)] = w;
