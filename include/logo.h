@@ -266,7 +266,7 @@ typedef struct {
 } logo_decode_problem;
 
 /* Bytes of workspace logo_decode_step needs (per-chunk partial softmax
- * states: B*Hq*ceil(cap/256)*2*(d+4)*4). */
+ * states: B*Hq*ceil(cap/1024)*2*(d+4)*4). */
 logo_status logo_decode_workspace_size(const logo_decode_problem* p, size_t* bytes);
 
 /* The newest token of each sequence attends over its cache:

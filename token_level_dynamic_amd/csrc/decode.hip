@@ -24,7 +24,11 @@
 namespace logo {
 namespace {
 
-constexpr int kChunk = 256;       // keys per workgroup
+// keys per chunk partial: a work item of the stream (and a workgroup of the
+// chunked kernel). Larger chunks mean fewer partial stores between the tile
+// loads (each delays the next wait) and fewer partials to merge, smaller
+// ones a finer balance over the compute units; 1024 measured best.
+constexpr int kChunk = 1024;
 constexpr int kSub = 64;          // keys per wave step (one per lane)
 constexpr int kDecWaves = 4;
 constexpr float kLog2e = 1.4426950408889634f;
