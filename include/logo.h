@@ -217,7 +217,8 @@ logo_status logo_backward(const logo_problem* p, const void* q, const void* k,
  *              the combine use exactly these values)
  *   o, mask, idx, rank as logo_forward.
  * Workspace: logo_routed_workspace_size bytes (the float32 local output of
- * every row, B*Hq*n*d*4, and B*Hq*n*4 of per-head partial logits).
+ * every row, B*Hq*n*d*4, B*Hq*n*4 of per-head partial logits and B*Hkv*4
+ * of work queues, each rounded up to 256).
  * Errors: as logo_forward; LOGO_ERR_INVALID_ARG for a non-finite bias. */
 logo_status logo_routed_workspace_size(const logo_problem* p, size_t* bytes);
 logo_status logo_forward_routed(const logo_problem* p, const void* q, const void* k,

@@ -138,9 +138,14 @@ logo_status need_ptr(const void* ptr, const char* name) {
 }
 
 
+// logo_forward's workspace: the float32 local outputs of the selected rows.
 size_t scratch_bytes(const logo::Dims& d) {
   const size_t b = (size_t)d.B * d.Hq * d.k * d.d * sizeof(float);
   return (b + 255) / 256 * 256;
+}
+// The routed global branch's workgroup queues (one int per (b, kv head)).
+size_t queue_bytes(const logo::Dims& d) {  // none when nothing is selected
+  return d.k == 0 ? 0 : (logo::attn_bf16_sched_ints(d, false) * sizeof(int32_t) + 255) / 256 * 256;
 }
 
 // ---- kernel timing --------------------------------------------------------
@@ -496,8 +501,11 @@ logo_status logo_backward(const logo_problem* p, const void* q, const void* k, c
 size_t routed_local_bytes(const logo::Dims& d) {
   return ((size_t)d.B * d.Hq * d.n * d.d * sizeof(float) + 255) / 256 * 256;
 }
+size_t routed_part_bytes(const logo::Dims& d) {
+  return ((size_t)d.B * d.Hq * d.n * sizeof(float) + 255) / 256 * 256;
+}
 size_t routed_bytes(const logo::Dims& d) {
-  return routed_local_bytes(d) + ((size_t)d.B * d.Hq * d.n * sizeof(float) + 255) / 256 * 256;
+  return routed_local_bytes(d) + routed_part_bytes(d) + queue_bytes(d);
 }
 
 logo_status logo_routed_workspace_size(const logo_problem* p, size_t* bytes) {
@@ -547,6 +555,9 @@ logo_status logo_forward_routed(const logo_problem* p, const void* q, const void
   a.out_io = o;
   a.router_w = router_w;
   a.router_part = part;
+  if (d.dtype == LOGO_BF16)
+    a.sched = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + routed_local_bytes(d) +
+                                         routed_part_bytes(d));
   hipError_t e;
   {
     StageTimer tm(1, s);
@@ -700,7 +711,7 @@ VarlenWs varlen_ws(const logo::Dims& d, int64_t E, int64_t K) {
   w.sched = w.scratch + up((size_t)d.Hq * (size_t)K * d.d * sizeof(float));
   logo::Dims dk = d;
   dk.k = (int)K;
-  w.total = w.sched + up(logo::attn_bf16_sched_ints(dk) * sizeof(int32_t));
+  w.total = w.sched + up(logo::attn_bf16_sched_ints(dk, true) * sizeof(int32_t));
   return w;
 }
 

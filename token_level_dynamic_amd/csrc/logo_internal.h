@@ -52,8 +52,9 @@ struct AttnArgs {
   float* router_part;    // routed local: [B][Hq][n] f32
   const int32_t* seg_start;  // packed examples: first token of each token's
                              // example (keys before it are masked); or NULL
-  int32_t* sched;        // packed examples, bf16 global branch: workspace of
-                         // attn_bf16_sched_ints() ints for the tile order, or NULL
+  int32_t* sched;        // bf16 global branch: workspace of attn_bf16_sched_ints()
+                         // ints for the workgroup queues (and, for packed examples,
+                         // the work order), or NULL for the static order
 };
 
 // Everything the backward kernels read and write. q, k, v, o and dout are
@@ -109,9 +110,9 @@ hipError_t launch_select_segments(int n_segments, const int4* seg, const float* 
 hipError_t launch_varlen_prep(const int32_t* cu, int E, int T, double rho, int4* seg,
                               int32_t* seg_start, hipStream_t s);
 
-// Ints of workspace the bf16 global branch of packed examples uses to order
-// its workgroups by work.
-size_t attn_bf16_sched_ints(const Dims& d);
+// Ints of workspace the bf16 global branch uses for its workgroup queues
+// (one counter per (b, kv head)) and, for packed examples, the work order.
+size_t attn_bf16_sched_ints(const Dims& d, bool packed);
 hipError_t launch_attn_bf16(const Dims& d, Epi epi, const AttnArgs& a,
                             hipStream_t s);
 
