@@ -130,6 +130,88 @@ def copy_calibration(torch) -> int:
     return 0
 
 
+def _counter_means(csv_dir: str, counter: str, n_first: int = 3) -> dict:
+    """Mean value of `counter` over the first n_first dispatches of each
+    kernel in a rocprofv3 --pmc csv directory (values summed per dispatch)."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(csv_dir, "*counter_collection.csv"))
+    if len(files) != 1:
+        raise SystemExit(f"expected one counter_collection.csv in {csv_dir}")
+    per = {}
+    order = {}
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], int(r["Dispatch_Id"]))
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+            order.setdefault(r["Kernel_Name"], set()).add(int(r["Dispatch_Id"]))
+    out = {}
+    for name, ids in order.items():
+        first = sorted(ids)[:n_first]
+        out[name] = sum(per[(name, i)] for i in first) / len(first)
+    return out
+
+
+def _pick(means: dict, fragment: str) -> float:
+    hits = [v for k, v in means.items() if fragment in k]
+    if len(hits) != 1:
+        raise SystemExit(f"kernel {fragment!r}: {len(hits)} matches")
+    return hits[0]
+
+
+def record_traffic(args) -> int:
+    """Write profiles/traffic.json from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+    (KiB per dispatch): the copy calibration fixes the scale of each counter
+    (bytes the 1 GiB copy moves over what the counter reports), and each
+    kernel's bytes per launch are its mean counter value (warm-up and the two
+    timed dispatches) times 1024 times that scale. The current kernel-source
+    hashes are stored with them, so bench.py reports the figures only while
+    the kernels are unchanged."""
+    fs = COPY_BYTES / (1024.0 * _pick(_counter_means(args.copy_fetch, "FETCH_SIZE"), "add"))
+    ws = COPY_BYTES / (1024.0 * _pick(_counter_means(args.copy_write, "WRITE_SIZE"), "add"))
+    fm = _counter_means(args.fwd_fetch, "FETCH_SIZE")
+    wm = _counter_means(args.fwd_write, "WRITE_SIZE")
+    g = "attn_bf16_kernel<128, true, 3, false>"
+    lo = "attn_bf16_kernel<128, false, 1, false>"
+    gr, gw = _pick(fm, g) * 1024 * fs, _pick(wm, g) * 1024 * ws
+    data = {"gqa32k": {
+        "source_hash": kernel_source_hash(),
+        "global_bytes_per_launch": round(gr + gw),
+        "global_read_bytes": round(gr),
+        "global_write_bytes": round(gw),
+        "local_bytes_per_launch": round((_pick(fm, lo) * fs + _pick(wm, lo) * ws) * 1024),
+        "fetch_scale": round(fs, 5),
+        "write_scale": round(ws, 5),
+        "note": "FETCH_SIZE/WRITE_SIZE KiB per dispatch (rocprofv3 --pmc, one counter per run; "
+                "mean of the warm-up and the two timed dispatches) times 1024 times the "
+                "copy-kernel scale; written by bench.py --record-traffic, see "
+                "hbm_traffic_gqa32k.md"}}
+    if args.train_fetch and args.train_write:
+        tf = _counter_means(args.train_fetch, "FETCH_SIZE")
+        tw = _counter_means(args.train_write, "WRITE_SIZE")
+        dk = "bwd_dkdv_kernel<128>"
+        dq = ("bwd_dq_kernel<128, true>", "bwd_dq_kernel<128, false>")
+        dr, dw = _pick(tf, dk) * 1024 * fs, _pick(tw, dk) * 1024 * ws
+        data["gqa32k_train"] = {
+            "source_hash": kernel_source_hash(TRAIN_SOURCES),
+            "bwd_dkdv_bytes_per_launch": round(dr + dw),
+            "bwd_dkdv_read_bytes": round(dr),
+            "bwd_dkdv_write_bytes": round(dw),
+            "bwd_dq_bytes_per_launch": round(sum((_pick(tf, x) * fs + _pick(tw, x) * ws) * 1024
+                                                 for x in dq)),
+            "fetch_scale": round(fs, 5),
+            "write_scale": round(ws, 5),
+            "note": "same counters on bench.py --mode train; bwd_dq is both dQ launches"}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1)
+        f.write("\n")
+    print(json.dumps(data))
+    return 0
+
+
 def gemm_ceiling(torch) -> int:
     """Sustained bf16 matrix-core rate of a plain library GEMM on this part,
     on random N(0,1) operands and on zero operands. The published dense peak
@@ -552,6 +634,13 @@ def main() -> int:
                          "logo_forward_routed per step (gate computed from the local branch); "
                          "decode: one logo_decode_step of the 128K decode workload per step; "
                          "varlen: one logo_forward_varlen over a packed 64K-token batch")
+    ap.add_argument("--record-traffic", action="store_true",
+                    help="write profiles/traffic.json from rocprofv3 counter csv directories "
+                         "(--copy-fetch, --copy-write, --fwd-fetch, --fwd-write, optionally "
+                         "--train-fetch, --train-write) and exit; needs no GPU")
+    for opt in ("copy-fetch", "copy-write", "fwd-fetch", "fwd-write", "train-fetch",
+                "train-write"):
+        ap.add_argument("--" + opt, default=None)
     ap.add_argument("--gemm-ceiling", action="store_true",
                     help="time a plain bf16 GEMM on random and on zero operands and exit")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -563,6 +652,9 @@ def main() -> int:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
         return 2
+
+    if args.record_traffic:
+        return record_traffic(args)
 
     import torch
 
