@@ -204,7 +204,7 @@ def record_traffic(args) -> int:
             "fetch_scale": round(fs, 5),
             "write_scale": round(ws, 5),
             "note": "same counters on bench.py --mode train; bwd_dq is both dQ launches"}
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = args.traffic_out or os.path.join(ROOT, "profiles", "traffic.json")
     with open(path, "w") as f:
         json.dump(data, f, indent=1)
         f.write("\n")
@@ -639,7 +639,7 @@ def main() -> int:
                          "(--copy-fetch, --copy-write, --fwd-fetch, --fwd-write, optionally "
                          "--train-fetch, --train-write) and exit; needs no GPU")
     for opt in ("copy-fetch", "copy-write", "fwd-fetch", "fwd-write", "train-fetch",
-                "train-write"):
+                "train-write", "traffic-out"):
         ap.add_argument("--" + opt, default=None)
     ap.add_argument("--gemm-ceiling", action="store_true",
                     help="time a plain bf16 GEMM on random and on zero operands and exit")

@@ -1,0 +1,62 @@
+"""bench.py's host-side contract: the one-GPU guard, and the reduction of
+rocprofv3 counter runs into traffic.json. No GPU."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_exits_with_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def _counters(path, counter, kernels):
+    """A rocprofv3-style counter csv: kernels = {name: [values per dispatch]},
+    each value split over two rows (two shader engines)."""
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "p_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        did = 0
+        for name, vals in kernels.items():
+            for v in vals:
+                did += 1
+                for part in (0.25 * v, 0.75 * v):
+                    w.writerow({"Dispatch_Id": did, "Kernel_Name": name, "Counter_Name": counter,
+                                "Counter_Value": part})
+
+
+def test_record_traffic(tmp_path):
+    g = "void logo::attn_bf16_kernel<128, true, 3, false>(Params)"
+    lo = "void logo::attn_bf16_kernel<128, false, 1, false>(Params)"
+    add = "void at::native::vectorized_elementwise_kernel<4, CUDAFunctorOnSelf_add<float>>"
+    gib_kib = (1 << 30) / 1024
+    # FETCH_SIZE reads half of what a streaming read moves, WRITE_SIZE all of it
+    _counters(tmp_path / "cf", "FETCH_SIZE", {add: [gib_kib / 2] * 3})
+    _counters(tmp_path / "cw", "WRITE_SIZE", {add: [gib_kib] * 3})
+    # the mean of the first three dispatches is taken; later ones are ignored
+    _counters(tmp_path / "ff", "FETCH_SIZE", {g: [1000, 1002, 1004, 9999], lo: [10, 10, 10]})
+    _counters(tmp_path / "fw", "WRITE_SIZE", {g: [50, 50, 50, 9999], lo: [7, 7, 7]})
+    out = tmp_path / "traffic.json"
+    args = bench.argparse.Namespace(copy_fetch=str(tmp_path / "cf"),
+                                    copy_write=str(tmp_path / "cw"),
+                                    fwd_fetch=str(tmp_path / "ff"), fwd_write=str(tmp_path / "fw"),
+                                    train_fetch=None, train_write=None, traffic_out=str(out))
+    assert bench.record_traffic(args) == 0
+    d = json.loads(out.read_text())["gqa32k"]
+    assert d["fetch_scale"] == pytest.approx(2.0) and d["write_scale"] == pytest.approx(1.0)
+    assert d["global_read_bytes"] == round(1002 * 1024 * 2)
+    assert d["global_write_bytes"] == 50 * 1024
+    assert d["global_bytes_per_launch"] == d["global_read_bytes"] + d["global_write_bytes"]
+    assert d["local_bytes_per_launch"] == (10 * 2 + 7) * 1024
+    assert d["source_hash"] == bench.kernel_source_hash()
