@@ -255,7 +255,8 @@ logo_status logo_select_threshold(const logo_problem* p, const float* gate,
 /* One decode step per sequence. */
 typedef struct {
   int64_t B;       /* sequences                                              */
-  int64_t Hq;      /* query heads; Hq / Hkv in {1, 2, 4, 7, 8}               */
+  int64_t Hq;      /* query heads; G = Hq / Hkv in 1..16 for bf16 caches of
+                      at most 1023 sequences, else G in {1, 2, 4, 7, 8}       */
   int64_t Hkv;     /* key/value heads                                        */
   int64_t cap;     /* cache capacity (positions per sequence and kv head)    */
   int64_t d;       /* head dimension: 64 or 128                              */
@@ -282,7 +283,11 @@ logo_status logo_decode_workspace_size(const logo_decode_problem* p, size_t* byt
  *            sigmoid(gate) o_global over the whole cache when selected
  *   selected [B] uint8 out.
  * Reads each needed cached key and value once (the kv head's query heads
- * share it); unselected sequences read only their window. */
+ * share it); unselected sequences read only their window. Errors:
+ * LOGO_ERR_INVALID_ARG (bad sizes, ratio, step, scale or dtype, NULL or
+ * misaligned pointers), LOGO_ERR_UNSUPPORTED (head dimension, group size,
+ * sizes past the 32-bit work counts), LOGO_ERR_WORKSPACE, LOGO_ERR_HIP;
+ * nothing is enqueued on an argument error. */
 logo_status logo_decode_step(const logo_decode_problem* p, const void* q,
                              const void* k_cache, const void* v_cache,
                              const int32_t* lens, const float* gate, float* tau,

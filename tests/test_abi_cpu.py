@@ -266,3 +266,67 @@ def test_forward_train_validation(L):
     p0 = _prob(n=0)
     assert L.logo_forward_train(ctypes.byref(p0), *([None] * 12), None) == 0
     assert L.logo_backward(ctypes.byref(p0), *([None] * 16), None, 0, None) == 0
+
+
+# ---- decode step ---------------------------------------------------------------
+
+def _dprob(**kw):
+    base = dict(B=3, Hq=8, Hkv=2, cap=5000, d=128, window=64, rho=0.25, eta=0.1, scale=0.0,
+                dtype="bf16")
+    base.update(kw)
+    return T.make_decode_problem(**base)
+
+
+def _dsize(L, p):
+    size = ctypes.c_size_t(0)
+    st = L.logo_decode_workspace_size(ctypes.byref(p), ctypes.byref(size))
+    return st, size.value
+
+
+def test_decode_group_sizes(L):
+    # bf16 caches of at most 1023 sequences: any group up to 16
+    for hq, hkv in ((3, 1), (12, 4), (16, 1), (10, 2)):
+        assert _dsize(L, _dprob(Hq=hq, Hkv=hkv))[0] == 0
+
+
+def test_decode_workspace_formula(L):
+    # one (d + 4)-float record per (b, query head, 1024-key chunk, branch)
+    st, size = _dsize(L, _dprob())
+    assert st == 0
+    want = 3 * 8 * math.ceil(5000 / 1024) * 2 * (128 + 4) * 4
+    assert size == (want + 255) // 256 * 256
+    st, size = _dsize(L, _dprob(B=0))
+    assert st == 0 and size == 0
+
+
+@pytest.mark.parametrize("bad", [dict(Hq=6, Hkv=4), dict(Hq=0), dict(cap=0), dict(window=0),
+                                 dict(rho=1.5), dict(rho=math.nan), dict(eta=-1.0),
+                                 dict(eta=math.inf), dict(scale=math.nan), dict(B=-1)])
+def test_decode_rejects_bad_problems(L, bad):
+    st, _ = _dsize(L, _dprob(**bad))
+    assert st == _lib.LOGO_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", [dict(d=96), dict(Hq=17, Hkv=1), dict(Hq=12, Hkv=4, dtype="f32"),
+                                 dict(Hq=12, Hkv=4, B=1024), dict(cap=1 << 30),
+                                 # work items beyond 32-bit counts
+                                 dict(B=(1 << 19) - 1, Hq=64, Hkv=64, cap=1 << 20)])
+def test_decode_unsupported_sizes(L, bad):
+    st, _ = _dsize(L, _dprob(**bad))
+    assert st == _lib.LOGO_ERR_UNSUPPORTED
+    assert L.logo_last_error()
+
+
+def test_decode_step_rejects_null_pointers_before_launching(L):
+    p = _dprob()
+    args = [FAKE] * 8  # q, k_cache, v_cache, lens, gate, tau, o, selected
+    for i, name in enumerate(["q", "k_cache", "v_cache", "lens", "gate", "tau", "o", "selected"]):
+        a = list(args)
+        a[i] = None
+        st = L.logo_decode_step(ctypes.byref(p), *a, FAKE, 1 << 30, None)
+        assert st == _lib.LOGO_ERR_INVALID_ARG, name
+        assert name.encode() in L.logo_last_error()
+    # too small a workspace
+    _, need = _dsize(L, p)
+    st = L.logo_decode_step(ctypes.byref(p), *args, FAKE, need - 1, None)
+    assert st == _lib.LOGO_ERR_WORKSPACE

@@ -54,6 +54,8 @@ CASES = {
     "bf16_g4": dict(B=5, Hq=8, Hkv=2, cap=4500, d=128, window=2049, rho=0.3, dtype="bf16"),
     "bf16_g7": dict(B=3, Hq=14, Hkv=2, cap=3000, d=128, window=100, rho=0.2, dtype="bf16"),
     "bf16_g8_window1": dict(B=4, Hq=8, Hkv=1, cap=700, d=64, window=1, rho=0.2, dtype="bf16"),
+    "bf16_g3_d64": dict(B=3, Hq=6, Hkv=2, cap=3100, d=64, window=1500, rho=0.3, dtype="bf16"),
+    "bf16_g16": dict(B=2, Hq=16, Hkv=1, cap=2500, d=128, window=700, rho=0.5, dtype="bf16"),
     "f32_g2": dict(B=4, Hq=4, Hkv=2, cap=2500, d=128, window=64, rho=0.25, dtype="f32"),
     "f32_g1_d64": dict(B=3, Hq=2, Hkv=2, cap=600, d=64, window=600, rho=0.1, dtype="f32"),
 }

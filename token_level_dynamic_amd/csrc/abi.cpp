@@ -600,11 +600,11 @@ logo_status check_decode(const logo_decode_problem* p, logo::DecodeDims* out) {
   if (p->d != 64 && p->d != 128)
     return fail(LOGO_ERR_UNSUPPORTED, "head dimension %lld not supported (64 or 128)",
                 (long long)p->d);
-  if (!logo::decode_group_supported((int)(p->Hq / p->Hkv)))
-    return fail(LOGO_ERR_UNSUPPORTED, "query heads per kv head %lld not built (1, 2, 4, 7, 8)",
-                (long long)(p->Hq / p->Hkv));
   if (p->cap >= (int64_t(1) << 30) || p->B >= (int64_t(1) << 20) || p->Hq >= (int64_t(1) << 16))
     return fail(LOGO_ERR_UNSUPPORTED, "sizes beyond the supported range");
+  // work items (b, branch, kv head, chunk) are counted in 32-bit integers
+  if (2 * p->B * p->Hkv * logo::decode_chunks(p->cap) >= (int64_t(1) << 30))
+    return fail(LOGO_ERR_UNSUPPORTED, "B * Hkv * cache chunks beyond the supported range");
   out->B = (int)p->B;
   out->Hq = (int)p->Hq;
   out->Hkv = (int)p->Hkv;
@@ -615,6 +615,11 @@ logo_status check_decode(const logo_decode_problem* p, logo::DecodeDims* out) {
   out->eta = p->eta;
   out->scale = p->scale == 0.0f ? (float)(1.0 / std::sqrt((double)p->d)) : p->scale;
   out->dtype = p->dtype;
+  if (!logo::decode_group_supported(*out))
+    return fail(LOGO_ERR_UNSUPPORTED,
+                "query heads per kv head %lld not supported (up to 16 for bf16 caches of at most "
+                "1023 sequences; otherwise 1, 2, 4, 7 or 8)",
+                (long long)(p->Hq / p->Hkv));
   return LOGO_OK;
 }
 

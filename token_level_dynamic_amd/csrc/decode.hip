@@ -901,8 +901,13 @@ int compute_units() {
   return n;
 }
 
+hipError_t launch_reduce_d(int D, bool bf16, const DecodeDims& d, const DecodeArgs& a, int nchunk,
+                           hipStream_t s);
+
+// The chunked kernel: float32 caches, or more sequences than the stream
+// kernel's item table holds; G is a template parameter.
 template <int D, int G, bool BF16>
-hipError_t decode_t(const DecodeDims& d, const DecodeArgs& a, hipStream_t s) {
+hipError_t decode_chunked(const DecodeDims& d, const DecodeArgs& a, hipStream_t s) {
   DecParams p;
   p.q = a.q;
   p.kc = a.k_cache;
@@ -917,30 +922,40 @@ hipError_t decode_t(const DecodeDims& d, const DecodeArgs& a, hipStream_t s) {
   p.W = d.window;
   p.nchunk = (d.cap + kChunk - 1) / kChunk;
   p.scale_log2 = d.scale * kLog2e;
-  if (BF16 && d.B <= kStMaxB) {
-    StParams sp;
-    sp.q = static_cast<const uint16_t*>(a.q);
-    sp.kc = static_cast<const uint16_t*>(a.k_cache);
-    sp.vc = static_cast<const uint16_t*>(a.v_cache);
-    sp.lens = a.lens;
-    sp.selected = a.selected;
-    sp.part = a.part;
-    sp.B = d.B;
-    sp.Hq = d.Hq;
-    sp.Hkv = d.Hkv;
-    sp.cap = d.cap;
-    sp.W = d.window;
-    sp.nchunk = p.nchunk;
-    sp.nwg = compute_units();
-    sp.scale_log2 = p.scale_log2;
-    hipLaunchKernelGGL((decode_stream_kernel<D>), dim3((unsigned)sp.nwg),
-                       dim3(kStWaves * 64), 0, s, sp);
-  } else {
-    const dim3 grid((unsigned)(2LL * d.B * d.Hkv * p.nchunk));
-    hipLaunchKernelGGL((decode_partial_kernel<D, G, BF16>), grid, dim3(kDecWaves * 64), 0, s, p);
-  }
-  hipError_t e = hipGetLastError();
+  const dim3 grid((unsigned)(2LL * d.B * d.Hkv * p.nchunk));
+  hipLaunchKernelGGL((decode_partial_kernel<D, G, BF16>), grid, dim3(kDecWaves * 64), 0, s, p);
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_reduce_d(D, BF16, d, a, p.nchunk, s);
+}
+
+// The stream kernel: bf16 caches, B <= kStMaxB, any G <= kStCols.
+template <int D>
+hipError_t decode_stream(const DecodeDims& d, const DecodeArgs& a, hipStream_t s) {
+  StParams sp;
+  sp.q = static_cast<const uint16_t*>(a.q);
+  sp.kc = static_cast<const uint16_t*>(a.k_cache);
+  sp.vc = static_cast<const uint16_t*>(a.v_cache);
+  sp.lens = a.lens;
+  sp.selected = a.selected;
+  sp.part = a.part;
+  sp.B = d.B;
+  sp.Hq = d.Hq;
+  sp.Hkv = d.Hkv;
+  sp.cap = d.cap;
+  sp.W = d.window;
+  sp.nchunk = (d.cap + kChunk - 1) / kChunk;
+  sp.nwg = compute_units();
+  sp.scale_log2 = d.scale * kLog2e;
+  hipLaunchKernelGGL((decode_stream_kernel<D>), dim3((unsigned)sp.nwg), dim3(kStWaves * 64), 0,
+                     s, sp);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_reduce_d(D, true, d, a, sp.nchunk, s);
+}
+
+hipError_t launch_reduce_d(int D, bool bf16, const DecodeDims& d, const DecodeArgs& a, int nchunk,
+                           hipStream_t s) {
   RedParams r;
   r.part = a.part;
   r.lens = a.lens;
@@ -952,27 +967,41 @@ hipError_t decode_t(const DecodeDims& d, const DecodeArgs& a, hipStream_t s) {
   r.Hkv = d.Hkv;
   r.cap = d.cap;
   r.W = d.window;
-  r.nchunk = p.nchunk;
-  hipLaunchKernelGGL((decode_reduce_kernel<D, BF16>), dim3((unsigned)((long long)d.B * d.Hq)),
-                     dim3(kRedWaves * 64), 0, s, r);
+  r.nchunk = nchunk;
+  const dim3 grid((unsigned)((long long)d.B * d.Hq)), block(kRedWaves * 64);
+  if (D == 64 && bf16) hipLaunchKernelGGL((decode_reduce_kernel<64, true>), grid, block, 0, s, r);
+  else if (D == 64) hipLaunchKernelGGL((decode_reduce_kernel<64, false>), grid, block, 0, s, r);
+  else if (bf16) hipLaunchKernelGGL((decode_reduce_kernel<128, true>), grid, block, 0, s, r);
+  else hipLaunchKernelGGL((decode_reduce_kernel<128, false>), grid, block, 0, s, r);
   return hipGetLastError();
+}
+
+bool stream_path(const DecodeDims& d) {
+  return d.dtype == 1 && d.B <= kStMaxB && d.Hq / d.Hkv <= kStCols;
 }
 
 template <int D, bool BF16>
 hipError_t decode_g(const DecodeDims& d, const DecodeArgs& a, hipStream_t s) {
+  if (BF16 && stream_path(d)) return decode_stream<D>(d, a, s);
   switch (d.Hq / d.Hkv) {
-    case 1: return decode_t<D, 1, BF16>(d, a, s);
-    case 2: return decode_t<D, 2, BF16>(d, a, s);
-    case 4: return decode_t<D, 4, BF16>(d, a, s);
-    case 7: return decode_t<D, 7, BF16>(d, a, s);
-    case 8: return decode_t<D, 8, BF16>(d, a, s);
+    case 1: return decode_chunked<D, 1, BF16>(d, a, s);
+    case 2: return decode_chunked<D, 2, BF16>(d, a, s);
+    case 4: return decode_chunked<D, 4, BF16>(d, a, s);
+    case 7: return decode_chunked<D, 7, BF16>(d, a, s);
+    case 8: return decode_chunked<D, 8, BF16>(d, a, s);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-bool decode_group_supported(int G) { return G == 1 || G == 2 || G == 4 || G == 7 || G == 8; }
+int64_t decode_chunks(int64_t cap) { return (cap + kChunk - 1) / kChunk; }
+
+bool decode_group_supported(const DecodeDims& d) {
+  if (stream_path(d)) return true;  // any G up to 16
+  const int G = d.Hq / d.Hkv;
+  return G == 1 || G == 2 || G == 4 || G == 7 || G == 8;
+}
 
 size_t decode_partial_bytes(const DecodeDims& d) {
   const size_t nchunk = (d.cap + kChunk - 1) / kChunk;

@@ -141,7 +141,11 @@ struct DecodeArgs {
   float* part;            // workspace: chunk partials
   void* o;                // [B][Hq][d]
 };
-bool decode_group_supported(int G);
+// query heads per kv head the decode step supports for this problem: up to
+// 16 for bf16 caches of at most 1023 sequences, else 1, 2, 4, 7 or 8
+bool decode_group_supported(const DecodeDims& d);
+// chunk partials per cache of `cap` positions
+int64_t decode_chunks(int64_t cap);
 size_t decode_partial_bytes(const DecodeDims& d);
 hipError_t launch_decode_ctrl(const DecodeDims& d, const float* gate, float* tau,
                               uint8_t* selected, hipStream_t s);
