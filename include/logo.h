@@ -100,8 +100,9 @@ typedef struct {
 int64_t logo_target_count(double rho, int64_t n);
 
 /* Bytes of workspace logo_forward needs for this problem (float32 local
- * outputs of the selected rows: B*Hq*k*d*4, rounded up to 256). Writes 0
- * when nothing is needed. Errors: LOGO_ERR_INVALID_ARG / _UNSUPPORTED as
+ * outputs of the selected rows: B*Hq*k*d*4, rounded up to 256, then one
+ * int32 per (b, kv head) for the global branch's work queues, rounded up to
+ * 256). Writes 0 when nothing is needed. Errors: LOGO_ERR_INVALID_ARG / _UNSUPPORTED as
  * for logo_forward. */
 logo_status logo_workspace_size(const logo_problem* p, size_t* bytes);
 

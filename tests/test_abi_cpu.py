@@ -109,8 +109,8 @@ def test_workspace_checks(L):
     size = ctypes.c_size_t(0)
     assert L.logo_workspace_size(ctypes.byref(p), ctypes.byref(size)) == 0
     k = T.logo_target_count(0.2, 100)
-    want = 2 * 4 * k * 128 * 4
-    assert size.value == (want + 255) // 256 * 256
+    want = 2 * 4 * k * 128 * 4           # float32 local outputs of the selected rows
+    assert size.value == (want + 255) // 256 * 256 + 256   # + B*Hkv int32 queues
     assert _forward(L, p, ws=None) == _lib.LOGO_ERR_WORKSPACE
     assert _forward(L, p, ws=FAKE, ws_bytes=size.value - 1) == _lib.LOGO_ERR_WORKSPACE
     # rho = 0 selects nothing: no workspace needed

@@ -138,15 +138,17 @@ logo_status need_ptr(const void* ptr, const char* name) {
 }
 
 
-// logo_forward's workspace: the float32 local outputs of the selected rows.
-size_t scratch_bytes(const logo::Dims& d) {
-  const size_t b = (size_t)d.B * d.Hq * d.k * d.d * sizeof(float);
-  return (b + 255) / 256 * 256;
-}
-// The routed global branch's workgroup queues (one int per (b, kv head)).
+// The global branch's workgroup queues (one int per (b, kv head)).
 size_t queue_bytes(const logo::Dims& d) {  // none when nothing is selected
   return d.k == 0 ? 0 : (logo::attn_bf16_sched_ints(d, false) * sizeof(int32_t) + 255) / 256 * 256;
 }
+// logo_forward's workspace: the float32 local outputs of the selected rows,
+// then the queues.
+size_t scratch_only_bytes(const logo::Dims& d) {
+  const size_t b = (size_t)d.B * d.Hq * d.k * d.d * sizeof(float);
+  return (b + 255) / 256 * 256;
+}
+size_t scratch_bytes(const logo::Dims& d) { return scratch_only_bytes(d) + queue_bytes(d); }
 
 // ---- kernel timing --------------------------------------------------------
 struct Profiler {
@@ -342,6 +344,8 @@ logo_status logo_forward(const logo_problem* p, const void* q, const void* k, co
   a.out_f32 = static_cast<float*>(workspace);
   a.scratch = static_cast<const float*>(workspace);
   a.out_io = o;
+  if (d.k > 0 && d.dtype == LOGO_BF16)
+    a.sched = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + scratch_only_bytes(d));
   {
     StageTimer tm(1, s);
     e = run_attn(d, logo::Epi::LocalFused, a, s);

@@ -139,7 +139,7 @@ __device__ __forceinline__ void issue_tile(const uint16_t* base, int nbytes, uin
 // are clamped and ranks beyond the scratch rows ignored, so inconsistent
 // example offsets cannot address outside the buffers. Compiled separately so
 // the plain path carries none of it.
-template <int D, bool GLOBAL, int EPI, bool SEG>
+template <int D, bool GLOBAL, int EPI, bool SEG, bool QUEUE>
 __global__ __launch_bounds__(kThreads, 2)
 __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   using SM = Smem<D>;
@@ -163,13 +163,16 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   // that leans late in one sequence and early in another) goes on with
   // the others' remaining blocks instead of idling. An empty queue stays
   // empty, so every block is taken exactly once. Otherwise the workgroup
-  // does the one block its index names. Compiled for the routed and the
-  // packed-example global branches only: on the fused branch with a
+  // does the one block its index names. Always compiled for the routed and
+  // the packed-example global branches; the fused branch has both forms
+  // and takes the queue when fewer (b, kv head) units than XCDs make the
+  // static order split a unit's blocks over XCDs by index (longest first:
+  // one XCD of the pair gets most of the work). With one unit per XCD and a
   // balanced selection the queue measured 3.5 % slower (its codegen and
-  // atomics) and gained nothing, while it saves 2.5 % on the routed
-  // branch's router-driven selection and 38 % on a selection as skewed as
-  // latest tokens in one sequence, earliest in the other.
-  constexpr bool kQueue = GLOBAL && (EPI == 5 || SEG);
+  // atomics); it saves 2.5 % on the routed branch's router-driven selection
+  // and 38 % on a selection as skewed as latest tokens in one sequence,
+  // earliest in the other.
+  constexpr bool kQueue = GLOBAL && (EPI == 5 || SEG || QUEUE);
   const bool queued = kQueue && p.sched_count != nullptr;
   __shared__ int taken[2];
 #pragma unroll 1
@@ -613,11 +616,11 @@ __global__ void zero_ints_kernel(int32_t* __restrict__ p, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
 }
 
-template <int D, bool GLOBAL, int EPI, bool SEG = false>
+template <int D, bool GLOBAL, int EPI, bool SEG = false, bool QUEUE = false>
 hipError_t launch_one(const Params& prm, hipStream_t s) {
   static_assert(GLOBAL == (EPI == 2 || EPI == 3 || EPI == 5), "epilogue of the other branch");
   const int grid = prm.per_xcd * kNumXcd;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, GLOBAL, EPI, SEG>), dim3(grid), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((attn_bf16_kernel<D, GLOBAL, EPI, SEG, QUEUE>), dim3(grid), dim3(kThreads), 0, s,
                      prm);
   return hipGetLastError();
 }
@@ -633,7 +636,9 @@ hipError_t dispatch_epi(Epi epi, const Params& prm, hipStream_t s) {
     case Epi::LocalAll: return launch_one<D, false, 0>(prm, s);
     case Epi::LocalFused: return launch_one<D, false, 1>(prm, s);
     case Epi::GlobalAll: return launch_one<D, true, 2>(prm, s);
-    case Epi::GlobalFused: return launch_one<D, true, 3>(prm, s);
+    case Epi::GlobalFused:
+      return prm.sched_count ? launch_one<D, true, 3, false, true>(prm, s)
+                             : launch_one<D, true, 3>(prm, s);
     case Epi::LocalRouted: return launch_one<D, false, 4>(prm, s);
     case Epi::GlobalRouted: return launch_one<D, true, 5>(prm, s);
   }
@@ -697,7 +702,7 @@ hipError_t launch_attn_bf16(const Dims& d, Epi epi, const AttnArgs& a, hipStream
                          d.n, d.k, G, prm.units, prm.wg_per_unit, d.B * d.Hkv, perm, count);
       prm.sched_perm = perm;
       prm.sched_count = count;
-    } else {
+    } else if (epi != Epi::GlobalFused || d.B * d.Hkv < kNumXcd) {
       hipLaunchKernelGGL(zero_ints_kernel, dim3(1), dim3(256), 0, s, a.sched, d.B * d.Hkv);
       prm.sched_count = a.sched;
     }
