@@ -173,8 +173,8 @@ def record_traffic(args) -> int:
     ws = COPY_BYTES / (1024.0 * _pick(_counter_means(args.copy_write, "WRITE_SIZE"), "add"))
     fm = _counter_means(args.fwd_fetch, "FETCH_SIZE")
     wm = _counter_means(args.fwd_write, "WRITE_SIZE")
-    g = "attn_bf16_kernel<128, true, 3, false>"
-    lo = "attn_bf16_kernel<128, false, 1, false>"
+    g = "attn_bf16_kernel<128, true, 3, false, false>"
+    lo = "attn_bf16_kernel<128, false, 1, false, false>"
     gr, gw = _pick(fm, g) * 1024 * fs, _pick(wm, g) * 1024 * ws
     data = {"gqa32k": {
         "source_hash": kernel_source_hash(),

@@ -37,8 +37,8 @@ def _counters(path, counter, kernels):
 
 
 def test_record_traffic(tmp_path):
-    g = "void logo::attn_bf16_kernel<128, true, 3, false>(Params)"
-    lo = "void logo::attn_bf16_kernel<128, false, 1, false>(Params)"
+    g = "void logo::attn_bf16_kernel<128, true, 3, false, false>(Params)"
+    lo = "void logo::attn_bf16_kernel<128, false, 1, false, false>(Params)"
     add = "void at::native::vectorized_elementwise_kernel<4, CUDAFunctorOnSelf_add<float>>"
     gib_kib = (1 << 30) / 1024
     # FETCH_SIZE reads half of what a streaming read moves, WRITE_SIZE all of it
