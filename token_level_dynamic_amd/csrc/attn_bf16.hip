@@ -205,7 +205,9 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   const int R = GLOBAL ? p.ksel : p.n;          // rows per (b, head)
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // uniform in the wave: what derives from it (rows, heads, key ranges)
+  // lives in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int col = lane & 31;   // query row of this lane within the wave
   const int half = lane >> 5;  // which 8-wide k slice / 4-row group
@@ -501,9 +503,22 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   }
   float sig = 0.0f;
   if (EPI == 3 || EPI == 5) sig = 1.0f / (1.0f + expf(-p.gate[(size_t)b * p.n + pos]));
-  // routed local: this lane's half of <router_w[h], o_local row>
+  // Everything the stores combine with is loaded first: the compiler cannot
+  // tell these buffers from the outputs, so a load placed after a store
+  // would wait for every store before it. EPI 3/5: the row's local output;
+  // EPI 4: the head's router weights, for this lane's half of
+  // <router_w[h], o_local row>.
+  constexpr bool kPre = EPI == 3 || EPI == 4 || EPI == 5;
+  float4 pre[kPre ? DB * 4 : 1];
+  if (kPre) {
+    const float* src = EPI == 4 ? p.router_w + (size_t)h * D
+                       : EPI == 5 ? p.scratch + (head_row * p.n + pos) * D
+                                  : p.scratch + (head_row * p.ksel + r_lane) * D;
+#pragma unroll
+    for (int k = 0; k < DB * 4; ++k)
+      pre[k] = *reinterpret_cast<const float4*>(src + (k >> 2) * 32 + (k & 3) * 8 + half * 4);
+  }
   float rdot = 0.0f;
-  const float* rw = EPI == 4 ? p.router_w + (size_t)h * D : nullptr;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -511,17 +526,15 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
       const int d0 = db * 32 + j * 8 + half * 4;
       float4 o4 = make_float4(acc_o[db][j * 4 + 0] * inv, acc_o[db][j * 4 + 1] * inv,
                               acc_o[db][j * 4 + 2] * inv, acc_o[db][j * 4 + 3] * inv);
+      const float4 l4 = pre[kPre ? db * 4 + j : 0];
       if (EPI == 0) {
         *reinterpret_cast<float4*>(p.out_f32 + (head_row * p.n + pos) * D + d0) = o4;
       } else if (EPI == 4) {
         *reinterpret_cast<float4*>(p.out_f32 + (head_row * p.n + pos) * D + d0) = o4;
         uint2 w2 = make_uint2(pack_bf16x2(o4.x, o4.y), pack_bf16x2(o4.z, o4.w));
         *reinterpret_cast<uint2*>(orow + d0) = w2;
-        const float4 w4 = *reinterpret_cast<const float4*>(rw + d0);
-        rdot = fmaf(o4.x, w4.x, fmaf(o4.y, w4.y, fmaf(o4.z, w4.z, fmaf(o4.w, w4.w, rdot))));
+        rdot = fmaf(o4.x, l4.x, fmaf(o4.y, l4.y, fmaf(o4.z, l4.z, fmaf(o4.w, l4.w, rdot))));
       } else if (EPI == 5) {
-        const float4 l4 =
-            *reinterpret_cast<const float4*>(p.scratch + (head_row * p.n + pos) * D + d0);
         float4 c4 = make_float4(l4.x + sig * o4.x, l4.y + sig * o4.y, l4.z + sig * o4.z,
                                 l4.w + sig * o4.w);
         uint2 w2 = make_uint2(pack_bf16x2(c4.x, c4.y), pack_bf16x2(c4.z, c4.w));
@@ -536,8 +549,6 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
           *reinterpret_cast<uint2*>(orow + d0) = w2;
         }
       } else {
-        const float4 l4 =
-            *reinterpret_cast<const float4*>(p.scratch + (head_row * p.ksel + r_lane) * D + d0);
         if (p.og_out)
           *reinterpret_cast<float4*>(p.og_out + (head_row * p.ksel + r_lane) * D + d0) = o4;
         float4 c4 = make_float4(l4.x + sig * o4.x, l4.y + sig * o4.y, l4.z + sig * o4.z,
