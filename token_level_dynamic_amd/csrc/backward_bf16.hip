@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(DkdvParams p) {
   const int j0 = kb * kKB;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
@@ -544,7 +544,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqParams p) {
   const int R = GLOBAL ? p.ksel : p.n;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;

@@ -187,7 +187,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_partial_kernel(DecParam
   // uniform over the workgroup: no barrier is skipped
   if (loc ? !in_win : (!sel || c0 > i)) return;
   const bool act[1] = {true};
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
   const int grp = lane >> 4, seg = lane & 15;
   for (int e = tid; e < G * D; e += kDecWaves * 64) {
     float x[1];
@@ -447,7 +448,8 @@ __global__ __launch_bounds__(kStWaves * 64, 1) void decode_stream_kernel(StParam
   __shared__ int last[kStMaxB];     // last position (lens - 1) of each sequence
   __shared__ int wtot[kStWaves];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
   const int col = lane & 15, grp = lane >> 4;
   const int G = p.Hq / p.Hkv;
   const int S = 2 * p.B;
