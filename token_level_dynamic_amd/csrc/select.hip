@@ -24,6 +24,8 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kItems = 8;                 // positions per thread per chunk
 constexpr int kChunk = kThreads * kItems; // 8192 < 2^16: packed counts fit
+constexpr int kRegChunks = 8;             // sequences of up to 65536 positions are read
+                                          // once, into registers (8 x 8 per thread)
 
 __device__ __forceinline__ uint32_t order_image(float x) {
   uint32_t u = __float_as_uint(x);
@@ -103,6 +105,33 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   int32_t* irow = idx ? idx + (size_t)koff : nullptr;
   const int icap = SEG ? idx_cap - koff : k;  // entries of irow that may be written
 
+  // This thread's positions c * kChunk + t * kItems + j, as order images,
+  // read once (every radix pass and the compaction use them); longer
+  // sequences stream the logits from memory in each pass instead.
+  const bool vec = (n % 4) == 0 && (start % 4) == 0;
+  auto load_chunk = [&](int p0, uint32_t* img) {
+    if (vec && p0 + kItems <= n) {
+      const float4* src = reinterpret_cast<const float4*>(g + p0);
+      const float4 a = src[0], c = src[1];
+      img[0] = order_image(a.x); img[1] = order_image(a.y);
+      img[2] = order_image(a.z); img[3] = order_image(a.w);
+      img[4] = order_image(c.x); img[5] = order_image(c.y);
+      img[6] = order_image(c.z); img[7] = order_image(c.w);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kItems; ++j) img[j] = (p0 + j < n) ? order_image(g[p0 + j]) : 0u;
+    }
+  };
+  const bool in_regs = n <= kRegChunks * kChunk;
+  uint32_t reg[kRegChunks][kItems];
+  if (in_regs) {
+#pragma unroll
+    for (int c = 0; c < kRegChunks; ++c) {
+      if (c * kChunk >= n) break;
+      load_chunk(c * kChunk + t * kItems, reg[c]);
+    }
+  }
+
   uint32_t T;        // threshold image
   uint32_t need;     // ties at T to take
   if (k == 0) {
@@ -117,9 +146,22 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       const int nb = 1 << bits;
       for (int i = t; i < nb; i += kThreads) hist[i] = 0;
       __syncthreads();
-      for (int i = t; i < n; i += kThreads) {
-        uint32_t u = order_image(g[i]);
-        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
+      if (in_regs) {
+#pragma unroll
+        for (int c = 0; c < kRegChunks; ++c) {
+          if (c * kChunk >= n) break;
+#pragma unroll
+          for (int j = 0; j < kItems; ++j) {
+            const uint32_t u = reg[c][j];
+            if (c * kChunk + t * kItems + j < n && (u & pmask) == prefix)
+              atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
+          }
+        }
+      } else {
+        for (int i = t; i < n; i += kThreads) {
+          uint32_t u = order_image(g[i]);
+          if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
+        }
       }
       __syncthreads();
       // Thread t owns bins_per descending digits starting at nb-1-t*bins_per.
@@ -149,23 +191,8 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
 
   // Compaction in position order.
   uint32_t carry_gt = 0, carry_tie = 0;
-  const bool vec = (n % 4) == 0 && (start % 4) == 0;
-#pragma unroll 1
-  for (int base = 0; base < n; base += kChunk) {
+  auto compact = [&](int base, const uint32_t* img) {
     const int p0 = base + t * kItems;
-    uint32_t img[kItems];
-    if (vec && p0 + kItems <= n) {
-      const float4* src = reinterpret_cast<const float4*>(g + p0);
-      float4 a = src[0], c = src[1];
-      img[0] = order_image(a.x); img[1] = order_image(a.y);
-      img[2] = order_image(a.z); img[3] = order_image(a.w);
-      img[4] = order_image(c.x); img[5] = order_image(c.y);
-      img[6] = order_image(c.z); img[7] = order_image(c.w);
-    } else {
-#pragma unroll
-      for (int j = 0; j < kItems; ++j)
-        img[j] = (p0 + j < n) ? order_image(g[p0 + j]) : 0u;
-    }
     uint32_t ngt = 0, ntie = 0;
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
@@ -210,6 +237,20 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     }
     carry_gt += tot & 0xffffu;
     carry_tie += tot >> 16;
+  };
+  if (in_regs) {
+#pragma unroll
+    for (int c = 0; c < kRegChunks; ++c) {
+      if (c * kChunk >= n) break;
+      compact(c * kChunk, reg[c]);
+    }
+  } else {
+#pragma unroll 1
+    for (int base = 0; base < n; base += kChunk) {
+      uint32_t img[kItems];
+      load_chunk(base + t * kItems, img);
+      compact(base, img);
+    }
   }
 }
 
