@@ -102,8 +102,13 @@ int64_t logo_target_count(double rho, int64_t n);
 /* Bytes of workspace logo_forward needs for this problem (float32 local
  * outputs of the selected rows: B*Hq*k*d*4, rounded up to 256, then one
  * int32 per (b, kv head) for the global branch's work queues, rounded up to
- * 256). Writes 0 when nothing is needed. Errors: LOGO_ERR_INVALID_ARG / _UNSUPPORTED as
- * for logo_forward. */
+ * 256). A bf16 problem whose global branch has fewer than 512 workgroups
+ * (one per 32 selected rows of up to 4 query heads of a kv head:
+ * B*Hkv*ceil(ceil(k/32)*Hq/Hkv / 4)) splits each workgroup's keys into
+ * s = min(8, ceil(512 / workgroups), floor(ceil(n/64) / 4)) ranges when
+ * that is 2 or more, and then adds s*B*Hq*k*(d+4)*4 bytes of float32
+ * partials, rounded up to 256. Writes 0 when nothing is needed. Errors:
+ * LOGO_ERR_INVALID_ARG / _UNSUPPORTED as for logo_forward. */
 logo_status logo_workspace_size(const logo_problem* p, size_t* bytes);
 
 /* Budget controller + compaction (LoGo abstract: threshold-based budget
@@ -144,7 +149,10 @@ logo_status logo_combine(const logo_problem* p, const float* o_local,
  * selection (mask, idx, rank). `workspace` must hold logo_workspace_size
  * bytes (may be NULL when that is 0). Output equals logo_select_queries ->
  * logo_local_attn -> logo_global_attn_sparse -> logo_combine up to float32
- * rounding order. */
+ * rounding order; where a bf16 problem's global branch is split into key
+ * ranges (see logo_workspace_size), each range also rounds its
+ * probabilities to bf16 against its own running maximum, so the two then
+ * agree to the bf16 parity tolerance rather than bit for bit. */
 logo_status logo_forward(const logo_problem* p, const void* q, const void* k,
                          const void* v, const float* gate, void* o,
                          uint8_t* mask, int32_t* idx, int32_t* rank,

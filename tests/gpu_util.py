@@ -77,3 +77,15 @@ def host(t):
 
 def say(msg):
     print(msg, flush=True)
+
+
+def global_splits(p):
+    """True when logo_forward splits this problem's global branch into key
+    ranges: its workspace then holds more than the selected rows' float32
+    local outputs and the (b, kv head) queue counters."""
+    kk = T.logo_target_count(p.rho, p.n)
+
+    def r256(x):
+        return (x + 255) // 256 * 256
+    base = r256(p.B * p.Hq * kk * p.d * 4) + (r256(4 * p.B * p.Hkv) if kk else 0)
+    return p.dtype == 1 and T.logo_workspace_size(p) > base

@@ -119,6 +119,39 @@ def test_workspace_checks(L):
     assert size.value == 0
 
 
+def _ws_bytes(L, **kw):
+    p = _prob(**kw)
+    size = ctypes.c_size_t(0)
+    assert L.logo_workspace_size(ctypes.byref(p), ctypes.byref(size)) == 0
+    return size.value
+
+
+def _round(x):
+    return (x + 255) // 256 * 256
+
+
+def test_workspace_split_partials(L):
+    # A bf16 problem with fewer than 512 global row-block workgroups splits
+    # each block's keys over ceil(512 / workgroups) ranges, at most 8 and at
+    # least 4 key tiles of 64 each; the workspace then adds
+    # splits * B * Hq * k * (d + 4) float32 partials.
+    # n=1000, rho=0.2: k=200, 7 row blocks x 2 heads per (b, kv head) = 4
+    # workgroups each, 16 in all; 16 key tiles -> 4 ranges
+    k = T.logo_target_count(0.2, 1000)
+    base = _round(2 * 4 * k * 128 * 4) + 256
+    assert _ws_bytes(L, n=1000) == base + _round(4 * 2 * 4 * k * (128 + 4) * 4)
+    # d = 64, n = 4000 (63 tiles): 8 ranges
+    k = T.logo_target_count(0.2, 4000)
+    base = _round(2 * 4 * k * 64 * 4) + 256
+    assert _ws_bytes(L, n=4000, d=64) == base + _round(8 * 2 * 4 * k * (64 + 4) * 4)
+    # two key tiles: too few to split; float32: never split
+    assert _ws_bytes(L, n=100) == _round(2 * 4 * 20 * 128 * 4) + 256
+    assert _ws_bytes(L, n=1000, dtype=0) == _round(2 * 4 * 200 * 128 * 4) + 256
+    # 32K positions, 16 query / 4 kv heads: 1640 workgroups, no split
+    k = T.logo_target_count(0.2, 32768)
+    assert _ws_bytes(L, n=32768, Hq=16, Hkv=4) == _round(2 * 16 * k * 128 * 4) + 256
+
+
 def test_empty_problems_enqueue_nothing(L):
     for kw in (dict(B=0), dict(n=0)):
         p = _prob(**kw)

@@ -7,7 +7,8 @@ import torch
 
 import oracle
 import token_level_dynamic_amd as T
-from gpu_util import ensure_built, host, problem, run_forward, run_unfused, say, to_dev
+from gpu_util import (ensure_built, global_splits, host, problem, run_forward, run_unfused,
+                      say, to_dev)
 from workloads import get_workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -85,9 +86,17 @@ def test_forward_matches_oracle_and_unfused(name):
     assert np.array_equal(host(got["idx"]), ref["idx"])
     assert np.array_equal(host(got["rank"]), ref["rank"])
     assert _report("o", host(got["o"]), ref["o"]) <= TOL[w.dtype]
-    # the fused path does the same float32 arithmetic as the four calls
+    # the fused path does the same float32 arithmetic as the four calls,
+    # except that a small bf16 problem splits the global branch's keys into
+    # ranges (its workspace then holds their partials): each range rounds
+    # its probabilities to bf16 against its own running maximum, so the two
+    # agree to the parity tolerance, as both agree with the oracle
     un = run_unfused(p, q, k, v, gate)
-    assert torch.equal(got["o"], un["o"])
+    if global_splits(p):
+        assert _report("o vs unfused (split)", host(got["o"]), host(un["o"])) <= TOL[w.dtype]
+    else:
+        assert torch.equal(got["o"], un["o"])
+
 
 
 def test_forward_is_deterministic():

@@ -8,7 +8,7 @@ import torch
 import oracle
 import oracle.varlen as VL
 import token_level_dynamic_amd as T
-from gpu_util import dev, ensure_built, say
+from gpu_util import dev, ensure_built, global_splits, say
 from workloads import VARLEN_WORKLOADS, make_varlen_inputs
 
 pytestmark = pytest.mark.gpu
@@ -87,7 +87,10 @@ def test_varlen_matches_oracle(name):
 
 
 def test_single_example_equals_forward():
-    """One example: the same arithmetic as logo_forward, bit for bit."""
+    """One example: the same arithmetic as logo_forward, bit for bit, except
+    where logo_forward splits a small problem's global branch into key
+    ranges (probabilities rounded against each range's maximum): then the
+    two agree to the parity tolerance."""
     Hq, Hkv, d, n, W, rho = 4, 2, 128, 777, 90, 0.2
     inp = make_varlen_inputs([n], Hq, Hkv, d, "bf16", seed=2)
     got = run_varlen(inp, Hq, Hkv, d, W, rho, "bf16")
@@ -100,7 +103,12 @@ def test_single_example_equals_forward():
     T.logo_forward(p, q, k, v, g, buf["o"], buf["mask"], buf["idx"], buf["rank"],
                    buf["workspace"])
     torch.cuda.synchronize()
-    assert torch.equal(got["o_dev"].view(torch.int16), buf["o"].view(torch.int16))
+    if global_splits(p):
+        err = float((got["o_dev"].float() - buf["o"].float()).abs().max())
+        say(f"  split forward vs packed max_abs={err:.3e}")
+        assert err <= TOL["bf16"]
+    else:
+        assert torch.equal(got["o_dev"].view(torch.int16), buf["o"].view(torch.int16))
     assert np.array_equal(got["idx"], buf["idx"][0].cpu().numpy())
 
 

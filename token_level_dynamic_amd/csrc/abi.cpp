@@ -148,7 +148,15 @@ size_t scratch_only_bytes(const logo::Dims& d) {
   const size_t b = (size_t)d.B * d.Hq * d.k * d.d * sizeof(float);
   return (b + 255) / 256 * 256;
 }
-size_t scratch_bytes(const logo::Dims& d) { return scratch_only_bytes(d) + queue_bytes(d); }
+// and, for a bf16 problem small enough that the global branch splits its
+// key ranges, the partials of the split
+size_t split_bytes(const logo::Dims& d) {
+  if (d.dtype != LOGO_BF16) return 0;
+  return (logo::attn_bf16_split_floats(d) * sizeof(float) + 255) / 256 * 256;
+}
+size_t scratch_bytes(const logo::Dims& d) {
+  return scratch_only_bytes(d) + queue_bytes(d) + split_bytes(d);
+}
 
 // ---- kernel timing --------------------------------------------------------
 struct Profiler {
@@ -344,8 +352,12 @@ logo_status logo_forward(const logo_problem* p, const void* q, const void* k, co
   a.out_f32 = static_cast<float*>(workspace);
   a.scratch = static_cast<const float*>(workspace);
   a.out_io = o;
-  if (d.k > 0 && d.dtype == LOGO_BF16)
+  if (d.k > 0 && d.dtype == LOGO_BF16) {
     a.sched = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + scratch_only_bytes(d));
+    if (split_bytes(d) > 0)
+      a.split_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                              scratch_only_bytes(d) + queue_bytes(d));
+  }
   {
     StageTimer tm(1, s);
     e = run_attn(d, logo::Epi::LocalFused, a, s);

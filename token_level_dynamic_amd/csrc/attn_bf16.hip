@@ -34,6 +34,8 @@
 // turn, so logical tiles are renumbered so each XCD walks a contiguous
 // range of (b, kv head) units and keeps their K/V in its own L2. Global
 // tiles of one unit run longest causal prefix first.
+#include <algorithm>
+
 #include "logo_internal.h"
 
 namespace logo {
@@ -99,6 +101,9 @@ struct Params {
                              // (NULL: the last row block first)
   int32_t* sched_count;      // global: per (b, kv head) next rank, zeroed before the
                              // launch; NULL: the static order
+  int nsplit;                // fused global: key ranges per row block (1: none)
+  float* part;               // nsplit > 1: partials [nsplit][B*Hq][ksel][D + 4]
+                             // (unnormalised o, then max and sum)
 };
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
@@ -152,8 +157,12 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
 
   // ---- which tile -------------------------------------------------------
   const int bid = blockIdx.x;
-  const int L = (bid % kNumXcd) * p.per_xcd + bid / kNumXcd;
-  if (L >= p.total_wg) return;
+  const int Lx = (bid % kNumXcd) * p.per_xcd + bid / kNumXcd;
+  if (Lx >= p.total_wg * p.nsplit) return;
+  // split key ranges (fused global branch of a small problem): workgroup
+  // Lx takes key range `split` of row block L
+  const int split = Lx % p.nsplit;
+  const int L = Lx / p.nsplit;
   // Queued global launches (p.sched_count set): each (b, kv head) unit has a
   // queue of its row blocks, heaviest first (the last rows; for packed
   // examples the order the schedule kernel built). A workgroup takes blocks
@@ -243,8 +252,14 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   const int gpos_lo = row_pos((u_first / G) * kRows);
   const int gpos_hi = row_pos(min((u_last / G) * kRows + kRows, R) - 1);
   const int gss_lo = seg0(gpos_lo);
-  const int t_lo = (GLOBAL ? gss_lo : max(gss_lo, gpos_lo - p.W + 1)) / kKeys;
-  const int t_hi = gpos_hi / kKeys;
+  int t_lo = (GLOBAL ? gss_lo : max(gss_lo, gpos_lo - p.W + 1)) / kKeys;
+  int t_hi = gpos_hi / kKeys;
+  if (EPI == 3 && p.nsplit > 1) {
+    // this workgroup's share of the block's key tiles (possibly none)
+    const int per = (t_hi - t_lo + p.nsplit) / p.nsplit;
+    t_lo += split * per;
+    t_hi = min(t_hi, t_lo + per - 1);
+  }
 
   // This (b, kv head)'s K and V, read through bounds-checked buffer loads:
   // keys past the end read as zero (they only occur in tiles masked per
@@ -488,9 +503,23 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
                                                      __float_as_uint(l_run), false, false);
   const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
-  if (row_ok) {
-  const float inv = 1.0f / l_tot;
   const size_t head_row = (size_t)(b * p.Hq + h);
+  if (EPI == 3 && p.nsplit > 1 && row_ok) {
+    // partial of one key range: unnormalised o, running max (log2 units),
+    // row sum; a merge kernel combines the ranges and applies the gate
+    float* const po =
+        p.part + (((size_t)split * p.B * p.Hq + head_row) * p.ksel + r_lane) * (D + 4);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4*>(po + db * 32 + j * 8 + half * 4) =
+            make_float4(acc_o[db][j * 4 + 0], acc_o[db][j * 4 + 1], acc_o[db][j * 4 + 2],
+                        acc_o[db][j * 4 + 3]);
+    }
+    if (half == 0) *reinterpret_cast<float2*>(po + D) = make_float2(m_run, l_tot);
+  } else if (row_ok) {
+  const float inv = 1.0f / l_tot;
   if (p.lse_out && half == 0)
     p.lse_out[head_row * R + (GLOBAL ? r_lane : pos)] = (m_run + __log2f(l_tot)) * kLn2;
   uint16_t* const orow = p.out_io + b * p.vo.sb + h * p.vo.sh + (long long)pos * p.vo.st;
@@ -627,10 +656,56 @@ __global__ void zero_ints_kernel(int32_t* __restrict__ p, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
 }
 
+// Fused global branch split over key ranges: one wave per selected row
+// merges the ranges' partials (max m_s and sum l_s in log2 units, o_s
+// unnormalised: o = sum_s 2^(m_s - m) o_s / sum_s 2^(m_s - m) l_s, m the
+// largest m_s), then writes o_local + sigmoid(gate) o_global as the fused
+// epilogue does. Every row has key 0 in the first range, so the sum is
+// positive.
+template <int D>
+__global__ __launch_bounds__(256) void global_merge_kernel(
+    const float* __restrict__ part, int nsplit, int B, int Hq, int k, int n,
+    const int32_t* __restrict__ idx, const float* __restrict__ gate,
+    const float* __restrict__ scratch, uint16_t* __restrict__ out, View vo) {
+  constexpr int E = D / 64;  // elements per lane
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long long rows = (long long)B * Hq * k;
+  const long long row = (long long)blockIdx.x * 4 + wave;  // (b * Hq + h) * k + r
+  if (row >= rows) return;
+  const int head_row = (int)(row / k), r = (int)(row % k);
+  const int b = head_row / Hq, h = head_row % Hq;
+  const size_t plane = (size_t)rows * (D + 4);
+  const float* const p0 = part + (size_t)row * (D + 4);
+  float m = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, p0[s * plane + D]);
+  float l = 0.0f, acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float* const ps = p0 + s * plane;
+    const float wgt = __builtin_amdgcn_exp2f(ps[D] - m);
+    l = fmaf(ps[D + 1], wgt, l);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = fmaf(ps[lane * E + e], wgt, acc[e]);
+  }
+  const float inv = 1.0f / l;
+  const int pos = idx[(size_t)b * k + r];
+  const float sig = 1.0f / (1.0f + expf(-gate[(size_t)b * n + pos]));
+  const float* const lrow = scratch + ((size_t)head_row * k + r) * D + lane * E;
+  uint16_t* const orow = out + b * vo.sb + h * vo.sh + (long long)pos * vo.st + lane * E;
+  if (E == 2) {
+    const float c0 = lrow[0] + sig * (acc[0] * inv);
+    const float c1 = lrow[1] + sig * (acc[E - 1] * inv);
+    *reinterpret_cast<uint32_t*>(orow) = pack_bf16x2(c0, c1);
+  } else {
+    orow[0] = f32_to_bf16_bits(lrow[0] + sig * (acc[0] * inv));
+  }
+}
+
 template <int D, bool GLOBAL, int EPI, bool SEG = false, bool QUEUE = false>
 hipError_t launch_one(const Params& prm, hipStream_t s) {
   static_assert(GLOBAL == (EPI == 2 || EPI == 3 || EPI == 5), "epilogue of the other branch");
-  const int grid = prm.per_xcd * kNumXcd;
+  const int grid = prm.per_xcd * kNumXcd;  // per_xcd counts split workgroups
   hipLaunchKernelGGL((attn_bf16_kernel<D, GLOBAL, EPI, SEG, QUEUE>), dim3(grid), dim3(kThreads), 0, s,
                      prm);
   return hipGetLastError();
@@ -657,6 +732,27 @@ hipError_t dispatch_epi(Epi epi, const Params& prm, hipStream_t s) {
 }
 
 }  // namespace
+
+int attn_bf16_splits(const Dims& d) {
+  // Enough workgroups for two per CU on a 256-CU part, at most 8 ranges and
+  // at least 4 key tiles per range; a fixed function of the shape, so the
+  // workspace it needs does not depend on the device.
+  constexpr long long kTarget = 512;
+  if (d.k <= 0) return 1;
+  const long long G = d.Hq / d.Hkv;
+  const long long units = ((long long)d.k + kRows - 1) / kRows * G;
+  const long long total = (long long)d.B * d.Hkv * ((units + kWaves - 1) / kWaves);
+  if (total >= kTarget) return 1;
+  long long s = (kTarget + total - 1) / total;
+  s = std::min<long long>(s, 8);
+  s = std::min<long long>(s, std::max<long long>(1, ((long long)d.n + kKeys - 1) / kKeys / 4));
+  return (int)std::max<long long>(s, 1);
+}
+
+size_t attn_bf16_split_floats(const Dims& d) {
+  const int s = attn_bf16_splits(d);
+  return s > 1 ? (size_t)s * d.B * d.Hq * d.k * (d.d + 4) : 0;
+}
 
 size_t attn_bf16_sched_ints(const Dims& d, bool packed) {
   const size_t npb = ((size_t)d.k + kRows - 1) / kRows;
@@ -691,7 +787,6 @@ hipError_t launch_attn_bf16(const Dims& d, Epi epi, const AttnArgs& a, hipStream
   prm.units = npb * G;
   prm.wg_per_unit = (prm.units + kWaves - 1) / kWaves;
   prm.total_wg = d.B * d.Hkv * prm.wg_per_unit;
-  prm.per_xcd = (prm.total_wg + kNumXcd - 1) / kNumXcd;
   prm.vq = d.vq;
   prm.vk = d.vk;
   prm.vv = d.vv;
@@ -703,7 +798,17 @@ hipError_t launch_attn_bf16(const Dims& d, Epi epi, const AttnArgs& a, hipStream
   prm.seg_start = a.seg_start;
   prm.sched_perm = nullptr;
   prm.sched_count = nullptr;
-  if (global && a.sched) {
+  // a small fused global branch splits each row block's keys over several
+  // workgroups (partials in a.split_part) and merges them after
+  prm.nsplit = 1;
+  prm.part = nullptr;
+  if (epi == Epi::GlobalFused && a.split_part && !a.seg_start && !a.lse_out && !a.og_out) {
+    prm.nsplit = attn_bf16_splits(d);
+    if (prm.nsplit > 1) prm.part = a.split_part;
+    else prm.nsplit = 1;
+  }
+  prm.per_xcd = (prm.total_wg * prm.nsplit + kNumXcd - 1) / kNumXcd;
+  if (global && a.sched && prm.nsplit == 1) {
     // the queues' counters are zeroed by a kernel on the stream (no memset
     // node, so the sequence can be captured in a graph)
     if (a.seg_start) {
@@ -720,9 +825,20 @@ hipError_t launch_attn_bf16(const Dims& d, Epi epi, const AttnArgs& a, hipStream
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (d.d == 64) return dispatch_epi<64>(epi, prm, s);
-  if (d.d == 128) return dispatch_epi<128>(epi, prm, s);
-  return hipErrorInvalidValue;
+  hipError_t e;
+  if (d.d == 64) e = dispatch_epi<64>(epi, prm, s);
+  else if (d.d == 128) e = dispatch_epi<128>(epi, prm, s);
+  else return hipErrorInvalidValue;
+  if (e != hipSuccess || prm.nsplit == 1) return e;
+  const long long rows = (long long)d.B * d.Hq * d.k;
+  const dim3 mgrid((unsigned)((rows + 3) / 4));
+  if (d.d == 64)
+    hipLaunchKernelGGL(global_merge_kernel<64>, mgrid, dim3(256), 0, s, prm.part, prm.nsplit,
+                       d.B, d.Hq, d.k, d.n, a.idx, a.gate, a.scratch, prm.out_io, d.vo);
+  else
+    hipLaunchKernelGGL(global_merge_kernel<128>, mgrid, dim3(256), 0, s, prm.part, prm.nsplit,
+                       d.B, d.Hq, d.k, d.n, a.idx, a.gate, a.scratch, prm.out_io, d.vo);
+  return hipGetLastError();
 }
 
 }  // namespace logo

@@ -55,6 +55,9 @@ struct AttnArgs {
   int32_t* sched;        // bf16 global branch: workspace of attn_bf16_sched_ints()
                          // ints for the workgroup queues (and, for packed examples,
                          // the work order), or NULL for the static order
+  float* split_part;     // bf16 fused global branch: attn_bf16_split_floats() floats
+                         // for the key-range partials of a small problem, or NULL
+                         // (no split)
 };
 
 // Everything the backward kernels read and write. q, k, v, o and dout are
@@ -113,6 +116,11 @@ hipError_t launch_varlen_prep(const int32_t* cu, int E, int T, double rho, int4*
 // Ints of workspace the bf16 global branch uses for its workgroup queues
 // (one counter per (b, kv head)) and, for packed examples, the work order.
 size_t attn_bf16_sched_ints(const Dims& d, bool packed);
+// Key ranges the bf16 fused global branch splits each row block into (1: no
+// split; more when the problem has fewer than 512 row-block workgroups), and
+// the float32 partials that takes: splits * B * Hq * k * (d + 4), or 0.
+int attn_bf16_splits(const Dims& d);
+size_t attn_bf16_split_floats(const Dims& d);
 hipError_t launch_attn_bf16(const Dims& d, Epi epi, const AttnArgs& a,
                             hipStream_t s);
 
