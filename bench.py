@@ -60,6 +60,15 @@ def kernel_source_hash(sources=None) -> str:
     return h.hexdigest()[:16]
 
 
+def input_sha256(*arrays) -> str:
+    """SHA-256 (first 16 hex digits) of the input arrays' bytes, in order: the
+    same seed and workload give the same digest on any machine."""
+    h = hashlib.sha256()
+    for a in arrays:
+        h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()[:16]
+
+
 def effective_flops(w, idx: np.ndarray) -> dict:
     """Effective FLOPs of the layer from the realised selection idx [B, k]."""
     i = np.arange(w.n, dtype=np.float64)
@@ -270,7 +279,7 @@ def band_pairs(w) -> float:
     return float(np.minimum(w.window, i + 1).sum())
 
 
-def train_bench(args, torch, T, w, inp, p, q, k, v, gate, dev) -> int:
+def train_bench(args, torch, T, w, inp, p, q, k, v, gate, dev, digest) -> int:
     """One step = logo_forward_train + logo_backward over one batch."""
     from workloads import make_dout
     dvals, dbits = make_dout(w, args.seed)
@@ -338,6 +347,7 @@ def train_bench(args, torch, T, w, inp, p, q, k, v, gate, dev) -> int:
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
+        "input_sha256": digest,
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "n": w.n,
                    "d": w.d, "window": w.window, "rho": w.rho,
                    "k_sel": int(T.logo_target_count(w.rho, w.n)), "seed": args.seed,
@@ -363,7 +373,7 @@ def train_bench(args, torch, T, w, inp, p, q, k, v, gate, dev) -> int:
     return 0
 
 
-def routed_bench(args, torch, T, w, inp, p, q, k, v, dev) -> int:
+def routed_bench(args, torch, T, w, inp, p, q, k, v, dev, digest) -> int:
     """One step = logo_forward_routed (local, router logits, select, global)."""
     from workloads import make_router
     rw, rb = make_router(w, args.seed)
@@ -412,6 +422,7 @@ def routed_bench(args, torch, T, w, inp, p, q, k, v, dev) -> int:
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
+        "input_sha256": digest,
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "n": w.n,
                    "d": w.d, "window": w.window, "rho": w.rho,
                    "k_sel": int(T.logo_target_count(w.rho, w.n)), "seed": args.seed,
@@ -450,6 +461,7 @@ def decode_bench(args, torch, T) -> int:
 
     def cv(bits):
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    digest = input_sha256(inp.bits["q"], inp.bits["k"], inp.bits["v"], inp.lens, inp.gate, inp.tau)
     q, k, v = cv(inp.bits["q"]), cv(inp.bits["k"]), cv(inp.bits["v"])
     del inp.k, inp.v, inp.bits
     lens = torch.from_numpy(inp.lens).to(dev)
@@ -501,6 +513,7 @@ def decode_bench(args, torch, T) -> int:
         "vs_baseline": None,
         "dtype": cfg["dtype"],
         "data": "synthetic",
+        "input_sha256": digest,
         "config": {"workload": "decode128k", "B": B, "Hq": Hq, "Hkv": Hkv, "cap": cap, "d": d,
                    "window": W, "rho": cfg["rho"], "tau": round(tau0, 6), "eta": 0.0,
                    "selected": int(selected.sum()), "seed": args.seed, "mode": "decode",
@@ -536,6 +549,8 @@ def varlen_bench(args, torch, T) -> int:
 
     def cv(bits):
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)[None]
+    digest = input_sha256(inp["bits"]["q"], inp["bits"]["k"], inp["bits"]["v"], inp["gate"],
+                          inp["cu"])
     q, k, v = cv(inp["bits"]["q"]), cv(inp["bits"]["k"]), cv(inp["bits"]["v"])
     Tn = int(inp["cu"][-1])
     p = T.make_problem(1, Hq, Hkv, Tn, d, W, rho)
@@ -594,6 +609,7 @@ def varlen_bench(args, torch, T) -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
+        "input_sha256": digest,
         "config": {"workload": "varlen64k", "lens": lens, "Hq": Hq, "Hkv": Hkv, "d": d,
                    "window": W, "rho": rho, "k_sel": K, "seed": args.seed, "mode": "varlen",
                    "parallelism": "none (1 GPU)"},
@@ -683,6 +699,10 @@ def main() -> int:
     if args.rho is not None:
         w = w.with_(rho=args.rho)
     inp = make_inputs(w, args.seed)
+    if w.dtype == "bf16":
+        digest = input_sha256(inp.q_bits, inp.k_bits, inp.v_bits, inp.gate)
+    else:
+        digest = input_sha256(inp.q, inp.k, inp.v, inp.gate)
     dev = torch.device("cuda:0")
     if w.dtype == "bf16":
         def cv(bits):
@@ -693,9 +713,9 @@ def main() -> int:
     gate = torch.from_numpy(inp.gate).to(dev)
     p = T.make_problem(w.B, w.Hq, w.Hkv, w.n, w.d, w.window, w.rho, dtype=w.dtype)
     if args.mode == "train":
-        return train_bench(args, torch, T, w, inp, p, q, k, v, gate, dev)
+        return train_bench(args, torch, T, w, inp, p, q, k, v, gate, dev, digest)
     if args.mode == "routed":
-        return routed_bench(args, torch, T, w, inp, p, q, k, v, dev)
+        return routed_bench(args, torch, T, w, inp, p, q, k, v, dev, digest)
     buf = T.alloc_forward_buffers(p, dev)
 
     def step():
@@ -745,6 +765,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
+        "input_sha256": digest,
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "n": w.n,
                    "d": w.d, "window": w.window, "rho": w.rho,
                    "k_sel": int(T.logo_target_count(w.rho, w.n)), "seed": args.seed,

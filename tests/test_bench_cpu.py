@@ -60,3 +60,16 @@ def test_record_traffic(tmp_path):
     assert d["global_bytes_per_launch"] == d["global_read_bytes"] + d["global_write_bytes"]
     assert d["local_bytes_per_launch"] == (10 * 2 + 7) * 1024
     assert d["source_hash"] == bench.kernel_source_hash()
+
+
+def test_input_digest_follows_the_seed():
+    # the bench line's input_sha256: same workload and seed -> same digest;
+    # another seed or another array order -> another
+    from workloads import get_workload, make_inputs
+    w = get_workload("gqa32k", B=1, Hq=2, Hkv=1, n=64, window=16, rho=0.25)
+    a, b, c = make_inputs(w, 0), make_inputs(w, 0), make_inputs(w, 1)
+    da = bench.input_sha256(a.q_bits, a.k_bits, a.v_bits, a.gate)
+    assert da == bench.input_sha256(b.q_bits, b.k_bits, b.v_bits, b.gate)
+    assert da != bench.input_sha256(c.q_bits, c.k_bits, c.v_bits, c.gate)
+    assert da != bench.input_sha256(a.k_bits, a.q_bits, a.v_bits, a.gate)
+    assert len(da) == 16
