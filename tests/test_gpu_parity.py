@@ -37,6 +37,12 @@ CASES = {
     "f32_single_token": ("tiny", dict(B=1, Hq=2, Hkv=1, n=1, window=8, rho=0.5)),
     "bf16_unscaled_mha4k_shape": ("mha4k", dict(Hq=2, Hkv=2, n=700, qkv_scale=False)),
     "bf16_bursty": ("sweep64k", dict(B=1, Hq=2, Hkv=2, n=3000, window=256, rho=0.05)),
+    # the fused global branch's key-range split: one selected row per sequence
+    # (4 ranges, most of them empty for that row's block), and d = 64 with
+    # seven-head groups (7 ranges of uneven length)
+    "bf16_split_one_row": ("gqa32k", dict(B=2, Hq=4, Hkv=2, n=1000, window=64, rho=0.001)),
+    "bf16_split_d64_group7": ("sweep64k", dict(B=1, Hq=14, Hkv=2, n=1800, window=100,
+                                               rho=0.1)),
 }
 
 
