@@ -83,10 +83,13 @@ __device__ __forceinline__ void issue_rows(const uint16_t* base, int nbytes, uin
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(base), (short)0, nbytes, 0x00020000);
 #pragma unroll
-  for (int j = wave; j < NCH; j += kWaves) {
-    const uint32_t voff = slot_off(j * 64 + lane, CHUNKS, DCH, st2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)(dst + j * 512), 16, voff, soff, 0,
-                                             0);
+  for (int i = 0; i < (NCH + kWaves - 1) / kWaves; ++i) {
+    const int j = wave + kWaves * i;
+    if (j < NCH) {
+      const uint32_t voff = slot_off(j * 64 + lane, CHUNKS, DCH, st2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)(dst + j * 512), 16, voff, soff,
+                                               0, 0);
+    }
   }
 }
 

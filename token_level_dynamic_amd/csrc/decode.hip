@@ -440,6 +440,7 @@ __global__ __launch_bounds__(kStWaves * 64, 1) void decode_stream_kernel(StParam
   // one LDS object per stage (K tile, V tile, query rows): the compiler
   // tells the stage being read from the stages whose loads are in flight
   // only when they are distinct objects
+  static_assert(kStStages == 4, "the stages are the four LDS objects T0..T3");
   __shared__ __attribute__((aligned(16))) uint16_t T0[TL::kStage];
   __shared__ __attribute__((aligned(16))) uint16_t T1[TL::kStage];
   __shared__ __attribute__((aligned(16))) uint16_t T2[TL::kStage];
