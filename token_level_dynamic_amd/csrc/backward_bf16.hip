@@ -17,18 +17,21 @@
 // (e/4)*8 + (l/32)*4 + e%4 for element e):
 //
 // bwd_dkdv_kernel: key-stationary. A workgroup owns 128 keys of one
-//   (b, kv head), 32 per wave; the K and V rows of its keys sit in registers
-//   as B operands. It streams 32-row query tiles through LDS: for each query
-//   head of the group, the local rows that read its keys and then the
-//   selected rows at or after its first key. Per tile and wave:
-//     S  [32 q x 32 keys] = Q  K^T     (A = Q rows from LDS)
-//     dP [32 q x 32 keys] = dO V^T     (A = dO rows from LDS)
-//     P = exp2(S scale log2e - lse log2e), dS = P (dP - Dr)
-//     dV^T[d x keys] += dO^T P,  dK^T[d x keys] += Q^T dS
-//   where dO^T and Q^T come from the same row-major LDS tiles through the
-//   gfx950 transposing read (ds_read_b64_tr_b16) and P, dS feed the B
-//   operand straight from the accumulator layout (the query order of the
-//   contraction is permuted to match, as in the forward's PV product).
+//   (b, kv head) and streams 32-row query tiles through LDS: for each query
+//   head of the group, the selected rows at or after its first key, then
+//   the local rows that read its keys. Its eight waves form four pairs of
+//   32 keys with two roles, one wave of each role per SIMD:
+//     producer (K, V rows of its keys in registers as A operands):
+//       S^T [32 keys x 32 q] = K Q^T,  dP^T = V dO^T   (B = Q, dO rows)
+//       P = exp2(S scale log2e - lse log2e), dS = P (dP - Dr)
+//       and hands P, dS over through LDS as bf16 [32 q x 32 keys] tiles;
+//     consumer (the dK^T, dV^T accumulators):
+//       dV^T [d x keys] += dO^T P,  dK^T [d x keys] += Q^T dS
+//       with dO^T, Q^T, P and dS all read by the gfx950 transposing LDS read
+//       (ds_read_b64_tr_b16), and issues the workgroup's tile loads.
+//   While one wave of a SIMD runs its elementwise work the other's matrix
+//   products keep the matrix core busy; one wave alone per SIMD leaves it
+//   idle whenever that wave is not issuing products.
 //
 // bwd_dq_kernel: query-stationary, like the forward: 32 rows per wave with
 //   Q and dO rows in registers, K/V tiles of 64 keys through LDS:
@@ -117,8 +120,10 @@ __device__ __forceinline__ bf16x8 read_tr(const uint16_t* tile, int stride, int 
 // dK / dV
 // =========================================================================
 constexpr int kQT = 32;    // query rows per tile
-constexpr int kKW = 32;    // keys per wave
-constexpr int kKB = kKW * kWaves;  // keys per workgroup
+constexpr int kKW = 32;    // keys per wave pair
+constexpr int kPairs = 4;  // wave pairs per workgroup
+constexpr int kKB = kKW * kPairs;  // keys per workgroup
+constexpr int kDkdvThreads = 2 * kPairs * 64;
 
 template <int D>
 struct QTile {
@@ -157,6 +162,30 @@ struct DkdvParams {
 // others read out of range (zeros), so each array gets a 1 KiB landing slot.
 constexpr int kSlot = 256;  // floats per landing slot
 
+// P and dS of one tile, handed from producer to consumer waves: per wave
+// pair a [32 query rows][32 keys] bf16 tile of each, rows of 64 bytes whose
+// 8-byte chunks are XOR-swizzled by (row / 4) % 8, so the producers' row
+// writes and the consumers' transposing reads both cover the banks once.
+constexpr int kPsPair = 2 * kQT * kKW;      // P then dS (elements)
+constexpr int kPsElems = kPairs * kPsPair;
+
+__device__ __forceinline__ int ps_off(int row, int chunk) {
+  return row * kKW + ((chunk ^ ((row >> 2) & 7)) << 2);
+}
+
+// The B operand of a dV / dK product from a P or dS tile: key column l % 32,
+// rows r0 + {half*4 + [0,4)} and r0 + 8 + {half*4 + [0,4)}, the order of
+// the A operand that read_tr gives for the same rows.
+__device__ __forceinline__ bf16x8 read_tr_ps(const uint16_t* tile, int r0, int lane) {
+  const int rl = r0 + (lane >> 5) * 4 + ((lane & 15) >> 2);
+  const int chunk = ((lane >> 4) & 1) * 4 + (lane & 3);
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(tile + ps_off(rl, chunk)));
+  const v4i16 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(tile + ps_off(rl + 8, chunk)));
+  const uint2 l2 = __builtin_bit_cast(uint2, lo);
+  const uint2 h2 = __builtin_bit_cast(uint2, hi);
+  return __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+}
 
 // 32 consecutive 4-byte values from byte soff of [src, src + nbytes) into
 // dst[0..32) (values past nbytes read zero); the rest of the slot gets zeros.
@@ -171,18 +200,19 @@ __device__ __forceinline__ void issue_row_data(const void* src, int nbytes, floa
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)dst, 16, voff, soff, 0, 0);
 }
 
+// Wave pair w owns keys j0 + 32w ... j0 + 32w + 31: producer wave w,
+// consumer wave 4 + w. Step u: producers work on tile u, consumers on tile
+// u-1 and issue the loads of tile u+1; one barrier per step.
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(DkdvParams p) {
+__global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(DkdvParams p) {
   using QT = QTile<D>;
   constexpr int QS = D / 16;  // k-steps along d
   constexpr int DB = D / 32;  // 32-wide d blocks
   constexpr int DCH = D / 8;
   constexpr int NQ = QT::kInstr;
-  // Three tile buffers (tile t is consumed while t+1 is read for the next
-  // products and t+2 lands), each a distinct LDS object so the compiler can
-  // tell reads of one from buffer loads still landing in another. (Loading
-  // one tile further ahead, with a fourth buffer, measured slower: the cost
-  // of the loads is LDS and texture-path bandwidth, not latency.)
+  // Three of each buffer (tile u read by producers, u-1 by consumers, u+1
+  // landing), each a distinct LDS object so the compiler can tell reads of
+  // one from buffer loads still landing in another.
   __shared__ __attribute__((aligned(16))) uint16_t Q0[QT::kElems];
   __shared__ __attribute__((aligned(16))) uint16_t Q1[QT::kElems];
   __shared__ __attribute__((aligned(16))) uint16_t Q2[QT::kElems];
@@ -192,6 +222,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(DkdvParams p) {
   __shared__ __attribute__((aligned(16))) float R0[3 * kSlot];  // lse | Dr | pos
   __shared__ __attribute__((aligned(16))) float R1[3 * kSlot];
   __shared__ __attribute__((aligned(16))) float R2[3 * kSlot];
+  __shared__ __attribute__((aligned(16))) uint16_t PS0[kPsElems];
+  __shared__ __attribute__((aligned(16))) uint16_t PS1[kPsElems];
+  __shared__ __attribute__((aligned(16))) uint16_t PS2[kPsElems];
 
   const int bid = blockIdx.x;
   const int L = (bid % kNumXcd) * p.per_xcd + bid / kNumXcd;
@@ -205,24 +238,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(DkdvParams p) {
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
+  const bool producer = wave < kPairs;
+  const int pw = wave & (kPairs - 1);  // wave pair
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
-  const int kw0 = j0 + wave * kKW;
-  const int key = kw0 + col;
-
-  // K and V rows of this lane's key: B operands for the whole kernel.
-  bf16x8 kreg[QS], vreg[QS];
-  {
-    const int kk = min(key, p.n - 1);
-    const uint16_t* kr = p.k + b * p.vk.sb + hk * p.vk.sh + (long long)kk * p.vk.st + half * 8;
-    const uint16_t* vr = p.v + b * p.vv.sb + hk * p.vv.sh + (long long)kk * p.vv.st + half * 8;
-#pragma unroll
-    for (int s = 0; s < QS; ++s) {
-      kreg[s] = ld16(kr + s * 16);
-      vreg[s] = ld16(vr + s * 16);
-    }
-  }
+  const int key0 = j0 + pw * kKW;  // first key of the wave pair
+  const int key = key0 + col;
 
   // Query tiles: selected rows at or after j0 (T_glb tiles per head of the
   // group), then per head T_loc local tiles (rows j0 ..., every row whose
@@ -269,9 +291,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(DkdvParams p) {
     return d;
   };
 
-  // Buffer loads of tile t: Q and dO rows (NQ instructions each, shared by
-  // the four waves), then lse, Dr and, for selected rows, their positions
-  // (one instruction each, waves 0..2).
+  // Buffer loads of tile t, issued by the consumer waves (cw = 0..3): Q and
+  // dO rows (NQ instructions each), then lse, Dr and, for selected rows,
+  // their positions (one instruction each, cw 0..2).
+  const int cw = wave - kPairs;
   auto issue = [&] __device__ (int t, uint16_t* qdst, uint16_t* odst, float* rdst)
       __attribute__((always_inline)) {
     const Desc d = desc(t);
@@ -280,189 +303,154 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(DkdvParams p) {
       const int qst2 = p.vq.st * 2, ost2 = p.vo.st * 2;
       issue_rows<NQ, QT::kChunks, DCH>(p.q + b * p.vq.sb + d.h * p.vq.sh,
                                        ((p.n - 1) * p.vq.st + D) * 2, qdst, d.r0 * qst2, qst2,
-                                       wave, lane);
+                                       cw, lane);
       issue_rows<NQ, QT::kChunks, DCH>(p.dout + b * p.vo.sb + d.h * p.vo.sh,
                                        ((p.n - 1) * p.vo.st + D) * 2, odst, d.r0 * ost2, ost2,
-                                       wave, lane);
+                                       cw, lane);
     } else {
       const long long cb = hb * p.ksel;
       issue_rows<NQ, QT::kChunks, DCH>(p.qs + cb * D, p.ksel * D * 2, qdst, d.r0 * D * 2,
-                                       D * 2, wave, lane);
+                                       D * 2, cw, lane);
       issue_rows<NQ, QT::kChunks, DCH>(p.dog + cb * D, p.ksel * D * 2, odst, d.r0 * D * 2,
-                                       D * 2, wave, lane);
+                                       D * 2, cw, lane);
     }
-    if (wave < 3) {
+    if (cw < 2) {
       const void* src;
-      int nbytes;
-      if (wave == 0) {
+      if (cw == 0) {
         src = d.glb ? (const void*)(p.L2_g + hb * p.ksel) : (const void*)(p.L2_l + hb * p.n);
-      } else if (wave == 1) {
-        src = d.glb ? (const void*)(p.D_g + hb * p.ksel) : (const void*)(p.D_l + hb * p.n);
       } else {
-        src = idx_b;
+        src = d.glb ? (const void*)(p.D_g + hb * p.ksel) : (const void*)(p.D_l + hb * p.n);
       }
-      nbytes = (d.glb ? p.ksel : p.n) * 4;
-      if (wave < 2 || d.glb) issue_row_data(src, nbytes, rdst + wave * kSlot, d.r0 * 4, lane);
+      issue_row_data(src, (d.glb ? p.ksel : p.n) * 4, rdst + cw * kSlot, d.r0 * 4, lane);
+    } else if (cw == 2) {
+      // positions: the selected rows' from idx, a local tile's written here
+      if (d.glb) {
+        issue_row_data(idx_b, p.ksel * 4, rdst + 2 * kSlot, d.r0 * 4, lane);
+      } else if (lane < kQT) {
+        reinterpret_cast<int*>(rdst)[2 * kSlot + lane] = d.r0 + lane;
+      }
     }
   };
 
-  f32x16 acc_dk[DB], acc_dv[DB];
+  bf16x8 kreg[QS], vreg[QS];  // producer: K and V rows of the lane's key
+  f32x16 acc_dk[DB], acc_dv[DB];  // consumer: dK^T, dV^T
+
+  // Producer work for tile t: S^T = K Q^T and dP^T = V dO^T (a lane holds
+  // one query row, l % 32, and 16 keys), then per element
+  // P = exp2(S scale log2e - lse log2e) on the key's range (0 elsewhere)
+  // and dS = P (dP - Dr), packed to bf16 and handed over.
+  auto produce = [&] __device__ (int t, const uint16_t* qc, const uint16_t* oc, const float* rc,
+                                 uint16_t* ps) __attribute__((always_inline)) {
+    // key j is read by row pos iff 0 <= pos - j < wlim (window, or any
+    // earlier key for selected rows). Rows past the end of the tile's list
+    // have zero Q / dO rows and zero row terms, so they add exactly zero.
+    const uint32_t wlim = t < T_gs ? 0x80000000u : (uint32_t)p.W;
+    const uint16_t* qrow = qc + col * QT::kStride + half * 8;
+    const uint16_t* orow = oc + col * QT::kStride + half * 8;
+    f32x16 s_acc = (f32x16){}, p_acc = (f32x16){};
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kreg[s], ld16(qrow + s * 16), s_acc, 0, 0,
+                                                      0);
+      p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vreg[s], ld16(orow + s * 16), p_acc, 0, 0,
+                                                      0);
+    }
+    const float l2 = rc[col];
+    const float dr = rc[kSlot + col];
+    // element e is key kw0 + (e/4)*8 + half*4 + e%4
+    const int rel = reinterpret_cast<const int*>(rc)[2 * kSlot + col] - (key0 + half * 4);
+    uint16_t* pt = ps + pw * kPsPair;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float pv[4], dsv[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int e = j * 4 + w;
+        const bool ok = (uint32_t)(rel - (j * 8 + w)) < wlim;
+        const float x = __builtin_amdgcn_exp2f(fmaf(s_acc[e], p.scale_log2, -l2));
+        pv[w] = ok ? x : 0.0f;
+        dsv[w] = pv[w] * (p_acc[e] - dr);
+      }
+      const int off = ps_off(col, 2 * j + half);
+      *reinterpret_cast<uint2*>(pt + off) =
+          make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]));
+      *reinterpret_cast<uint2*>(pt + kQT * kKW + off) =
+          make_uint2(pack_bf16x2(dsv[0], dsv[1]), pack_bf16x2(dsv[2], dsv[3]));
+    }
+  };
+
+  // Consumer work for a tile: dV^T += dO^T P and dK^T += Q^T dS, contraction
+  // rows 0..15 then 16..31.
+  auto consume = [&] __device__ (const uint16_t* qc, const uint16_t* oc, const uint16_t* ps)
+      __attribute__((always_inline)) {
+    const uint16_t* pt = ps + pw * kPsPair;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const bf16x8 pb = read_tr_ps(pt, hh * 16, lane);
+      const bf16x8 sb = read_tr_ps(pt + kQT * kKW, hh * 16, lane);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        acc_dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            read_tr(oc, QT::kStride, hh * 16, db, lane), pb, acc_dv[db], 0, 0, 0);
+        acc_dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            read_tr(qc, QT::kStride, hh * 16, db, lane), sb, acc_dk[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // Step u: producers work on tile u, consumers on tile u-1 and issue the
+  // loads of tile u+1; buffers named at compile time, three steps per trip.
+  // Each role runs its own loop (so the allocator gives the producer's K, V
+  // operands and the consumer's accumulators the same registers); both
+  // loops pass the same barriers: one before the first step, one per step.
+  if (producer) {
+    // K and V rows of this lane's key: A operands for the whole kernel.
+    const int kk = min(key, p.n - 1);
+    const uint16_t* kr = p.k + b * p.vk.sb + hk * p.vk.sh + (long long)kk * p.vk.st + half * 8;
+    const uint16_t* vr = p.v + b * p.vv.sb + hk * p.vv.sh + (long long)kk * p.vv.st + half * 8;
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      kreg[s] = ld16(kr + s * 16);
+      vreg[s] = ld16(vr + s * 16);
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int u = 0; u <= T; u += 3) {
+      if (u < T) produce(u, Q0, O0, R0, PS0);
+      __syncthreads();
+      if (u + 1 <= T) {
+        if (u + 1 < T) produce(u + 1, Q1, O1, R1, PS1);
+        __syncthreads();
+      }
+      if (u + 2 <= T) {
+        if (u + 2 < T) produce(u + 2, Q2, O2, R2, PS2);
+        __syncthreads();
+      }
+    }
+    return;
+  }
+
 #pragma unroll
   for (int i = 0; i < DB; ++i) {
     acc_dk[i] = (f32x16){};
     acc_dv[i] = (f32x16){};
   }
-
-  // One iteration, scheduled by hand (one wave per SIMD: nothing else hides
-  // latency). Step s of QS issues the S / dP products of tile t+1 for d
-  // slice s, the elementwise slice s-1 of tile t (P, dS of 16/QS of this
-  // lane's 16 elements), and LDS reads 1-2 steps ahead of their use: the
-  // next operands, the next row group, and the transposed dO / Q fragments
-  // of tile t for its dV / dK products, which follow (the last elementwise
-  // slice runs after the first half of them).
-  constexpr int E = 16 / QS;        // elements per slice
-  constexpr int NT = 2 * DB;        // transposed operands per matrix (dV: dO^T, dK: Q^T)
-  constexpr int TPS = (2 * NT + QS - 1) / QS;  // transposed operands read per step
-  auto iter = [&] __device__ (int t, const uint16_t* qc, const uint16_t* oc, const float* rc,
-                              const uint16_t* qn, const uint16_t* on, uint16_t* qm,
-                              uint16_t* om, float* rm, const f32x16& s_in, const f32x16& p_in,
-                              f32x16& s_out, f32x16& p_out) __attribute__((always_inline)) {
-    if (t + 2 < T) issue(t + 2, qm, om, rm);
-    const Desc d = desc(t);
-    // key j is read by row pos iff 0 <= pos - j < wlim (window, or any
-    // earlier key for selected rows). Rows past the end of the tile's list
-    // have zero Q / dO rows and zero row terms, so they add exactly zero.
-    const uint32_t wlim = d.glb ? 0x80000000u : (uint32_t)p.W;
-    const int r0 = d.r0;
-    const bool glb = d.glb;
-    const uint16_t* qrow = qn + col * QT::kStride + half * 8;
-    const uint16_t* orow = on + col * QT::kStride + half * 8;
-    bf16x8 qa[QS], oa[QS];
-    bf16x8 tr[2 * NT];  // [0, NT): dO^T for dV, [NT, 2NT): Q^T for dK; index db*2 + hh
-    float4 gl[4], gd[4];
-    int4 gp[4];
-    auto read_group = [&] __device__ (int j) __attribute__((always_inline)) {
-      const int q0 = j * 8 + half * 4;
-      gl[j] = *reinterpret_cast<const float4*>(rc + q0);
-      gd[j] = *reinterpret_cast<const float4*>(rc + kSlot + q0);
-      // loaded for every tile and blended without a branch (a select here
-      // becomes a branch around the read, which splits the schedule)
-      const int4 pr = *reinterpret_cast<const int4*>(rc + 2 * kSlot + q0);
-      const int gm = glb ? -1 : 0;
-      gp[j] = make_int4((pr.x & gm) | ((r0 + q0) & ~gm), (pr.y & gm) | ((r0 + q0 + 1) & ~gm),
-                        (pr.z & gm) | ((r0 + q0 + 2) & ~gm), (pr.w & gm) | ((r0 + q0 + 3) & ~gm));
-    };
-    auto read_tr_op = [&] __device__ (int o) __attribute__((always_inline)) {
-      const int m = o % NT, db = m >> 1, hh = m & 1;
-      tr[o] = read_tr(o < NT ? oc : qc, QT::kStride, hh * 16, db, lane);
-    };
-    uint32_t pk[8], dk2[8];
-    auto slice = [&] __device__ (int sl) __attribute__((always_inline)) {
-#pragma unroll
-      for (int c2 = 0; c2 < E / 2; ++c2) {
-        const int c = sl * (E / 2) + c2;  // pair index: elements 2c, 2c+1
-        float pr[2], ds[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int e = 2 * c + i;
-          const int j = e >> 2, w = e & 3;
-          const float l2 = w == 0 ? gl[j].x : w == 1 ? gl[j].y : w == 2 ? gl[j].z : gl[j].w;
-          const float dr = w == 0 ? gd[j].x : w == 1 ? gd[j].y : w == 2 ? gd[j].z : gd[j].w;
-          const int pos = w == 0 ? gp[j].x : w == 1 ? gp[j].y : w == 2 ? gp[j].z : gp[j].w;
-          const bool ok = (uint32_t)(pos - key) < wlim;
-          const float x = __builtin_amdgcn_exp2f(fmaf(s_in[e], p.scale_log2, -l2));
-          pr[i] = ok ? x : 0.0f;
-          ds[i] = pr[i] * (p_in[e] - dr);
-        }
-        pk[c] = pack_bf16x2(pr[0], pr[1]);
-        dk2[c] = pack_bf16x2(ds[0], ds[1]);
-        asm volatile("" : "+v"(pk[c]), "+v"(dk2[c]));
-      }
-    };
-    // prologue reads
-    qa[0] = ld16(qrow);
-    oa[0] = ld16(orow);
-    if (QS > 1) {
-      qa[1] = ld16(qrow + 16);
-      oa[1] = ld16(orow + 16);
-    }
-    read_group(0);
-#pragma unroll
-    for (int s = 0; s < QS; ++s) {
-      if (s + 2 < QS) {
-        qa[s + 2] = ld16(qrow + (s + 2) * 16);
-        oa[s + 2] = ld16(orow + (s + 2) * 16);
-      }
-#pragma unroll
-      for (int u = 0; u < TPS; ++u) {
-        const int o = s * TPS + u;
-        if (o < 2 * NT) read_tr_op(o);
-      }
-      // the group first used by slice s+1 (run at step s+2)
-      {
-        const int jn = ((s + 1) * E) >> 2;
-        const int jc = (s * E) >> 2;
-        if (s + 1 < QS && jn != jc && jn < 4) read_group(jn);
-      }
-      s_out = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kreg[s], s ? s_out : (f32x16){}, 0,
-                                                      0, 0);
-      p_out = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[s], vreg[s], s ? p_out : (f32x16){}, 0,
-                                                      0, 0);
-      if (s >= 1) slice(s - 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // dV^T += dO^T P, dK^T += Q^T dS for tile t: keys 0..15 of the
-    // contraction (elements 0..7) first, then the last slice, then 16..31
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      if (hh == 1) {
-        slice(QS - 1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      const bf16x8 pb = __builtin_bit_cast(
-          bf16x8, make_uint4(pk[4 * hh], pk[4 * hh + 1], pk[4 * hh + 2], pk[4 * hh + 3]));
-      const bf16x8 sb = __builtin_bit_cast(
-          bf16x8, make_uint4(dk2[4 * hh], dk2[4 * hh + 1], dk2[4 * hh + 2], dk2[4 * hh + 3]));
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        acc_dv[db] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr[db * 2 + hh], pb, acc_dv[db], 0, 0, 0);
-        acc_dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr[NT + db * 2 + hh], sb,
-                                                             acc_dk[db], 0, 0, 0);
-      }
-    }
+  auto cstep = [&] __device__ (int u, const uint16_t* qp, const uint16_t* op, const uint16_t* psr,
+                               uint16_t* qn, uint16_t* on, float* rn)
+      __attribute__((always_inline)) {
+    if (u + 1 < T) issue(u + 1, qn, on, rn);
+    if (u >= 1) consume(qp, op, psr);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
   };
-
-  // prologue: tiles 0 and 1 land, S and dP of tile 0
-  f32x16 sA, pA, sB, pB;
   issue(0, Q0, O0, R0);
-  if (T > 1) issue(1, Q1, O1, R1);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
-  {
-    const uint16_t* qrow = Q0 + col * QT::kStride + half * 8;
-    const uint16_t* orow = O0 + col * QT::kStride + half * 8;
-    sA = (f32x16){};
-    pA = (f32x16){};
-#pragma unroll
-    for (int s = 0; s < QS; ++s) {
-      sA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld16(qrow + s * 16), kreg[s], sA, 0, 0, 0);
-      pA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld16(orow + s * 16), vreg[s], pA, 0, 0, 0);
-    }
-  }
-  // Three tiles per trip (buffers named at compile time); the products of
-  // tile t+1 in the last iteration read a stale buffer and are never used.
 #pragma unroll 1
-  for (int t = 0; t < T; t += 3) {
-    iter(t, Q0, O0, R0, Q1, O1, Q2, O2, R2, sA, pA, sB, pB);
-    if (t + 1 < T) iter(t + 1, Q1, O1, R1, Q2, O2, Q0, O0, R0, sB, pB, sA, pA);
-    if (t + 2 < T) {
-      iter(t + 2, Q2, O2, R2, Q0, O0, Q1, O1, R1, sA, pA, sB, pB);
-      sA = sB;
-      pA = pB;
-    }
+  for (int u = 0; u <= T; u += 3) {
+    cstep(u, Q2, O2, PS2, Q1, O1, R1);
+    if (u + 1 <= T) cstep(u + 1, Q0, O0, PS0, Q2, O2, R2);
+    if (u + 2 <= T) cstep(u + 2, Q1, O1, PS1, Q0, O0, R0);
   }
 
   if (key >= p.n) return;
@@ -482,7 +470,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(DkdvParams p) {
     }
   }
 }
-
 // =========================================================================
 // dQ
 // =========================================================================
@@ -734,7 +721,8 @@ hipError_t dkdv_t(const Dims& d, const BwdArgs& a, hipStream_t s) {
   p.vk = d.vk;
   p.vv = d.vv;
   p.vo = d.vo;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(p.per_xcd * kNumXcd), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(p.per_xcd * kNumXcd), dim3(kDkdvThreads), 0,
+                     s, p);
   return hipGetLastError();
 }
 
