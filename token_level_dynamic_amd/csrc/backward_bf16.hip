@@ -96,6 +96,27 @@ __device__ __forceinline__ void issue_rows(const uint16_t* base, int nbytes, uin
   }
 }
 
+// Row-load instructions j = part, part + 2, ... (< NQ) of a tile: lane l
+// of instruction j fills LDS slot j*64 + l from byte (glb ? voff_g : voff_l)[i]
+// + soff of [base, base + nbytes) (out of range: zero). The buffer resource
+// is built here, in a device function: its type must not reach the host pass.
+template <int NQ, int NI>
+__device__ __forceinline__ void issue_part(const uint16_t* base, int nbytes, uint16_t* dst,
+                                           const uint32_t (&voff_g)[NI],
+                                           const uint32_t (&voff_l)[NI], bool glb, int soff,
+                                           int part) {
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(base), (short)0, nbytes, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    if (part + 2 * i < NQ) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)(dst + (part + 2 * i) * 512), 16,
+                                               glb ? voff_g[i] : voff_l[i], soff, 0, 0);
+    }
+  }
+}
+
 // Transposing fragment read: rows (a "key" or "query" index of the
 // contraction) r0 + {half*4 + [0,4)} and r0 + 8 + {half*4 + [0,4)} of a
 // row-major LDS tile, d column block `db`; each lane gets 8 values of its
@@ -272,64 +293,88 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(DkdvParams p)
   const int T_gs = G * T_glb;  // selected-row tiles come first
   const int T = T_gs + G * T_loc;
 
-  struct Desc {
-    int h;
-    bool glb;
-    int r0;
-  };
-  auto desc = [&] __device__ (int t) __attribute__((always_inline)) {
-    Desc d;
-    d.glb = t < T_gs;
-    if (d.glb) {
-      d.h = hk * G + t % G;
-      d.r0 = (rb0 + T_glb - 1 - t / G) * kQT;
-    } else {
-      const int u = t - T_gs;
-      d.h = hk * G + u / T_loc;
-      d.r0 = j0 + (u % T_loc) * kQT;
-    }
-    return d;
-  };
-
-  // Buffer loads of tile t, issued by the consumer waves (cw = 0..3): Q and
-  // dO rows (NQ instructions each), then lse, Dr and, for selected rows,
-  // their positions (one instruction each, cw 0..2).
+  // Tile loads, issued by the consumer waves (cw = 0..3) one tile per step
+  // in tile order. Wave cw loads half the row loads of one matrix (Q for
+  // cw 0, 1, dO for cw 2, 3: instructions j = cw % 2, cw % 2 + 2, ...) and
+  // one row-data array (lse: cw 1, positions: cw 2, Dr: cw 3). Everything
+  // that does not change from tile to tile is set up here once; a cursor
+  // walks the tiles (selected-row tiles first, heads innermost, then each
+  // head's local tiles) without divisions.
   const int cw = wave - kPairs;
-  auto issue = [&] __device__ (int t, uint16_t* qdst, uint16_t* odst, float* rdst)
-      __attribute__((always_inline)) {
-    const Desc d = desc(t);
-    const long long hb = (long long)b * p.Hq + d.h;
-    if (!d.glb) {
-      const int qst2 = p.vq.st * 2, ost2 = p.vo.st * 2;
-      issue_rows<NQ, QT::kChunks, DCH>(p.q + b * p.vq.sb + d.h * p.vq.sh,
-                                       ((p.n - 1) * p.vq.st + D) * 2, qdst, d.r0 * qst2, qst2,
-                                       cw, lane);
-      issue_rows<NQ, QT::kChunks, DCH>(p.dout + b * p.vo.sb + d.h * p.vo.sh,
-                                       ((p.n - 1) * p.vo.st + D) * 2, odst, d.r0 * ost2, ost2,
-                                       cw, lane);
+  const bool mat_o = cw >= 2;   // dO rather than Q
+  const int part = cw & 1;
+  constexpr int NI = (NQ + 1) / 2;  // row-load instructions per wave (at most)
+  const View& mv = mat_o ? p.vo : p.vq;
+  const uint16_t* lsrc = (mat_o ? p.dout : p.q) + b * mv.sb + (long long)hk * G * mv.sh;
+  const long long lhead = mv.sh;                        // elements per head
+  const int lbytes = ((p.n - 1) * mv.st + D) * 2;
+  const int lst2 = mv.st * 2;
+  const long long ghead = (long long)p.ksel * D;
+  const uint16_t* gsrc = (mat_o ? p.dog : p.qs) + ((long long)b * p.Hq + hk * G) * ghead;
+  const int gbytes = p.ksel * D * 2;
+  uint32_t voff_l[NI], voff_g[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int slot = (part + 2 * i) * 64 + lane;
+    voff_l[i] = slot_off(slot, QT::kChunks, DCH, lst2);
+    voff_g[i] = slot_off(slot, QT::kChunks, DCH, D * 2);
+  }
+  const float* row_l = (cw == 1 ? p.L2_l : p.D_l) + ((long long)b * p.Hq + hk * G) * p.n;
+  const float* row_g = (cw == 1 ? p.L2_g : p.D_g) + ((long long)b * p.Hq + hk * G) * p.ksel;
+  struct Cursor {
+    int h;     // head within the group
+    int r0;    // first row (position, or index into the selected rows)
+    int left;  // tiles left in this head's run (local) or this row block (selected)
+    bool glb;
+  };
+  Cursor cur;
+  cur.glb = T_gs > 0;
+  cur.h = 0;
+  cur.r0 = cur.glb ? (rb0 + T_glb - 1) * kQT : j0;
+  cur.left = cur.glb ? G : T_loc;
+  int glb_blocks = T_glb;  // selected-row blocks not yet finished
+  auto advance = [&] __device__ () __attribute__((always_inline)) {
+    if (cur.glb) {
+      ++cur.h;
+      if (--cur.left == 0) {
+        cur.h = 0;
+        cur.left = G;
+        cur.r0 -= kQT;
+        if (--glb_blocks == 0) {
+          cur.glb = false;
+          cur.r0 = j0;
+          cur.left = T_loc;
+        }
+      }
     } else {
-      const long long cb = hb * p.ksel;
-      issue_rows<NQ, QT::kChunks, DCH>(p.qs + cb * D, p.ksel * D * 2, qdst, d.r0 * D * 2,
-                                       D * 2, cw, lane);
-      issue_rows<NQ, QT::kChunks, DCH>(p.dog + cb * D, p.ksel * D * 2, odst, d.r0 * D * 2,
-                                       D * 2, cw, lane);
-    }
-    if (cw < 2) {
-      const void* src;
-      if (cw == 0) {
-        src = d.glb ? (const void*)(p.L2_g + hb * p.ksel) : (const void*)(p.L2_l + hb * p.n);
-      } else {
-        src = d.glb ? (const void*)(p.D_g + hb * p.ksel) : (const void*)(p.D_l + hb * p.n);
+      cur.r0 += kQT;
+      if (--cur.left == 0) {
+        ++cur.h;
+        cur.r0 = j0;
+        cur.left = T_loc;
       }
-      issue_row_data(src, (d.glb ? p.ksel : p.n) * 4, rdst + cw * kSlot, d.r0 * 4, lane);
-    } else if (cw == 2) {
+    }
+  };
+  auto issue = [&] __device__ (uint16_t* qdst, uint16_t* odst, float* rdst)
+      __attribute__((always_inline)) {
+    {
+      const uint16_t* src = cur.glb ? gsrc + cur.h * ghead : lsrc + cur.h * lhead;
+      issue_part<NQ, NI>(src, cur.glb ? gbytes : lbytes, mat_o ? odst : qdst,
+                         voff_g, voff_l, cur.glb, cur.r0 * (cur.glb ? D * 2 : lst2), part);
+    }
+    if (cw == 2) {
       // positions: the selected rows' from idx, a local tile's written here
-      if (d.glb) {
-        issue_row_data(idx_b, p.ksel * 4, rdst + 2 * kSlot, d.r0 * 4, lane);
+      if (cur.glb) {
+        issue_row_data(idx_b, p.ksel * 4, rdst + 2 * kSlot, cur.r0 * 4, lane);
       } else if (lane < kQT) {
-        reinterpret_cast<int*>(rdst)[2 * kSlot + lane] = d.r0 + lane;
+        reinterpret_cast<int*>(rdst)[2 * kSlot + lane] = cur.r0 + lane;
       }
+    } else if (cw != 0) {
+      const float* src = cur.glb ? row_g + cur.h * p.ksel : row_l + cur.h * (long long)p.n;
+      issue_row_data(src, (cur.glb ? p.ksel : p.n) * 4, rdst + (cw == 1 ? 0 : kSlot),
+                     cur.r0 * 4, lane);
     }
+    advance();
   };
 
   bf16x8 kreg[QS], vreg[QS];  // producer: K and V rows of the lane's key
@@ -438,12 +483,12 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(DkdvParams p)
   auto cstep = [&] __device__ (int u, const uint16_t* qp, const uint16_t* op, const uint16_t* psr,
                                uint16_t* qn, uint16_t* on, float* rn)
       __attribute__((always_inline)) {
-    if (u + 1 < T) issue(u + 1, qn, on, rn);
+    if (u + 1 < T) issue(qn, on, rn);
     if (u >= 1) consume(qp, op, psr);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
   };
-  issue(0, Q0, O0, R0);
+  issue(Q0, O0, R0);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
 #pragma unroll 1
