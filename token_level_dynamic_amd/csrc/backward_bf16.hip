@@ -40,6 +40,8 @@
 //   the selected rows' global part in place (same stream, so ordered).
 #include "logo_internal.h"
 
+#include <type_traits>
+
 namespace logo {
 namespace {
 
@@ -402,25 +404,44 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(DkdvParams p)
     }
     const float l2 = rc[col];
     const float dr = rc[kSlot + col];
+    const int pos = reinterpret_cast<const int*>(rc)[2 * kSlot + col];
     // element e is key kw0 + (e/4)*8 + half*4 + e%4
-    const int rel = reinterpret_cast<const int*>(rc)[2 * kSlot + col] - (key0 + half * 4);
+    const int rel = pos - (key0 + half * 4);
+    // Rows are in ascending position (row 0, lane 0's, first; rows past the
+    // end of the list read zero everywhere and add zero whatever P is): when
+    // row 0 already reads every key of the pair, and for local rows the
+    // last row still does, no element needs the range test.
+    const int pos0 = __builtin_amdgcn_readfirstlane(pos);
+    const bool all_in = pos0 >= key0 + kKW - 1 &&
+                        (t < T_gs || pos0 + kQT - 1 - key0 < p.W);
     uint16_t* pt = ps + pw * kPsPair;
+    auto body = [&] __device__ (auto masked) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float pv[4], dsv[4];
+      for (int j = 0; j < 4; ++j) {
+        float pv[4], dsv[4];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int e = j * 4 + w;
-        const bool ok = (uint32_t)(rel - (j * 8 + w)) < wlim;
-        const float x = __builtin_amdgcn_exp2f(fmaf(s_acc[e], p.scale_log2, -l2));
-        pv[w] = ok ? x : 0.0f;
-        dsv[w] = pv[w] * (p_acc[e] - dr);
+        for (int w = 0; w < 4; ++w) {
+          const int e = j * 4 + w;
+          const float x = __builtin_amdgcn_exp2f(fmaf(s_acc[e], p.scale_log2, -l2));
+          if (decltype(masked)::value) {
+            const bool ok = (uint32_t)(rel - (j * 8 + w)) < wlim;
+            pv[w] = ok ? x : 0.0f;
+          } else {
+            pv[w] = x;
+          }
+          dsv[w] = pv[w] * (p_acc[e] - dr);
+        }
+        const int off = ps_off(col, 2 * j + half);
+        *reinterpret_cast<uint2*>(pt + off) =
+            make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]));
+        *reinterpret_cast<uint2*>(pt + kQT * kKW + off) =
+            make_uint2(pack_bf16x2(dsv[0], dsv[1]), pack_bf16x2(dsv[2], dsv[3]));
       }
-      const int off = ps_off(col, 2 * j + half);
-      *reinterpret_cast<uint2*>(pt + off) =
-          make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]));
-      *reinterpret_cast<uint2*>(pt + kQT * kKW + off) =
-          make_uint2(pack_bf16x2(dsv[0], dsv[1]), pack_bf16x2(dsv[2], dsv[3]));
+    };
+    if (all_in) {
+      body(std::integral_constant<bool, false>());
+    } else {
+      body(std::integral_constant<bool, true>());
     }
   };
 
