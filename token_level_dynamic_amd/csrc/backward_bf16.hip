@@ -688,19 +688,37 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqParams p) {
       }
       uint32_t dk2[8];
       const int key0 = t * kKeys + kb * 32;
+      // Every row of the wave reads every key of the block: no range test
+      // (rows past the end compute garbage only for their own dq row, which
+      // is never stored).
+      const bool all_in = wpos_lo >= key0 + 31 && (GLOBAL || key0 >= wpos_hi - p.W + 1);
+      if (all_in) {
 #pragma unroll
-      for (int e2 = 0; e2 < 8; ++e2) {
-        float ds[2];
+        for (int e2 = 0; e2 < 8; ++e2) {
+          float ds[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int e = 2 * e2 + i;
-          const int key = key0 + (e >> 2) * 8 + half * 4 + (e & 3);
-          bool ok = row_ok && key <= pos;
-          if (!GLOBAL) ok = ok && key >= pos - p.W + 1;
-          const float pr = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[e], p.scale_log2, -lse2)) : 0.0f;
-          ds[i] = pr * (pacc[e] - dr);
+          for (int i = 0; i < 2; ++i) {
+            const int e = 2 * e2 + i;
+            ds[i] = __builtin_amdgcn_exp2f(fmaf(sacc[e], p.scale_log2, -lse2)) * (pacc[e] - dr);
+          }
+          dk2[e2] = pack_bf16x2(ds[0], ds[1]);
         }
-        dk2[e2] = pack_bf16x2(ds[0], ds[1]);
+      } else {
+#pragma unroll
+        for (int e2 = 0; e2 < 8; ++e2) {
+          float ds[2];
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int e = 2 * e2 + i;
+            const int key = key0 + (e >> 2) * 8 + half * 4 + (e & 3);
+            bool ok = row_ok && key <= pos;
+            if (!GLOBAL) ok = ok && key >= pos - p.W + 1;
+            const float pr =
+                ok ? __builtin_amdgcn_exp2f(fmaf(sacc[e], p.scale_log2, -lse2)) : 0.0f;
+            ds[i] = pr * (pacc[e] - dr);
+          }
+          dk2[e2] = pack_bf16x2(ds[0], ds[1]);
+        }
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
