@@ -665,7 +665,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the library runs on one GPU and has no multi-GPU path "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
         return 2
 
