@@ -80,38 +80,131 @@ def effective_flops(w, idx: np.ndarray) -> dict:
     return {"local": local, "global": glob, "total": local + glob}
 
 
-def cpu_baseline(w, inp, idx, budget_s: float = 15.0, seed: int = 0) -> dict:
-    """Times the CPU oracle on a random sample of the layer's rows."""
+# The CPU oracle's worker processes: forked in main() before the GPU is
+# touched, so they inherit the inputs and the oracle's selection and hold no
+# GPU state. Each runs NumPy with one BLAS thread.
+_CPU = {}
+
+
+def _cpu_worker_init() -> None:
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:  # threadpoolctl missing: the environment variables stand
+        pass
+
+
+def _cpu_rows(rows):
     import oracle
+    c = _CPU
+    r = oracle.forward_rows(c["q"], c["k"], c["v"], c["gate"], c["window"], c["rho"], rows,
+                            selection=c["selection"])
+    return rows, r["o_rows"]
+
+
+def cpu_cores() -> int:
+    """Cores the oracle may use: this process's CPU affinity, at most 16
+    (one GPU's share of its host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def start_cpu_oracle(w, inp):
+    """Selection by the oracle (timed: it is part of the oracle's forward),
+    then the worker pool. Call before any GPU work."""
+    import multiprocessing as mp
+    import oracle
+    t0 = time.perf_counter()
+    sel = oracle.select_queries(inp.gate, w.rho)
+    _CPU.update(q=inp.q, k=inp.k, v=inp.v, gate=inp.gate, window=w.window, rho=w.rho,
+                selection=sel, select_s=time.perf_counter() - t0)
+    cores = cpu_cores()
+    _CPU["pool"] = mp.get_context("fork").Pool(cores, initializer=_cpu_worker_init)
+    _CPU["cores"] = cores
+
+
+def _host_info() -> dict:
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
-    except Exception:  # threadpoolctl missing: numpy's BLAS threads unknown
-        threads = 1
+        blas = [f"{x.get('internal_api')} {x.get('version')}" for x in threadpool_info()
+                if x.get("user_api") == "blas"]
+        blas = ", ".join(blas) or None
+    except Exception:
+        pass
+    return {"cpu_model": model, "numpy": np.__version__, "blas": blas}
+
+
+def cpu_baseline(w, o_dev, budget_s: float = 15.0, seed: int = 0, chunk: int = 16) -> dict:
+    """The CPU oracle (oracle.forward_rows, row by row in float64) over a
+    uniform seeded sample of the layer's rows (b, h, i), spread over the
+    worker pool for about budget_s seconds of wall time. The rate is the
+    sample's effective FLOPs (4 d per (query, key) pair of each row's local
+    window and, for selected rows, its causal prefix) over the wall time; the
+    whole layer's time is extrapolated from it by the layer's pair count
+    (plus the one selection). The sampled rows are also compared with the
+    GPU's output of the timed run (o_dev)."""
+    pool, cores = _CPU["pool"], _CPU["cores"]
+    mask = _CPU["selection"][0]
     r = np.random.default_rng(seed)
-    sel = np.zeros((w.B, w.n), dtype=bool)
-    for b in range(w.B):
-        sel[b, idx[b]] = True
-    flops = 0.0
-    n_rows = n_glob = 0
+    pending = []
+    done = []
     t0 = time.perf_counter()
-    # the selection over the whole sequence is part of every oracle call
-    while time.perf_counter() - t0 < budget_s:
-        chunk = [(int(r.integers(0, w.B)), int(r.integers(0, w.Hq)), int(r.integers(0, w.n)))
-                 for _ in range(64)]
-        oracle.forward_rows(inp.q, inp.k, inp.v, inp.gate, w.window, w.rho, chunk)
-        for b, h, i in chunk:
-            flops += 4.0 * w.d * min(w.window, i + 1)
-            if sel[b, i]:
-                flops += 4.0 * w.d * (i + 1)
-                n_glob += 1
-        n_rows += len(chunk)
-    dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{n_rows} rows (b, h, i) drawn uniformly with seed {seed} from the "
-                      f"{w.name} layer ({n_glob} of them selected, so also global), one "
-                      f"oracle.forward_rows call per 64 rows, {dt:.1f} s wall"}
+    while time.perf_counter() - t0 < budget_s or pending:
+        while time.perf_counter() - t0 < budget_s and len(pending) < 2 * cores:
+            rows = [(int(r.integers(0, w.B)), int(r.integers(0, w.Hq)), int(r.integers(0, w.n)))
+                    for _ in range(chunk)]
+            pending.append(pool.apply_async(_cpu_rows, (rows,)))
+        still = []
+        for a in pending:
+            if a.ready():
+                done.append(a.get())
+            else:
+                still.append(a)
+        pending = still
+        time.sleep(0.002)
+    wall = time.perf_counter() - t0
+    pool.terminate()
+    rows = [x for rs, _ in done for x in rs]
+    ref = np.concatenate([o for _, o in done])
+    pairs = sum(min(w.window, i + 1) + (i + 1 if mask[b, i] else 0) for b, _, i in rows)
+    rate = 4.0 * w.d * pairs / wall                            # flops per second
+    layer_pairs = band_pairs(w) * w.B * w.Hq + w.Hq * float(
+        sum((np.flatnonzero(mask[b]) + 1).sum() for b in range(w.B)))
+    layer_s = 4.0 * w.d * layer_pairs / rate + _CPU["select_s"]
+    import torch
+    bi = torch.tensor([x[0] for x in rows], device=o_dev.device)
+    hi = torch.tensor([x[1] for x in rows], device=o_dev.device)
+    ii = torch.tensor([x[2] for x in rows], device=o_dev.device)
+    got = o_dev[bi, hi, ii].double().cpu().numpy()
+    err = float(np.abs(got - ref).max())
+    nsel = sum(int(mask[b, i]) for b, _, i in rows)
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(rows)} rows (b, h, i) drawn uniformly with seed {seed} from the "
+                      f"{w.name} layer ({nsel} selected, so also global), {chunk} rows per "
+                      f"task over {cores} worker processes (one BLAS thread each), "
+                      f"{wall:.1f} s wall; the selection computed once",
+            "extrapolated": {"layer_s": float(f"{layer_s:.4g}"),
+                             "how": "the whole layer's (query, key) pairs at the sample's rate, "
+                                    "plus the selection's time"},
+            "host": _host_info(),
+            "parity": {"rows": len(rows), "max_abs": err,
+                       "tolerance": 2e-2 if w.dtype == "bf16" else 1e-4,
+                       "against": "the GPU output of the timed run"}}
 
 
 def load_traffic(workload: str, current_hash: str, key: str = "global_bytes_per_launch"):
@@ -248,6 +341,96 @@ def gemm_ceiling(torch) -> int:
             out[f"{n}^3 {name}"] = {"ms": round(ms, 4), "TFLOP/s": round(2 * n ** 3 / ms / 1e9, 1)}
     print(json.dumps({"gemm_ceiling": out, "kernel": "torch.matmul bf16 (hipBLASLt)",
                       "published_dense_peak_TFLOP/s": BF16_PEAK_TFLOPS}))
+    return 0
+
+
+def ceilings(torch) -> int:
+    """Throughput ceilings of one compute unit from the microbenchmarks in
+    csrc/ceiling.hip (libceiling.so): each kernel records the shader clock and
+    the 100 MHz reference clock per workgroup, so rates come out per clock
+    cycle (and the clock under that load as a frequency). Two resident
+    256-thread workgroups per CU (2 waves per SIMD, as the attention kernels
+    run) unless the row says otherwise."""
+    import ctypes
+    from token_level_dynamic_amd.build import CEILING_LIB
+    lib = ctypes.CDLL(CEILING_LIB)
+    lib.ceiling_launch.restype = ctypes.c_int
+    lib.ceiling_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong,
+                                   ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    # kind: name, work per wave per iteration, unit
+    kinds = {0: ("mfma_32x32x16_bf16", 4 * 32768.0, "flop"),
+             1: ("ds_read_b128", 8 * 1024.0, "B"),
+             2: ("ds_read_b64_tr_b16", 8 * 512.0, "B"),
+             3: ("v_exp_f32", 8 * 64.0, "exp"),
+             4: ("mfma + 0.5 KiB LDS per product", 4 * 32768.0, "flop"),
+             5: ("mfma + 1 KiB LDS per product", 4 * 32768.0, "flop"),
+             6: ("mfma + 2 KiB LDS per product", 4 * 32768.0, "flop"),
+             7: ("V tile reads, stride 144", 32 * 512.0, "B"),
+             8: ("V tile reads, stride 160", 32 * 512.0, "B"),
+             9: ("V tile reads, swizzled 128", 32 * 512.0, "B"),
+             10: ("K tile reads, stride 136", 16 * 1024.0, "B"),
+             11: ("K tile reads, swizzled 128", 16 * 1024.0, "B")}
+    out = {}
+    for kind, (name, per_iter, unit) in kinds.items():
+        for wg_per_cu in (1, 2, 4):
+            blocks = cus * wg_per_cu
+            iters = 20000 if kind in (0, 4, 5, 6) else 4000 if kind >= 7 else 40000
+            sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+            clk = torch.zeros(blocks * 4, dtype=torch.int64, device="cuda")
+            rc = lib.ceiling_launch(kind, blocks, 10, sink.data_ptr(), clk.data_ptr(), None, 0,
+                                    stream.cuda_stream)
+            if rc != 0:
+                raise SystemExit(f"ceiling kernel {kind} failed: hip error {rc}")
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc = lib.ceiling_launch(kind, blocks, iters, sink.data_ptr(), clk.data_ptr(), None, 0,
+                                    stream.cuda_stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise SystemExit(f"ceiling kernel {kind} failed: hip error {rc}")
+            ms = e0.elapsed_time(e1)
+            c = clk.view(blocks, 4).cpu().numpy().astype(np.float64)
+            cyc = float(np.median(c[:, 1] - c[:, 0]))
+            ref = float(np.median(c[:, 3] - c[:, 2]))
+            ghz = cyc / ref * 0.1 if ref > 0 else None
+            total = per_iter * iters * 4 * blocks / (ms * 1e-3)
+            # per CU and shader clock cycle, at the clock the kernel ran at
+            per_cu_clk = total / (cus * ghz * 1e9) if ghz else float("nan")
+            out[f"{name} | {wg_per_cu} WG/CU"] = {
+                f"{unit}_per_clk_per_cu": round(per_cu_clk, 1),
+                "clock_GHz": round(ghz, 3) if ghz else None,
+                f"{unit}_per_s_chip": total, "ms": round(ms, 3)}
+            print(json.dumps({name: out[f"{name} | {wg_per_cu} WG/CU"],
+                              "wg_per_cu": wg_per_cu}), flush=True)
+    # HBM: streaming 16-byte reads over 4 GiB of random bytes, 4 passes
+    nbytes = 4 << 30
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda")
+    for wg_per_cu in (2, 4, 8):
+        blocks = cus * wg_per_cu
+        sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+        lib.ceiling_launch(12, blocks, 1, sink.data_ptr(), None, src.data_ptr(), nbytes,
+                           stream.cuda_stream)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(4):
+            rc = lib.ceiling_launch(12, blocks, 1, sink.data_ptr(), None, src.data_ptr(), nbytes,
+                                    stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if rc != 0:
+            raise SystemExit(f"stream read kernel failed: hip error {rc}")
+        gbs = 4 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        out[f"hbm stream read 4 GiB | {wg_per_cu} WG/CU"] = {"GB_per_s": round(gbs, 1)}
+        print(json.dumps({"hbm stream read": round(gbs, 1), "wg_per_cu": wg_per_cu}), flush=True)
+    del src
+    print(json.dumps({"ceilings": out, "cus": cus,
+                      "source": "token_level_dynamic_amd/csrc/ceiling.hip"}))
     return 0
 
 
@@ -659,6 +842,9 @@ def main() -> int:
         ap.add_argument("--" + opt, default=None)
     ap.add_argument("--gemm-ceiling", action="store_true",
                     help="time a plain bf16 GEMM on random and on zero operands and exit")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="run the matrix-core, LDS and exp2 throughput microbenchmarks "
+                         "(libceiling.so) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (read N, write N "
                          "bytes) so HBM counters can be scaled to bytes")
@@ -681,12 +867,23 @@ def main() -> int:
         return copy_calibration(torch)
     if args.gemm_ceiling:
         return gemm_ceiling(torch)
+    if args.ceilings:
+        return ceilings(torch)
 
     from token_level_dynamic_amd._lib import LIB_PATH
     if not os.path.exists(LIB_PATH):
         import __graft_entry__
         __graft_entry__.build()
     T.lib()
+
+    w = get_workload(args.workload)
+    if args.rho is not None:
+        w = w.with_(rho=args.rho)
+    inp = None
+    if args.mode == "forward":
+        inp = make_inputs(w, args.seed)
+        if not args.no_cpu_baseline:
+            start_cpu_oracle(w, inp)     # before the GPU is touched
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
@@ -695,10 +892,8 @@ def main() -> int:
         return decode_bench(args, torch, T)
     if args.mode == "varlen":
         return varlen_bench(args, torch, T)
-    w = get_workload(args.workload)
-    if args.rho is not None:
-        w = w.with_(rho=args.rho)
-    inp = make_inputs(w, args.seed)
+    if inp is None:
+        inp = make_inputs(w, args.seed)
     if w.dtype == "bf16":
         digest = input_sha256(inp.q_bits, inp.k_bits, inp.v_bits, inp.gate)
     else:
@@ -774,6 +969,10 @@ def main() -> int:
         "effective_flops": F["total"],
         "stage_ms_avg": {s: round(x, 4) for s, x in avg.items() if x is not None},
         "per_step_ms": per_step,
+        "timing": {"primary": "warm: value and ms_per_step are the K timed steps run back to "
+                              "back (the benchmark's contract); per_step_ms.cold times each "
+                              "forward after a 1 GiB write that evicts L2 and the MALL",
+                   "cold_median_ms": per_step["cold"]["median_ms"]},
         "roofline": {
             "kernel": f"attn_bf16_kernel ({dom} branch, fused epilogue)",
             "bound": "mfma",
@@ -787,7 +986,8 @@ def main() -> int:
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, inp, idx, budget_s=args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(w, buf["o"], budget_s=args.cpu_budget)
+        result["parity"] = result["cpu_baseline"]["parity"]
     print(json.dumps(result), flush=True)
     return 0
 

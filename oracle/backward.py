@@ -60,7 +60,7 @@ import numpy as np
 from . import logo as F
 
 __all__ = ["row_grad", "row_lse", "backward", "dq_rows", "dgate_at", "forward_stats",
-           "dkdv_tail"]
+           "dkdv_tail", "dkdv_keys"]
 
 
 def row_lse(qrow, keys, scale: float) -> float:
@@ -234,4 +234,49 @@ def dkdv_tail(q, k, v, gate, do, window: int, rho: float, b: int, hk: int, j_fro
                                         g[b, i] * e, scale)
                 dk[:i + 1 - j_from] += gk[j_from:]
                 dv[:i + 1 - j_from] += gv[j_from:]
+    return dk, dv
+
+
+def dkdv_keys(q, k, v, gate, do, window: int, rho: float, b: int, hk: int, j_lo: int,
+              j_hi: int, rows: Optional[Iterable[int]] = None,
+              scale: Optional[float] = None):
+    """dk, dv [j_hi - j_lo, d] of keys j_lo..j_hi-1 of (b, kv head hk): the
+    sum over the kv head's query heads and over query positions ``rows``
+    (default: every position) of each row's gradient on those keys, both
+    branches. A row's local branch reads L(i), its global branch (selected
+    rows only) [0, i]; rows that read none of the keys add nothing. Summing
+    the results over a partition of the positions gives the keys' full
+    gradients, so the earliest keys, which every selected row reads, can be
+    computed in parts."""
+    F._check_shapes(q, k, v)
+    B, Hq, n, d = q.shape
+    Hkv = k.shape[1]
+    scale = F.default_scale(d) if scale is None else scale
+    mask, _, _ = F.select_queries(gate, rho)
+    g = F.sigmoid(gate)
+    G = Hq // Hkv
+    dk = np.zeros((j_hi - j_lo, d))
+    dv = np.zeros((j_hi - j_lo, d))
+    positions = range(n) if rows is None else [int(i) for i in rows]
+    for i in positions:
+        if i < j_lo:
+            continue                       # a row reads no key after it
+        lo = max(0, i - window + 1)
+        local_hits = lo < j_hi              # the window reaches the range
+        if not local_hits and not mask[b, i]:
+            continue
+        for h in range(hk * G, hk * G + G):
+            e = np.asarray(do[b, h, i], np.float64)
+            if local_hits:
+                _, _, gk, gv = row_grad(q[b, h, i], k[b, hk, lo:i + 1], v[b, hk, lo:i + 1], e,
+                                        scale)
+                a, z = max(lo, j_lo), min(i + 1, j_hi)
+                dk[a - j_lo:z - j_lo] += gk[a - lo:z - lo]
+                dv[a - j_lo:z - j_lo] += gv[a - lo:z - lo]
+            if mask[b, i]:
+                _, _, gk, gv = row_grad(q[b, h, i], k[b, hk, :i + 1], v[b, hk, :i + 1],
+                                        g[b, i] * e, scale)
+                z = min(i + 1, j_hi)
+                dk[:z - j_lo] += gk[j_lo:z]
+                dv[:z - j_lo] += gv[j_lo:z]
     return dk, dv

@@ -215,17 +215,20 @@ def forward(q, k, v, gate, window: int, rho: float, scale: Optional[float] = Non
 
 
 def forward_rows(q, k, v, gate, window: int, rho: float,
-                 rows: Iterable[Sequence[int]], scale: Optional[float] = None) -> dict:
+                 rows: Iterable[Sequence[int]], scale: Optional[float] = None,
+                 selection: Optional[Tuple[np.ndarray, np.ndarray, np.ndarray]] = None) -> dict:
     """The layer's output on chosen rows only, for inputs too large to do whole.
 
     Rows are independent given the keys and values, so each (b, h, i) in
-    `rows` is computed exactly as in `forward`. The selection is always
-    computed for the whole sequence. Returns the selection and an array
-    o_rows [len(rows), d] float64 in the order given."""
+    `rows` is computed exactly as in `forward`. The selection is computed for
+    the whole sequence, or passed in as `selection` (the (mask, idx, rank)
+    that ``select_queries(gate, rho)`` returned, when many row sets share
+    it). Returns the selection and an array o_rows [len(rows), d] float64 in
+    the order given."""
     _check_shapes(q, k, v)
     d = q.shape[3]
     scale = default_scale(d) if scale is None else scale
-    mask, idx, rank = select_queries(gate, rho)
+    mask, idx, rank = select_queries(gate, rho) if selection is None else selection
     g = sigmoid(gate)
     rows = [tuple(int(x) for x in r) for r in rows]
     out = np.empty((len(rows), d), dtype=np.float64)

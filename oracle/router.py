@@ -22,10 +22,11 @@ Readings taken where the pages are silent:
   here are synthetic).
 * The budget controller, ties, combine and both branches are those of
   ``oracle/logo.py``.
-* Where floating point decides the selection, both sides decide in the same
-  precision: the routed forward can take the logits a caller computed (in
-  float32, as the GPU does) for the selection and the combine, while the
-  logits themselves are compared separately.
+* The logits are computed in float64; the selection, an integer decision
+  taken by floating point, is made on those logits rounded to float32 (the
+  precision the logits have on the device, where gates are float32), and the
+  combine uses the sigmoid of the float64 logits. The oracle never takes a
+  logit from anywhere else.
 
 Parity: pinned in ``tests/test_oracle_router.py`` (closed forms, an
 independent torch formulation, consistency with the pinned forward).
@@ -55,21 +56,23 @@ def router_logits(o_local: np.ndarray, w: np.ndarray, bias: float) -> np.ndarray
 
 
 def forward_routed(q, k, v, w, bias: float, window: int, rho: float,
-                   scale: Optional[float] = None, gate_used: Optional[np.ndarray] = None) -> dict:
-    """Local branch for every row, router logits from it, selection on the
-    logits (or on ``gate_used`` when given: the caller's float32 logits),
-    global branch on the selected rows, combine with sigmoid of the same
-    logits. Returns o, gate (the fp64 logits), the selection, o_local."""
+                   scale: Optional[float] = None) -> dict:
+    """Local branch for every row, router logits from it (float64), the
+    selection on those logits rounded to float32, global branch on the
+    selected rows, combine with the sigmoid of the float64 logits. Returns o,
+    gate (float64 logits), gate32 (the float32 logits the selection used),
+    the selection, o_local and o_global."""
     F._check_shapes(q, k, v)
     d = q.shape[3]
     scale = F.default_scale(d) if scale is None else scale
     o_local = F.local_attention(q, k, v, window, scale)
     gate = router_logits(o_local, w, bias)
-    g_sel = gate.astype(np.float32) if gate_used is None else np.asarray(gate_used, np.float32)
-    mask, idx, rank = F.select_queries(g_sel, rho)
+    gate32 = gate.astype(np.float32)
+    mask, idx, rank = F.select_queries(gate32, rho)
     o_global = F.global_attention(q, k, v, idx, scale)
-    o = F.combine(o_local, o_global, rank, g_sel)
-    return {"o": o, "gate": gate, "mask": mask, "idx": idx, "rank": rank, "o_local": o_local}
+    o = F.combine(o_local, o_global, rank, gate)
+    return {"o": o, "gate": gate, "gate32": gate32, "mask": mask, "idx": idx, "rank": rank,
+            "o_local": o_local, "o_global": o_global}
 
 
 def router_logits_at(q, k, v, w, bias: float, window: int,

@@ -70,6 +70,45 @@ def run_unfused(p, q, k, v, gate):
             "o_global": o_global, "o": o}
 
 
+def parity_rows(w, idx, seed, heads=None):
+    """Rows (b, h, i) of a full-size workload that the oracle recomputes: the
+    band edge (positions 0 .. W + 64), the last 256 positions, every selected
+    position in three 2048-position windows (the start, the middle and the
+    end of the sequence), and a seeded 1 % sample of positions. Every query
+    head of kv group 0 gets all of them (or the heads given); the 1 % sample
+    also goes to one seeded random head of the whole layer per position, so
+    every head is covered."""
+    r = np.random.default_rng(seed)
+    G = w.Hq // w.Hkv
+    heads = list(range(G)) if heads is None else list(heads)
+    rows = set()
+    n = w.n
+    for b in range(w.B):
+        pos = set(range(0, min(n, w.window + 65)))
+        pos |= set(range(max(0, n - 256), n))
+        sel = idx[b] if idx.shape[1] else np.zeros(0, np.int64)
+        for lo in (0, max(0, n // 2 - 1024), max(0, n - 2048)):
+            pos |= {int(x) for x in sel[(sel >= lo) & (sel < lo + 2048)]}
+        sample = r.choice(n, size=max(1, n // 100), replace=False)
+        pos |= {int(x) for x in sample}
+        for i in pos:
+            for h in heads:
+                rows.add((b, h, i))
+        for i in sample:
+            rows.add((b, int(r.integers(0, w.Hq)), int(i)))
+    return sorted(rows)
+
+
+def gather_rows(o, rows):
+    """Output rows (b, h, i) of a [B, H, n, d] device tensor, as float64 on
+    the host, in the order given."""
+    import torch as _t
+    bi = _t.tensor([x[0] for x in rows], device=o.device)
+    hi = _t.tensor([x[1] for x in rows], device=o.device)
+    ii = _t.tensor([x[2] for x in rows], device=o.device)
+    return o[bi, hi, ii].double().cpu().numpy()
+
+
 def host(t):
     return t.float().cpu().numpy() if t.dtype in (torch.bfloat16, torch.float16) \
         else t.cpu().numpy()

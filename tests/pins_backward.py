@@ -177,6 +177,15 @@ def pin_bwd_rows_match(F, BW):
         dk, dv = BW.dkdv_tail(q, k, v, gate, do, 5, 0.35, b, hk, j_from)
         assert np.allclose(dk, full["dk"][b, hk, j_from:], atol=1e-13)
         assert np.allclose(dv, full["dv"][b, hk, j_from:], atol=1e-13)
+    # any key range, from all rows at once or summed over a partition of them
+    for b, hk, j_lo, j_hi in ((0, 0, 0, 4), (1, 1, 3, 11), (0, 1, 0, 25), (1, 0, 24, 25)):
+        dk, dv = BW.dkdv_keys(q, k, v, gate, do, 5, 0.35, b, hk, j_lo, j_hi)
+        assert np.allclose(dk, full["dk"][b, hk, j_lo:j_hi], atol=1e-13)
+        assert np.allclose(dv, full["dv"][b, hk, j_lo:j_hi], atol=1e-13)
+        parts = [BW.dkdv_keys(q, k, v, gate, do, 5, 0.35, b, hk, j_lo, j_hi, rows=r)
+                 for r in (range(0, 9), range(9, 17), range(17, 25))]
+        assert np.allclose(sum(p[0] for p in parts), dk, atol=1e-13)
+        assert np.allclose(sum(p[1] for p in parts), dv, atol=1e-13)
     pos = [(b, i) for b in range(2) for i in range(25)]
     dg = BW.dgate_at(q, k, v, gate, do, 0.35, pos)
     assert np.allclose(dg, full["dgate"].reshape(-1), atol=1e-13)

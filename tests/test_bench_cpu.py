@@ -73,3 +73,23 @@ def test_input_digest_follows_the_seed():
     assert da != bench.input_sha256(c.q_bits, c.k_bits, c.v_bits, c.gate)
     assert da != bench.input_sha256(a.k_bits, a.q_bits, a.v_bits, a.gate)
     assert len(da) == 16
+
+
+def test_cpu_baseline_protocol():
+    # the oracle leg: a pool of worker processes over the host's cores, the
+    # selection computed once, a labelled extrapolation, host details, and
+    # the sampled rows compared with an output (here the oracle's own, so
+    # the difference is zero)
+    import torch
+    import oracle
+    from workloads import get_workload, make_inputs
+    w = get_workload("gqa32k", B=1, Hq=2, Hkv=1, n=300, window=40, rho=0.25)
+    inp = make_inputs(w, 0)
+    ref = oracle.forward(inp.q, inp.k, inp.v, inp.gate, w.window, w.rho)
+    bench.start_cpu_oracle(w, inp)
+    out = bench.cpu_baseline(w, torch.from_numpy(ref["o"]), budget_s=1.0, chunk=8)
+    assert out["kind"] == "oracle" and out["unit"] == "TFLOP/s" and out["value"] > 0
+    assert out["cores"] == bench.cpu_cores() >= 1
+    assert out["extrapolated"]["layer_s"] > 0
+    assert out["parity"]["rows"] >= 8 and out["parity"]["max_abs"] < 1e-12
+    assert "cpu_model" in out["host"] and "blas" in out["host"]

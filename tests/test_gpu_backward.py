@@ -5,9 +5,12 @@ and the gradients dq, dk, dv, dgate on the same seeded inputs and upstream
 gradient. Bound for the gradients (no page states one; derived from the
 arithmetic): max |err| <= tol * max(1, max |ref|) per tensor, tol = 2e-2
 with bf16 inputs (the forward's bf16 bound; the matrix-core operands P, dS
-and g*dout are rounded to bf16, relative 2^-9 each) and 1e-4 with float32
+and g*dout are rounded to bf16, unit roundoff 2^-8 each) and 1e-4 with float32
 inputs. Full-size cases check sampled dq rows, dgate at sampled positions,
-exact dk/dv of the last keys of each sequence, and sum rules over all keys."""
+exact dk/dv of the last keys of each sequence, exact dk/dv of the first 64
+keys of one (batch, kv head) (read by every selected row's global branch:
+the largest sums; the oracle's rows are spread over a process pool), and sum
+rules over all keys."""
 import numpy as np
 import pytest
 import torch
@@ -15,6 +18,7 @@ import torch
 import oracle
 import oracle.backward as BW
 import token_level_dynamic_amd as T
+import oracle_pool as OP
 from gpu_util import dev, ensure_built, host, problem, say, to_dev
 from workloads import get_workload, make_dout, make_inputs
 
@@ -171,6 +175,24 @@ def _check_full(w, label):
         e, bound = _err(f"dv tail (b={b}, kv={hk})", host(bw["dv"][b, hk, w.n - tail:]), rv,
                         TOL[w.dtype])
         assert e <= bound
+    # exact dk/dv of the first keys of (b, kv head) 0: every local row whose
+    # window reaches them and every selected row, in parts summed here
+    head = 64
+    b, hk = 0, 0
+    pos = sorted(set(range(0, min(w.n, head + w.window - 1))) | {int(i) for i in idx[b]})
+    with OP.SharedInputs(q=inp.q, k=inp.k, v=inp.v, gate=inp.gate, do=dvals) as sh:
+        parts = OP.map_chunks(sh, "backward.dkdv_keys",
+                              lambda c: ("@q", "@k", "@v", "@gate", "@do", w.window, w.rho, b,
+                                         hk, 0, head, list(c)),
+                              pos, chunk=64)
+    rk = sum(x[0] for x in parts)
+    rv = sum(x[1] for x in parts)
+    e, bound = _err(f"dk first {head} keys (b={b}, kv={hk}, {len(pos)} rows)",
+                    host(bw["dk"][b, hk, :head]), rk, TOL[w.dtype])
+    assert e <= bound
+    e, bound = _err(f"dv first {head} keys (b={b}, kv={hk})", host(bw["dv"][b, hk, :head]), rv,
+                    TOL[w.dtype])
+    assert e <= bound
     # sum rules over every key of each (b, kv head): sum_j dk_j = 0 and
     # sum_j dv_j = sum over the group's rows of dout_i (1 + [i in S] g_i)
     g = 1.0 / (1.0 + np.exp(-inp.gate.astype(np.float64)))

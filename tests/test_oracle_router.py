@@ -60,15 +60,36 @@ def pin_router_constant_values(RM):
 
 
 def pin_router_consistent_with_forward(RM):
-    """Given its own logits, the routed forward is the pinned forward."""
+    """Given its own logits, the routed forward is the pinned forward (which
+    selects on the float32 rounding of the logits it is given and squashes
+    them as given)."""
     q, k, v, w, bias = _inputs(5)
     out = RM.forward_routed(q, k, v, w, bias, 6, 0.4)
-    ref = F.forward(q, k, v, out["gate"].astype(np.float32), 6, 0.4)
+    assert np.array_equal(out["gate32"], out["gate"].astype(np.float32))
+    ref = F.forward(q, k, v, out["gate"], 6, 0.4)
     assert np.array_equal(out["idx"], ref["idx"])
     assert np.allclose(out["o"], ref["o"], atol=1e-12)
     g = RM.router_logits_at(q, k, v, w, bias, 6, [(0, 0), (1, 18), (1, 7)])
     assert np.allclose(g, [out["gate"][0, 0], out["gate"][1, 18], out["gate"][1, 7]],
                        atol=1e-12)
+
+
+def pin_router_decides_in_float32(RM):
+    """Values that differ from a constant per kv head by amounts far below
+    float32 resolution give float64 logits that differ only there: rounded to
+    float32 they tie, so the selection is the first k positions (ties to the
+    lower position), whatever order the float64 logits have."""
+    q, k, v, w, bias = _inputs(8, B=1)
+    n = q.shape[2]
+    v[:] = v[:, :, :1, :]
+    v[0, :, :, 0] += 1e-13 * np.arange(n)[::-1][None, :]   # later tokens: smaller
+    w[:] = np.abs(w)
+    out = RM.forward_routed(q, k, v, w, bias, n, 0.25)
+    g = out["gate"][0]
+    assert np.unique(out["gate32"][0]).size == 1      # one float32 value
+    assert np.unique(g).size > 1                      # distinct float64 values
+    kk = math.ceil(0.25 * n)
+    assert np.array_equal(out["idx"][0], np.arange(kk))
 
 
 def pin_router_linear(RM):
@@ -82,7 +103,7 @@ def pin_router_linear(RM):
 
 
 PINS = [pin_router_torch, pin_router_zero_weights, pin_router_constant_values,
-        pin_router_consistent_with_forward, pin_router_linear]
+        pin_router_consistent_with_forward, pin_router_decides_in_float32, pin_router_linear]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -120,3 +141,23 @@ def _logits_transposed_weights(o_local, w, bias):
 def test_router_mutant_is_caught(mut, monkeypatch):
     monkeypatch.setattr(R, "router_logits", mut)
     assert _some_pin_fails()
+
+
+def test_router_float64_decision_is_caught():
+    """A routed oracle that selected on the float64 logits (ordering them in
+    float64) would pick the largest float64 values instead of the float32
+    ties' lower positions."""
+    import types
+
+    def forward_routed_f64(q, k, v, w, bias, window, rho, scale=None):
+        out = R.forward_routed(q, k, v, w, bias, window, rho, scale)
+        g = out["gate"]
+        B, n = g.shape
+        kk = F.target_count(rho, n)
+        idx = np.stack([np.sort(np.argsort(-g[b], kind="stable")[:kk]) for b in range(B)])
+        return dict(out, idx=idx.astype(np.int32))
+
+    mutant = types.SimpleNamespace(forward_routed=forward_routed_f64,
+                                   router_logits_at=R.router_logits_at)
+    with pytest.raises(AssertionError):
+        pin_router_decides_in_float32(mutant)

@@ -14,7 +14,10 @@ from typing import Optional, Tuple
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblogo.so")
+# the in-tree build; LOGO_LIBRARY names another build of the same library
+# (for example to compare two builds on one machine)
+LIB_PATH = os.environ.get("LOGO_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "liblogo.so")
 
 LOGO_OK = 0
 LOGO_ERR_INVALID_ARG = 1

@@ -20,6 +20,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblogo.so")
+# throughput-ceiling microbenchmarks for the benchmark's --ceilings mode: a
+# library of their own, not linked into liblogo.so
+CEILING_SRC = "ceiling.hip"
+CEILING_LIB = os.path.join(PKG, "libceiling.so")
 
 SOURCES = ["abi.cpp", "select.hip", "attn_bf16.hip", "attn_f32.hip", "combine.hip",
            "backward_prep.hip", "backward_bf16.hip", "backward_f32.hip", "router.hip",
@@ -49,19 +53,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library. Returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link the shared libraries. Returns the path
+    of the attention library."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + [CEILING_SRC]
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], CEILING_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CEILING_LIB}")
     return LIB
 
 
