@@ -275,21 +275,35 @@ def record_traffic(args) -> int:
     ws = COPY_BYTES / (1024.0 * _pick(_counter_means(args.copy_write, "WRITE_SIZE"), "add"))
     fm = _counter_means(args.fwd_fetch, "FETCH_SIZE")
     wm = _counter_means(args.fwd_write, "WRITE_SIZE")
-    g = "attn_bf16_kernel<128, true, 3, false, false>"
-    lo = "attn_bf16_kernel<128, false, 1, false, false>"
-    gr, gw = _pick(fm, g) * 1024 * fs, _pick(wm, g) * 1024 * ws
-    data = {"gqa32k": {
-        "source_hash": kernel_source_hash(),
-        "global_bytes_per_launch": round(gr + gw),
-        "global_read_bytes": round(gr),
-        "global_write_bytes": round(gw),
-        "local_bytes_per_launch": round((_pick(fm, lo) * fs + _pick(wm, lo) * ws) * 1024),
-        "fetch_scale": round(fs, 5),
-        "write_scale": round(ws, 5),
-        "note": "FETCH_SIZE/WRITE_SIZE KiB per dispatch (rocprofv3 --pmc, one counter per run; "
-                "mean of the warm-up and the two timed dispatches) times 1024 times the "
-                "copy-kernel scale; written by bench.py --record-traffic, see "
-                "hbm_traffic_gqa32k.md"}}
+    note = ("FETCH_SIZE/WRITE_SIZE KiB per dispatch (rocprofv3 --pmc, one counter per run; "
+            "mean of the warm-up and the two timed dispatches) times 1024 times the "
+            "copy-kernel scale; written by bench.py --record-traffic, see "
+            "hbm_traffic_gqa32k.md")
+    fz = "attn_bf16_fused_kernel<128>"
+    if any(fz in k for k in fm):
+        # the single-launch forward: one kernel for both branches
+        fr, fw = _pick(fm, fz) * 1024 * fs, _pick(wm, fz) * 1024 * ws
+        data = {"gqa32k": {
+            "source_hash": kernel_source_hash(),
+            "fused_bytes_per_launch": round(fr + fw),
+            "fused_read_bytes": round(fr),
+            "fused_write_bytes": round(fw),
+            "fetch_scale": round(fs, 5),
+            "write_scale": round(ws, 5),
+            "note": note}}
+    else:
+        g = "attn_bf16_kernel<128, true, 3, false, false>"
+        lo = "attn_bf16_kernel<128, false, 1, false, false>"
+        gr, gw = _pick(fm, g) * 1024 * fs, _pick(wm, g) * 1024 * ws
+        data = {"gqa32k": {
+            "source_hash": kernel_source_hash(),
+            "global_bytes_per_launch": round(gr + gw),
+            "global_read_bytes": round(gr),
+            "global_write_bytes": round(gw),
+            "local_bytes_per_launch": round((_pick(fm, lo) * fs + _pick(wm, lo) * ws) * 1024),
+            "fetch_scale": round(fs, 5),
+            "write_scale": round(ws, 5),
+            "note": note}}
     if args.train_fetch and args.train_write:
         tf = _counter_means(args.train_fetch, "FETCH_SIZE")
         tw = _counter_means(args.train_write, "WRITE_SIZE")
@@ -941,11 +955,18 @@ def main() -> int:
     tflops = F["total"] / (ms_per_step * 1e-3) / 1e12
     avg = {s: (stage_ms[j] / stage_n[j] if stage_n[j] else None)
            for j, s in enumerate(T.STAGES)}
-    dom = "global" if F["global"] >= F["local"] else "local"
+    if avg.get("fused"):
+        # one launch computes both branches: its FLOPs are the layer's
+        dom, dom_flops = "fused", F["total"]
+        kname = "attn_bf16_fused_kernel (both branches, one launch)"
+    else:
+        dom = "global" if F["global"] >= F["local"] else "local"
+        dom_flops = F[dom]
+        kname = f"attn_bf16_kernel ({dom} branch, fused epilogue)"
     dom_ms = avg[dom]
-    dom_flops = F[dom]
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms else None
-    traffic = load_traffic(w.name, kernel_source_hash()) if dom == "global" else None
+    traffic = (load_traffic(w.name, kernel_source_hash(), f"{dom}_bytes_per_launch")
+               if dom in ("global", "fused") else None)
 
     result = {
         "metric": METRIC,
@@ -974,7 +995,7 @@ def main() -> int:
                               "forward after a 1 GiB write that evicts L2 and the MALL",
                    "cold_median_ms": per_step["cold"]["median_ms"]},
         "roofline": {
-            "kernel": f"attn_bf16_kernel ({dom} branch, fused epilogue)",
+            "kernel": kname,
             "bound": "mfma",
             "achieved": round(achieved, 2) if achieved else None,
             "peak": BF16_PEAK_TFLOPS,

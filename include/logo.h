@@ -107,7 +107,10 @@ int64_t logo_target_count(double rho, int64_t n);
  * B*Hkv*ceil(ceil(k/32)*Hq/Hkv / 4)) splits each workgroup's keys into
  * s = min(8, ceil(512 / workgroups), floor(ceil(n/64) / 4)) ranges when
  * that is 2 or more, and then adds s*B*Hq*k*(d+4)*4 bytes of float32
- * partials, rounded up to 256. Writes 0 when nothing is needed. Errors:
+ * partials, rounded up to 256. A bf16 problem with k > 0 that does not
+ * split and whose B*Hkv is a multiple or a divisor of 8 runs the single
+ * launch (see logo_forward) and adds B*(n-k)*4 bytes (the unselected
+ * positions), rounded up to 256. Writes 0 when nothing is needed. Errors:
  * LOGO_ERR_INVALID_ARG / _UNSUPPORTED as for logo_forward. */
 logo_status logo_workspace_size(const logo_problem* p, size_t* bytes);
 
@@ -149,10 +152,15 @@ logo_status logo_combine(const logo_problem* p, const float* o_local,
  * selection (mask, idx, rank). `workspace` must hold logo_workspace_size
  * bytes (may be NULL when that is 0). Output equals logo_select_queries ->
  * logo_local_attn -> logo_global_attn_sparse -> logo_combine up to float32
- * rounding order; where a bf16 problem's global branch is split into key
- * ranges (see logo_workspace_size), each range also rounds its
- * probabilities to bf16 against its own running maximum, so the two then
- * agree to the bf16 parity tolerance rather than bit for bit. */
+ * rounding order. Two bf16 forms take another order and then agree with
+ * those calls to the bf16 parity tolerance rather than bit for bit: a
+ * global branch split into key ranges (see logo_workspace_size), where each
+ * range rounds its probabilities to bf16 against its own running maximum;
+ * and the single launch (see logo_workspace_size for when it applies),
+ * where one kernel does every row: a selected row walks its causal prefix
+ * once, from the diagonal down, its window's keys first, so the running
+ * state after the window is its local output and at the end its global
+ * output, and the unselected rows do the local branch alone. */
 logo_status logo_forward(const logo_problem* p, const void* q, const void* k,
                          const void* v, const float* gate, void* o,
                          uint8_t* mask, int32_t* idx, int32_t* rank,
@@ -351,7 +359,8 @@ const char* logo_last_error(void);
  * logo_forward_routed and logo_decode_step. logo_profile_end() waits for those events and writes,
  * per stage (0 select, 1 local, 2 global, 3 combine, 4 backward row terms and
  * dgate, 5 backward dk/dv, 6 backward dq, 7 router logits, 8 decode: chunk
- * partials and their reduction), the summed milliseconds
+ * partials and their reduction, 9 both attention branches in one launch),
+ * the summed milliseconds
  * and the number of launches into arrays of `n_stages` entries. */
 logo_status logo_profile_begin(void);
 logo_status logo_profile_end(double* stage_ms, int64_t* stage_launches,

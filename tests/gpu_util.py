@@ -120,11 +120,25 @@ def say(msg):
 
 def global_splits(p):
     """True when logo_forward splits this problem's global branch into key
-    ranges: its workspace then holds more than the selected rows' float32
-    local outputs and the (b, kv head) queue counters."""
+    ranges (the rule include/logo.h states for logo_workspace_size: a bf16
+    problem with fewer than 512 row-block workgroups, at least 2 ranges)."""
     kk = T.logo_target_count(p.rho, p.n)
+    if p.dtype != 1 or kk == 0:
+        return False
+    wg = p.B * p.Hkv * -(-(-(-kk // 32) * (p.Hq // p.Hkv)) // 4)
+    if wg >= 512:
+        return False
+    s = min(8, -(-512 // wg), (-(-p.n // 64)) // 4)
+    return s >= 2
 
-    def r256(x):
-        return (x + 255) // 256 * 256
-    base = r256(p.B * p.Hq * kk * p.d * 4) + (r256(4 * p.B * p.Hkv) if kk else 0)
-    return p.dtype == 1 and T.logo_workspace_size(p) > base
+
+def single_launch(p):
+    """True when logo_forward runs its single-launch form (include/logo.h:
+    bf16, something selected, no key-range split, and B * Hkv a multiple or
+    a divisor of 8): selected rows then compute both branches in one walk,
+    so the output agrees with the four-call path to the parity tolerance
+    rather than bit for bit."""
+    kk = T.logo_target_count(p.rho, p.n)
+    U = p.B * p.Hkv
+    return (p.dtype == 1 and kk > 0 and p.d in (64, 128) and not global_splits(p)
+            and (U % 8 == 0 or 8 % U == 0))

@@ -110,7 +110,9 @@ def test_workspace_checks(L):
     assert L.logo_workspace_size(ctypes.byref(p), ctypes.byref(size)) == 0
     k = T.logo_target_count(0.2, 100)
     want = 2 * 4 * k * 128 * 4           # float32 local outputs of the selected rows
-    assert size.value == (want + 255) // 256 * 256 + 256   # + B*Hkv int32 queues
+    # + B*Hkv int32 queues + the unselected positions (single-launch forward:
+    # bf16, no key-range split, B*Hkv = 4 divides the 8 XCDs)
+    assert size.value == (want + 255) // 256 * 256 + 256 + _round(2 * (100 - k) * 4)
     assert _forward(L, p, ws=None) == _lib.LOGO_ERR_WORKSPACE
     assert _forward(L, p, ws=FAKE, ws_bytes=size.value - 1) == _lib.LOGO_ERR_WORKSPACE
     # rho = 0 selects nothing: no workspace needed
@@ -144,12 +146,18 @@ def test_workspace_split_partials(L):
     k = T.logo_target_count(0.2, 4000)
     base = _round(2 * 4 * k * 64 * 4) + 256
     assert _ws_bytes(L, n=4000, d=64) == base + _round(8 * 2 * 4 * k * (64 + 4) * 4)
-    # two key tiles: too few to split; float32: never split
-    assert _ws_bytes(L, n=100) == _round(2 * 4 * 20 * 128 * 4) + 256
+    # two key tiles: too few to split (single launch: + unselected positions);
+    # float32: never split, never a single launch
+    assert _ws_bytes(L, n=100) == _round(2 * 4 * 20 * 128 * 4) + 256 + _round(2 * 80 * 4)
     assert _ws_bytes(L, n=1000, dtype=0) == _round(2 * 4 * 200 * 128 * 4) + 256
-    # 32K positions, 16 query / 4 kv heads: 1640 workgroups, no split
+    # 32K positions, 16 query / 4 kv heads: 1640 workgroups, no split;
+    # B * Hkv = 8: the single launch
     k = T.logo_target_count(0.2, 32768)
-    assert _ws_bytes(L, n=32768, Hq=16, Hkv=4) == _round(2 * 16 * k * 128 * 4) + 256
+    assert _ws_bytes(L, n=32768, Hq=16, Hkv=4) == (_round(2 * 16 * k * 128 * 4) + 256
+                                                  + _round(2 * (32768 - k) * 4))
+    # B * Hkv = 6 does not map onto the 8 XCDs: two launches, no list
+    k = T.logo_target_count(0.2, 32768)
+    assert _ws_bytes(L, n=32768, B=3, Hq=8, Hkv=2) == _round(3 * 8 * k * 128 * 4) + 256
 
 
 def test_empty_problems_enqueue_nothing(L):

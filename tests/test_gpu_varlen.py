@@ -8,7 +8,7 @@ import torch
 import oracle
 import oracle.varlen as VL
 import token_level_dynamic_amd as T
-from gpu_util import dev, ensure_built, global_splits, say
+from gpu_util import dev, ensure_built, global_splits, say, single_launch
 from workloads import VARLEN_WORKLOADS, make_varlen_inputs
 
 pytestmark = pytest.mark.gpu
@@ -103,9 +103,9 @@ def test_single_example_equals_forward():
     T.logo_forward(p, q, k, v, g, buf["o"], buf["mask"], buf["idx"], buf["rank"],
                    buf["workspace"])
     torch.cuda.synchronize()
-    if global_splits(p):
+    if global_splits(p) or single_launch(p):
         err = float((got["o_dev"].float() - buf["o"].float()).abs().max())
-        say(f"  split forward vs packed max_abs={err:.3e}")
+        say(f"  split or single-launch forward vs packed max_abs={err:.3e}")
         assert err <= TOL["bf16"]
     else:
         assert torch.equal(got["o_dev"].view(torch.int16), buf["o"].view(torch.int16))

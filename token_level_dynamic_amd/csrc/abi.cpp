@@ -154,8 +154,14 @@ size_t split_bytes(const logo::Dims& d) {
   if (d.dtype != LOGO_BF16) return 0;
   return (logo::attn_bf16_split_floats(d) * sizeof(float) + 255) / 256 * 256;
 }
+// and, where the single-launch fused forward applies, the unselected
+// positions of each sequence (the rows its local-only work gathers)
+size_t nidx_bytes(const logo::Dims& d) {
+  if (!logo::attn_bf16_fused_ok(d)) return 0;
+  return ((size_t)d.B * (d.n - d.k) * sizeof(int32_t) + 255) / 256 * 256;
+}
 size_t scratch_bytes(const logo::Dims& d) {
-  return scratch_only_bytes(d) + queue_bytes(d) + split_bytes(d);
+  return scratch_only_bytes(d) + queue_bytes(d) + split_bytes(d) + nidx_bytes(d);
 }
 
 // ---- kernel timing --------------------------------------------------------
@@ -337,9 +343,17 @@ logo_status logo_forward(const logo_problem* p, const void* q, const void* k, co
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
+  // bf16 problems with enough work and a (b, kv head) count that maps onto
+  // the XCDs: selection (also listing the unselected positions), then one
+  // launch for every row (selected rows compute both branches)
+  const bool fused = logo::attn_bf16_fused_ok(d);
+  int32_t* nidx = fused ? reinterpret_cast<int32_t*>(
+                              static_cast<char*>(workspace) + scratch_only_bytes(d) +
+                              queue_bytes(d) + split_bytes(d))
+                        : nullptr;
   {
     StageTimer tm(0, s);
-    e = logo::launch_select(d, gate, mask, d.k > 0 ? idx : nullptr, rank, s);
+    e = logo::launch_select(d, gate, mask, d.k > 0 ? idx : nullptr, rank, s, nidx);
   }
   if (e != hipSuccess) return hip_fail(e, "select launch");
   logo::AttnArgs a{};
@@ -352,6 +366,12 @@ logo_status logo_forward(const logo_problem* p, const void* q, const void* k, co
   a.out_f32 = static_cast<float*>(workspace);
   a.scratch = static_cast<const float*>(workspace);
   a.out_io = o;
+  if (fused) {
+    StageTimer tm(9, s);
+    e = logo::launch_attn_bf16_fused(d, a, nidx, s);
+    if (e != hipSuccess) return hip_fail(e, "fused attention launch");
+    return LOGO_OK;
+  }
   if (d.k > 0 && d.dtype == LOGO_BF16) {
     a.sched = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + scratch_only_bytes(d));
     if (split_bytes(d) > 0)

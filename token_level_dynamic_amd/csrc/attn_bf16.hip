@@ -139,79 +139,42 @@ __device__ __forceinline__ void issue_tile(const uint16_t* base, int nbytes, uin
   }
 }
 
+// One row block of one (b, kv head): up to 4 units (32 rows x one query
+// head each, one per wave) that share K/V tiles.
+//
+// EPI: 0 LocalAll, 1 LocalFused, 2 GlobalAll, 3 GlobalFused, 4 LocalRouted,
+// 5 GlobalRouted (see Epi), and the two halves of the single-launch fused
+// forward:
+//   6 (global rows, gathered through idx): the selected rows' local branch
+//     and global branch from one walk over their causal prefix. The walk
+//     goes from the diagonal down to key 0. Keys inside a row's window
+//     [i-W+1, i] come first, so after the tile holding the window's lowest
+//     key the running output is that row's local output: it is normalised
+//     and parked in the scratch rows (this lane's row only). The walk then
+//     goes on over the keys below the window with the same running state,
+//     which ends as the global output over [0, i]. A tile holding some
+//     row's window edge is walked twice with complementary masks (window
+//     keys, then the keys below it). Writes o = o_local + sigmoid(g) o_global.
+//   7 (unselected rows, gathered through idx = the unselected positions,
+//     ksel = their count): the local branch only; writes o.
 // SEG: packed examples (p.seg_start set): keys before a row's example start
 // are masked and tile ranges start at the example; positions read from idx
 // are clamped and ranks beyond the scratch rows ignored, so inconsistent
 // example offsets cannot address outside the buffers. Compiled separately so
 // the plain path carries none of it.
-template <int D, bool GLOBAL, int EPI, bool SEG, bool QUEUE>
-__global__ __launch_bounds__(kThreads, 2)
-__attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
+template <int D, bool GLOBAL, int EPI, bool SEG>
+__device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, int split,
+                                           uint16_t* K0, uint16_t* K1, uint16_t* V0,
+                                           uint16_t* V1) {
   using SM = Smem<D>;
-  // Four distinct LDS objects, so the compiler can tell that reads of one
-  // buffer do not wait on buffer loads still landing in another.
-  __shared__ __attribute__((aligned(16))) uint16_t K0[SM::kElems];
-  __shared__ __attribute__((aligned(16))) uint16_t K1[SM::kElems];
-  __shared__ __attribute__((aligned(16))) uint16_t V0[SM::vElems];
-  __shared__ __attribute__((aligned(16))) uint16_t V1[SM::vElems];
-
-  // ---- which tile -------------------------------------------------------
-  const int bid = blockIdx.x;
-  const int Lx = (bid % kNumXcd) * p.per_xcd + bid / kNumXcd;
-  if (Lx >= p.total_wg * p.nsplit) return;
-  // split key ranges (fused global branch of a small problem): workgroup
-  // Lx takes key range `split` of row block L
-  const int split = Lx % p.nsplit;
-  const int L = Lx / p.nsplit;
-  // Queued global launches (p.sched_count set): each (b, kv head) unit has a
-  // queue of its row blocks, heaviest first (the last rows; for packed
-  // examples the order the schedule kernel built). A workgroup takes blocks
-  // from its home unit's queue (the unit its XCD holds, so K/V stay in that
-  // L2) and, once that queue is empty, from the other units' in turn, until
-  // every queue is empty: an XCD whose units have less work (a selection
-  // that leans late in one sequence and early in another) goes on with
-  // the others' remaining blocks instead of idling. An empty queue stays
-  // empty, so every block is taken exactly once. Otherwise the workgroup
-  // does the one block its index names. Always compiled for the routed and
-  // the packed-example global branches; the fused branch has both forms
-  // and takes the queue when fewer (b, kv head) units than XCDs make the
-  // static order split a unit's blocks over XCDs by index (longest first:
-  // one XCD of the pair gets most of the work). With one unit per XCD and a
-  // balanced selection the queue measured 3.5 % slower (its codegen and
-  // atomics); it saves 2.5 % on the routed branch's router-driven selection
-  // and 38 % on a selection as skewed as latest tokens in one sequence,
-  // earliest in the other.
-  constexpr bool kQueue = GLOBAL && (EPI == 5 || SEG || QUEUE);
-  const bool queued = kQueue && p.sched_count != nullptr;
-  __shared__ int taken[2];
-#pragma unroll 1
-  for (int iter = 0;; ++iter) {
-  int unit_bh = L / p.wg_per_unit;             // b * Hkv + kv head
-  int w = L % p.wg_per_unit;
-  if (queued) {
-    if (threadIdx.x == 0) {
-      const int nu = p.B * p.Hkv;
-      int u = unit_bh;
-      int r = atomicAdd(p.sched_count + u, 1);
-      for (int tries = 1; r >= p.wg_per_unit && tries < nu; ++tries) {
-        u = u + 1 < nu ? u + 1 : 0;
-        r = atomicAdd(p.sched_count + u, 1);
-      }
-      taken[0] = u;
-      taken[1] = r;
-    }
-    __syncthreads();
-    if (taken[1] >= p.wg_per_unit) return;  // every queue is empty
-    unit_bh = taken[0];
-    w = p.sched_perm ? p.sched_perm[taken[1]] : p.wg_per_unit - 1 - taken[1];
-  } else {
-    if (iter > 0) return;
-    if (GLOBAL) w = p.wg_per_unit - 1 - w;      // longest prefix first
-  }
+  // rows come from a position list (idx) rather than being 0..n-1
+  constexpr bool GATHER = GLOBAL || EPI == 7;
+  // the walk goes from the diagonal down to key 0
+  constexpr bool BACKWARD = EPI == 6;
   const int b = unit_bh / p.Hkv;
   const int hk = unit_bh % p.Hkv;
   const int G = p.Hq / p.Hkv;
-  const int R = GLOBAL ? p.ksel : p.n;          // rows per (b, head)
+  const int R = GATHER ? p.ksel : p.n;          // rows per (b, head)
 
   const int tid = threadIdx.x;
   // uniform in the wave: what derives from it (rows, heads, key ranges)
@@ -230,7 +193,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   const int h = hk * G + (wave_on ? u : u_last) % G;
 
   auto row_pos = [&] __device__ (int r) __attribute__((always_inline)) {
-    if (!GLOBAL) return r;
+    if (!GATHER) return r;
     const int ix = p.idx[(size_t)b * p.ksel + r];
     return SEG ? min(max(ix, 0), p.n - 1) : ix;
   };
@@ -260,6 +223,10 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
     t_lo += split * per;
     t_hi = min(t_hi, t_lo + per - 1);
   }
+  // EPI 6: the lowest window key of this lane's row and the wave's range of
+  // them (rows ascend, so the first and last rows bound it)
+  const int lb = pos - p.W + 1;
+  const int wlb_lo = wpos_lo - p.W + 1, wlb_hi = wpos_hi - p.W + 1;
 
   // This (b, kv head)'s K and V, read through bounds-checked buffer loads:
   // keys past the end read as zero (they only occur in tiles masked per
@@ -329,14 +296,21 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   for (int i = 0; i < DB; ++i) acc_o[i] = (f32x16){};
   float m_run = kNegInit;   // running row max, log2 units
   float l_run = 0.0f;       // this lane's half of the row sum
+  bool snapped = false;     // EPI 6: this lane's local output is parked
 
+  // Mask modes of one tile: the branch's own range (local window or causal
+  // prefix), or (EPI 6) the keys below the row's window.
+  constexpr int kOwn = 0, kBelow = 1;
   auto is_active = [&] __device__ (int t) __attribute__((always_inline)) {
     const int key0 = t * kKeys;
     return wave_on && key0 <= wkey_hi && key0 + kKeys - 1 >= wkey_lo;
   };
-  auto is_full = [&] __device__ (int t) __attribute__((always_inline)) {
+  // every element of the tile is read by every row of the wave (no mask)
+  auto is_full = [&] __device__ (int t, int mode) __attribute__((always_inline)) {
     const int key0 = t * kKeys;
     if (SEG && key0 < wss_hi) return false;  // a row's example starts inside or after the tile
+    if (EPI == 6 && mode == kBelow) return key0 + kKeys - 1 < wlb_lo;
+    if (EPI == 6) return key0 >= wlb_hi && key0 + kKeys - 1 <= wpos_lo;
     if (GLOBAL) return key0 + kKeys - 1 <= wpos_lo;
     return key0 >= wpos_hi - p.W + 1 && key0 + kKeys - 1 <= wpos_lo;
   };
@@ -382,13 +356,19 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
     asm volatile("" : "+v"(pk), "+v"(l_run));
     return pk;
   };
-  auto mask_block = [&] __device__ (int key0, f32x16& s) __attribute__((always_inline)) {
+  auto mask_block = [&] __device__ (int key0, f32x16& s, int mode)
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int key = key0 + (e >> 2) * 8 + half * 4 + (e & 3);
-      bool ok = key <= pos;
-      if (SEG) ok = ok && key >= ss;
-      if (!GLOBAL) ok = ok && key >= pos - p.W + 1;
+      bool ok;
+      if (EPI == 6 && mode == kBelow) {
+        ok = key < lb;                      // below the window (so also causal)
+      } else {
+        ok = key <= pos;
+        if (SEG) ok = ok && key >= ss;
+        if (!GLOBAL || EPI == 6) ok = ok && key >= lb;
+      }
       s[e] = ok ? s[e] : -INFINITY;
     }
   };
@@ -403,9 +383,9 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   //   QK(kb0) | QK(kb1) + softmax(kb0) | PV(kb0) + softmax(kb1) | PV(kb1)
   // so half of the MFMAs carry softmax VALU work of the other block in their
   // shadow; the second wave of the SIMD covers the rest.
-  auto tile = [&] __device__ (int t, const uint16_t* ks, const uint16_t* vs)
+  auto tile = [&] __device__ (int t, const uint16_t* ks, const uint16_t* vs, int mode)
       __attribute__((always_inline)) {
-    const bool full = __builtin_amdgcn_readfirstlane(is_full(t));
+    const bool full = __builtin_amdgcn_readfirstlane(is_full(t, mode));
     const int key0 = t * kKeys;
     f32x16 sc0, sc1;
     uint32_t pk0[8], pk1[8];   // bf16 probability pairs of blocks 0 and 1
@@ -425,7 +405,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
 #pragma unroll
     for (int s = 0; s < QS; ++s)
       kf1[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow1 + s * 16));
-    if (!full) mask_block(key0, sc0);
+    if (!full) mask_block(key0, sc0, mode);
     const float alpha0 = block_max(sc0);
     __builtin_amdgcn_sched_barrier(0);
     // QK(kb1), 8 pairs of block 0 spread over its QS MFMAs
@@ -441,7 +421,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     rescale(alpha0);
-    if (!full) mask_block(key0 + 32, sc1);
+    if (!full) mask_block(key0 + 32, sc1, mode);
     const float alpha1 = block_max(sc1);
     __builtin_amdgcn_sched_barrier(0);
     // PV(kb0), 8 pairs of block 1 spread over its 2*DB MFMAs
@@ -477,33 +457,74 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
           0, 0, 0);
     }
   };
+  // EPI 6: rows whose window's lowest key lies in tile t have now seen
+  // exactly their window: park acc / l (float32) in the row's scratch row.
+  const size_t head_row = (size_t)(b * p.Hq + h);
+  auto park_local = [&] __device__ (int t) __attribute__((always_inline)) {
+    const int key0 = t * kKeys;
+    const bool here = row_ok && lb >= key0 && lb < key0 + kKeys;
+    const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
+                                                       __float_as_uint(l_run), false, false);
+    const float inv = 1.0f / (__uint_as_float(lsw[0]) + __uint_as_float(lsw[1]));
+    if (here) {
+      float* const dst = p.out_f32 + (head_row * p.ksel + r_lane) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<float4*>(dst + db * 32 + j * 8 + half * 4) =
+              make_float4(acc_o[db][j * 4 + 0] * inv, acc_o[db][j * 4 + 1] * inv,
+                          acc_o[db][j * 4 + 2] * inv, acc_o[db][j * 4 + 3] * inv);
+      }
+    }
+    snapped = snapped || here;
+  };
+  auto compute = [&] __device__ (int t, const uint16_t* ks, const uint16_t* vs)
+      __attribute__((always_inline)) {
+    if (!__builtin_amdgcn_readfirstlane(is_active(t))) return;
+    if (EPI != 6) {
+      tile(t, ks, vs, kOwn);
+      return;
+    }
+    const int key0 = t * kKeys;
+    // window keys of some row in this tile; some row's window edge in it;
+    // keys below some row's window in it
+    if (key0 + kKeys - 1 >= wlb_lo) {
+      tile(t, ks, vs, kOwn);
+      if (key0 <= wlb_hi) park_local(t);
+    }
+    if (key0 < wlb_hi) tile(t, ks, vs, kBelow);
+  };
 
-  // ---- main loop: tile t computes from one buffer pair while tile t+1
-  // lands in the other. The loop is unrolled by two so every LDS access
-  // names its buffer at compile time.
-  auto step = [&] __device__ (int t, const uint16_t* ks, const uint16_t* vs, uint16_t* kn,
+  // ---- main loop: tile i of the walk computes from one buffer pair while
+  // tile i+1 lands in the other. The loop is unrolled by two so every LDS
+  // access names its buffer at compile time.
+  const int nt = t_hi - t_lo + 1;
+  auto tile_at = [&] __device__ (int i) __attribute__((always_inline)) {
+    return BACKWARD ? t_hi - i : t_lo + i;
+  };
+  auto step = [&] __device__ (int i, const uint16_t* ks, const uint16_t* vs, uint16_t* kn,
                               uint16_t* vn) __attribute__((always_inline)) {
-    if (t + 1 <= t_hi) issue_kv(t + 1, kn, vn);
-    if (__builtin_amdgcn_readfirstlane(is_active(t))) tile(t, ks, vs);
+    if (i + 1 < nt) issue_kv(tile_at(i + 1), kn, vn);
+    compute(tile_at(i), ks, vs);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
   };
-  if (t_lo <= t_hi) {
-    issue_kv(t_lo, K0, V0);
+  if (nt > 0) {
+    issue_kv(tile_at(0), K0, V0);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
   }
 #pragma unroll 1
-  for (int t = t_lo; t <= t_hi; t += 2) {
-    step(t, K0, V0, K1, V1);
-    if (t + 1 <= t_hi) step(t + 1, K1, V1, K0, V0);
+  for (int i = 0; i < nt; i += 2) {
+    step(i, K0, V0, K1, V1);
+    if (i + 1 < nt) step(i + 1, K1, V1, K0, V0);
   }
 
   // ---- epilogue ----------------------------------------------------------
   const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
                                                      __float_as_uint(l_run), false, false);
   const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
-  const size_t head_row = (size_t)(b * p.Hq + h);
   if (EPI == 3 && p.nsplit > 1 && row_ok) {
     // partial of one key range: unnormalised o, running max (log2 units),
     // row sum; a merge kernel combines the ranges and applies the gate
@@ -523,23 +544,21 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   if (p.lse_out && half == 0)
     p.lse_out[head_row * R + (GLOBAL ? r_lane : pos)] = (m_run + __log2f(l_tot)) * kLn2;
   uint16_t* const orow = p.out_io + b * p.vo.sb + h * p.vo.sh + (long long)pos * p.vo.st;
-  // EPI: 0 LocalAll, 1 LocalFused, 2 GlobalAll, 3 GlobalFused, 4 LocalRouted,
-  // 5 GlobalRouted
   int rk = -1;
   if (EPI == 1) {
     rk = p.rank[(size_t)b * p.n + pos];
     if (SEG && rk >= p.ksel) rk = -1;  // never address past the scratch rows
   }
   float sig = 0.0f;
-  if (EPI == 3 || EPI == 5) sig = 1.0f / (1.0f + expf(-p.gate[(size_t)b * p.n + pos]));
+  if (EPI == 3 || EPI == 5 || EPI == 6) sig = 1.0f / (1.0f + expf(-p.gate[(size_t)b * p.n + pos]));
   // Everything the stores combine with is loaded first: the compiler cannot
   // tell these buffers from the outputs, so a load placed after a store
   // would wait for every store before it. EPI 3/5: the row's local output;
-  // EPI 4: the head's router weights, for this lane's half of
-  // <router_w[h], o_local row>.
-  constexpr bool kPre = EPI == 3 || EPI == 4 || EPI == 5;
+  // EPI 6: the parked local output (rows that parked one); EPI 4: the head's
+  // router weights, for this lane's half of <router_w[h], o_local row>.
+  constexpr bool kPre = EPI == 3 || EPI == 4 || EPI == 5 || EPI == 6;
   float4 pre[kPre ? DB * 4 : 1];
-  if (kPre) {
+  if (kPre && (EPI != 6 || snapped)) {
     const float* src = EPI == 4 ? p.router_w + (size_t)h * D
                        : EPI == 5 ? p.scratch + (head_row * p.n + pos) * D
                                   : p.scratch + (head_row * p.ksel + r_lane) * D;
@@ -555,7 +574,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
       const int d0 = db * 32 + j * 8 + half * 4;
       float4 o4 = make_float4(acc_o[db][j * 4 + 0] * inv, acc_o[db][j * 4 + 1] * inv,
                               acc_o[db][j * 4 + 2] * inv, acc_o[db][j * 4 + 3] * inv);
-      const float4 l4 = pre[kPre ? db * 4 + j : 0];
+      float4 l4 = pre[kPre ? db * 4 + j : 0];
       if (EPI == 0) {
         *reinterpret_cast<float4*>(p.out_f32 + (head_row * p.n + pos) * D + d0) = o4;
       } else if (EPI == 4) {
@@ -563,7 +582,10 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
         uint2 w2 = make_uint2(pack_bf16x2(o4.x, o4.y), pack_bf16x2(o4.z, o4.w));
         *reinterpret_cast<uint2*>(orow + d0) = w2;
         rdot = fmaf(o4.x, l4.x, fmaf(o4.y, l4.y, fmaf(o4.z, l4.z, fmaf(o4.w, l4.w, rdot))));
-      } else if (EPI == 5) {
+      } else if (EPI == 5 || EPI == 6) {
+        // EPI 6: a row whose window reaches key 0 never parked one: its
+        // local output is its global output
+        if (EPI == 6 && !snapped) l4 = o4;
         float4 c4 = make_float4(l4.x + sig * o4.x, l4.y + sig * o4.y, l4.z + sig * o4.z,
                                 l4.w + sig * o4.w);
         uint2 w2 = make_uint2(pack_bf16x2(c4.x, c4.y), pack_bf16x2(c4.z, c4.w));
@@ -577,6 +599,9 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
           uint2 w2 = make_uint2(pack_bf16x2(o4.x, o4.y), pack_bf16x2(o4.z, o4.w));
           *reinterpret_cast<uint2*>(orow + d0) = w2;
         }
+      } else if (EPI == 7) {
+        uint2 w2 = make_uint2(pack_bf16x2(o4.x, o4.y), pack_bf16x2(o4.z, o4.w));
+        *reinterpret_cast<uint2*>(orow + d0) = w2;
       } else {
         if (p.og_out)
           *reinterpret_cast<float4*>(p.og_out + (head_row * p.ksel + r_lane) * D + d0) = o4;
@@ -595,10 +620,130 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
       p.router_part[head_row * p.n + pos] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
   }  // row_ok
-  // every wave is done with this block's tiles before the next block's
-  // loads reuse the buffers
-  if (kQueue) __syncthreads();
-  }  // blocks
+}
+
+template <int D, bool GLOBAL, int EPI, bool SEG, bool QUEUE>
+__global__ __launch_bounds__(kThreads, 2)
+__attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
+  using SM = Smem<D>;
+  // Four distinct LDS objects, so the compiler can tell that reads of one
+  // buffer do not wait on buffer loads still landing in another.
+  __shared__ __attribute__((aligned(16))) uint16_t K0[SM::kElems];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[SM::kElems];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[SM::vElems];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[SM::vElems];
+
+  // ---- which tile -------------------------------------------------------
+  const int bid = blockIdx.x;
+  const int Lx = (bid % kNumXcd) * p.per_xcd + bid / kNumXcd;
+  if (Lx >= p.total_wg * p.nsplit) return;
+  // split key ranges (fused global branch of a small problem): workgroup
+  // Lx takes key range `split` of row block L
+  const int split = Lx % p.nsplit;
+  const int L = Lx / p.nsplit;
+  // Queued global launches (p.sched_count set): each (b, kv head) unit has a
+  // queue of its row blocks, heaviest first (the last rows; for packed
+  // examples the order the schedule kernel built). A workgroup takes blocks
+  // from its home unit's queue (the unit its XCD holds, so K/V stay in that
+  // L2) and, once that queue is empty, from the other units' in turn, until
+  // every queue is empty: an XCD whose units have less work (a selection
+  // that leans late in one sequence and early in another) goes on with
+  // the others' remaining blocks instead of idling. An empty queue stays
+  // empty, so every block is taken exactly once. Otherwise the workgroup
+  // does the one block its index names. Always compiled for the routed and
+  // the packed-example global branches; the fused branch has both forms
+  // and takes the queue when fewer (b, kv head) units than XCDs make the
+  // static order split a unit's blocks over XCDs by index (longest first:
+  // one XCD of the pair gets most of the work). With one unit per XCD and a
+  // balanced selection the queue measured 3.5 % slower (its codegen and
+  // atomics); it saves 2.5 % on the routed branch's router-driven selection
+  // and 38 % on a selection as skewed as latest tokens in one sequence,
+  // earliest in the other.
+  constexpr bool kQueue = GLOBAL && (EPI == 5 || SEG || QUEUE);
+  const bool queued = kQueue && p.sched_count != nullptr;
+  __shared__ int taken[2];
+#pragma unroll 1
+  for (int iter = 0;; ++iter) {
+    int unit_bh = L / p.wg_per_unit;             // b * Hkv + kv head
+    int w = L % p.wg_per_unit;
+    if (queued) {
+      if (threadIdx.x == 0) {
+        const int nu = p.B * p.Hkv;
+        int u = unit_bh;
+        int r = atomicAdd(p.sched_count + u, 1);
+        for (int tries = 1; r >= p.wg_per_unit && tries < nu; ++tries) {
+          u = u + 1 < nu ? u + 1 : 0;
+          r = atomicAdd(p.sched_count + u, 1);
+        }
+        taken[0] = u;
+        taken[1] = r;
+      }
+      __syncthreads();
+      if (taken[1] >= p.wg_per_unit) return;  // every queue is empty
+      unit_bh = taken[0];
+      w = p.sched_perm ? p.sched_perm[taken[1]] : p.wg_per_unit - 1 - taken[1];
+    } else {
+      if (iter > 0) return;
+      if (GLOBAL) w = p.wg_per_unit - 1 - w;      // longest prefix first
+    }
+    attn_block<D, GLOBAL, EPI, SEG>(p, unit_bh, w, split, K0, K1, V0, V1);
+    // every wave is done with this block's tiles before the next block's
+    // loads reuse the buffers
+    if (kQueue) __syncthreads();
+  }
+}
+
+// Which (b, kv head) units each XCD serves in the single-launch fused
+// forward, and how many row-block workgroups of each kind there are. Units
+// are pinned to XCDs (their K/V stay in that XCD's L2): with U = 8 m units,
+// XCD x serves units x, x + 8, ...; with U = 8 / c, each unit has c XCDs,
+// which take its workgroups in turn.
+struct FusedPlan {
+  int U;        // B * Hkv
+  int per;      // U = 8m: m units per XCD; 8 % U == 0: c XCDs per unit
+  int gw, lw;   // global / local workgroups per unit
+};
+
+// Single-launch fused forward: on each XCD its global row blocks first
+// (longest causal prefix first), then its local row blocks, so the short
+// local blocks fill the gaps the long global ones leave at the end. The
+// global rows (selected) compute their local branch too (EPI 6); the local
+// rows are the unselected ones (EPI 7). Nothing depends on anything else
+// in the launch.
+template <int D>
+__global__ __launch_bounds__(kThreads, 2)
+__attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_fused_kernel(Params pg, Params pl,
+                                                                       FusedPlan plan) {
+  using SM = Smem<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t K0[SM::kElems];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[SM::kElems];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[SM::vElems];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[SM::vElems];
+  const int x = blockIdx.x % kNumXcd;
+  const int s = blockIdx.x / kNumXcd;
+  int unit, rank, ng;
+  if (plan.U >= kNumXcd) {
+    // m units on this XCD, their blocks interleaved by rank
+    const int m = plan.per;
+    ng = m * plan.gw;
+    const int sl = s < ng ? s : s - ng;
+    if (s >= ng && sl >= m * plan.lw) return;
+    unit = x + kNumXcd * (sl % m);
+    rank = sl / m;
+  } else {
+    // this XCD is number j of the c that serve unit x % U
+    const int c = plan.per, j = x / plan.U;
+    ng = plan.gw > j ? (plan.gw - j + c - 1) / c : 0;
+    const int nl = plan.lw > j ? (plan.lw - j + c - 1) / c : 0;
+    const int sl = s < ng ? s : s - ng;
+    if (s >= ng && sl >= nl) return;
+    unit = x % plan.U;
+    rank = j + sl * c;
+  }
+  if (s < ng)
+    attn_block<D, true, 6, false>(pg, unit, plan.gw - 1 - rank, 0, K0, K1, V0, V1);
+  else
+    attn_block<D, false, 7, false>(pl, unit, rank, 0, K0, K1, V0, V1);
 }
 
 // Work order of the global branch's workgroups over packed examples: the
@@ -731,7 +876,75 @@ hipError_t dispatch_epi(Epi epi, const Params& prm, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+template <int D>
+hipError_t launch_fused(const Params& pg, const Params& pl, const FusedPlan& plan, int grid,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(attn_bf16_fused_kernel<D>, dim3(grid), dim3(kThreads), 0, s, pg, pl, plan);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool attn_bf16_fused_ok(const Dims& d) {
+  if (d.dtype != 1 || d.k <= 0 || (d.d != 64 && d.d != 128)) return false;
+  if (attn_bf16_splits(d) > 1) return false;    // small problems split key ranges instead
+  const int U = d.B * d.Hkv;
+  return U % kNumXcd == 0 || kNumXcd % U == 0;
+}
+
+hipError_t launch_attn_bf16_fused(const Dims& d, const AttnArgs& a, const int32_t* nidx,
+                                  hipStream_t s) {
+  if (d.B == 0 || d.k == 0) return hipSuccess;
+  Params pg{};
+  pg.q = static_cast<const uint16_t*>(a.q);
+  pg.k = static_cast<const uint16_t*>(a.k);
+  pg.v = static_cast<const uint16_t*>(a.v);
+  pg.idx = a.idx;
+  pg.gate = a.gate;
+  pg.out_f32 = a.out_f32;          // parked local outputs of the selected rows
+  pg.scratch = a.out_f32;
+  pg.out_io = static_cast<uint16_t*>(a.out_io);
+  pg.B = d.B;
+  pg.Hq = d.Hq;
+  pg.Hkv = d.Hkv;
+  pg.n = d.n;
+  pg.W = d.window;
+  pg.ksel = d.k;
+  pg.scale_log2 = d.scale * kLog2e;
+  pg.vq = d.vq;
+  pg.vk = d.vk;
+  pg.vv = d.vv;
+  pg.vo = d.vo;
+  pg.nsplit = 1;
+  const int G = d.Hq / d.Hkv;
+  pg.units = (d.k + kRows - 1) / kRows * G;
+  pg.wg_per_unit = (pg.units + kWaves - 1) / kWaves;
+  pg.total_wg = d.B * d.Hkv * pg.wg_per_unit;
+  Params pl = pg;
+  const int nl = d.n - d.k;          // unselected rows per sequence
+  pl.idx = nidx;
+  pl.ksel = nl;
+  pl.units = (nl + kRows - 1) / kRows * G;
+  pl.wg_per_unit = (pl.units + kWaves - 1) / kWaves;
+  pl.total_wg = d.B * d.Hkv * pl.wg_per_unit;
+  FusedPlan plan;
+  plan.U = d.B * d.Hkv;
+  plan.gw = pg.wg_per_unit;
+  plan.lw = nl > 0 ? pl.wg_per_unit : 0;
+  int slots;
+  if (plan.U >= kNumXcd) {
+    plan.per = plan.U / kNumXcd;
+    slots = plan.per * (plan.gw + plan.lw);
+  } else {
+    plan.per = kNumXcd / plan.U;
+    // XCD j = 0 of a unit has the most slots
+    slots = (plan.gw + plan.per - 1) / plan.per + (plan.lw + plan.per - 1) / plan.per;
+  }
+  const int grid = slots * kNumXcd;
+  if (d.d == 64) return launch_fused<64>(pg, pl, plan, grid, s);
+  if (d.d == 128) return launch_fused<128>(pg, pl, plan, grid, s);
+  return hipErrorInvalidValue;
+}
 
 int attn_bf16_splits(const Dims& d) {
   // Enough workgroups for two per CU on a 256-CU part, at most 8 ranges and

@@ -102,8 +102,9 @@ hipError_t launch_bwd_dq_bf16(const Dims& d, bool global, const BwdArgs& a, hipS
 hipError_t launch_bwd_dkdv_f32(const Dims& d, const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dq_f32(const Dims& d, bool global, const BwdArgs& a, hipStream_t s);
 
+// nidx (optional, [B][n-k]): the unselected positions of each row, ascending.
 hipError_t launch_select(const Dims& d, const float* gate, uint8_t* mask,
-                         int32_t* idx, int32_t* rank, hipStream_t s);
+                         int32_t* idx, int32_t* rank, hipStream_t s, int32_t* nidx = nullptr);
 
 // Packed examples: select per example (see select.hip) and build the
 // per-example table and per-token example starts from cu_seqlens.
@@ -120,6 +121,12 @@ size_t attn_bf16_sched_ints(const Dims& d, bool packed);
 // split; more when the problem has fewer than 512 row-block workgroups), and
 // the float32 partials that takes: splits * B * Hq * k * (d + 4), or 0.
 int attn_bf16_splits(const Dims& d);
+// The single-launch fused bf16 forward: selected rows compute both
+// branches, unselected rows (nidx [B][n-k], ascending) the local one; a
+// kernel of its own writes o. Applies when attn_bf16_fused_ok(d).
+bool attn_bf16_fused_ok(const Dims& d);
+hipError_t launch_attn_bf16_fused(const Dims& d, const AttnArgs& a, const int32_t* nidx,
+                                  hipStream_t s);
 size_t attn_bf16_split_floats(const Dims& d);
 hipError_t launch_attn_bf16(const Dims& d, Epi epi, const AttnArgs& a,
                             hipStream_t s);

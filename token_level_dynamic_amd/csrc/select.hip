@@ -73,11 +73,13 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* w
 // is seg[e] = {start, length, k_e, offset}; positions written to idx (at
 // idx[offset ..]) are absolute token positions and rank is the index in the
 // concatenated list; writes past `idx_cap` are dropped.
+// Batched rows may also write nidx[b*(n-k) ..]: the positions not selected,
+// ascending (the rows the local-only work of a fused forward gathers).
 template <bool SEG>
 __global__ __launch_bounds__(kThreads) void select_kernel(
     const float* __restrict__ gate, int n_rows, int k_rows, uint8_t* __restrict__ mask,
     int32_t* __restrict__ idx, int32_t* __restrict__ rank, const int4* __restrict__ seg,
-    int idx_cap) {
+    int idx_cap, int32_t* __restrict__ nidx) {
   __shared__ uint32_t hist[4096];
   __shared__ uint32_t scan_ws[kWaves + 1];
   __shared__ uint32_t s_digit, s_before;
@@ -103,6 +105,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   uint8_t* mrow = mask + (size_t)start;
   int32_t* rrow = rank + (size_t)start;
   int32_t* irow = idx ? idx + (size_t)koff : nullptr;
+  int32_t* nrow = (!SEG && nidx) ? nidx + (size_t)b * (n_rows - k_rows) : nullptr;
   const int icap = SEG ? idx_cap - koff : k;  // entries of irow that may be written
 
   // This thread's positions c * kChunk + t * kItems + j, as order images,
@@ -215,6 +218,8 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       mv[j] = sel ? 1 : 0;
       rv[j] = sel ? (int32_t)r + rank_add : -1;
       if (sel && p0 + j < n && (int)r < icap) irow[r] = p0 + j + pos_add;
+      // unselected: p - r tokens before it are unselected too (r of them are selected)
+      if (!sel && nrow && p0 + j < n) nrow[p0 + j - (int)r] = p0 + j;
       gt_before += gt ? 1u : 0u;
       tie_before += tie ? 1u : 0u;
     }
@@ -257,10 +262,10 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
 }  // namespace
 
 hipError_t launch_select(const Dims& d, const float* gate, uint8_t* mask,
-                         int32_t* idx, int32_t* rank, hipStream_t s) {
+                         int32_t* idx, int32_t* rank, hipStream_t s, int32_t* nidx) {
   if (d.B == 0 || d.n == 0) return hipSuccess;
   hipLaunchKernelGGL(select_kernel<false>, dim3(d.B), dim3(kThreads), 0, s, gate, d.n, d.k, mask,
-                     idx, rank, nullptr, 0);
+                     idx, rank, nullptr, 0, nidx);
   return hipGetLastError();
 }
 
@@ -269,7 +274,7 @@ hipError_t launch_select_segments(int n_segments, const int4* seg, const float* 
                                   hipStream_t s) {
   if (n_segments == 0) return hipSuccess;
   hipLaunchKernelGGL(select_kernel<true>, dim3(n_segments), dim3(kThreads), 0, s, gate, 0, 0,
-                     mask, idx, rank, seg, idx_cap);
+                     mask, idx, rank, seg, idx_cap, nullptr);
   return hipGetLastError();
 }
 
