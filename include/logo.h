@@ -166,6 +166,24 @@ logo_status logo_forward(const logo_problem* p, const void* q, const void* k,
                          uint8_t* mask, int32_t* idx, int32_t* rank,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* The forward for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * allocation. Same arguments, results and errors as logo_forward, without
+ * the workspace: its scratch is one array of LOGO_NOALLOC_SCRATCH_BYTES in
+ * the library's device code, which every GPU the library runs on holds
+ * from the library's first use there until the process ends. No call
+ * allocates or frees memory. Returns LOGO_ERR_WORKSPACE, before enqueueing
+ * anything, when logo_workspace_size exceeds LOGO_NOALLOC_SCRATCH_BYTES
+ * (the headline 32K layer needs about 107 MB; the 128K one does not fit).
+ * Every call on one GPU uses that GPU's one array, which keeps the last
+ * call's contents: calls that overlap on one GPU (other streams, other host
+ * threads) race on it and must be serialised by the caller. */
+#define LOGO_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+logo_status logo_forward_noalloc(const logo_problem* p, const void* q,
+                                 const void* k, const void* v,
+                                 const float* gate, void* o, uint8_t* mask,
+                                 int32_t* idx, int32_t* rank, void* stream);
+
 /* ---- training: forward that saves statistics, and the backward --------
  *
  * The gate is learned (LoGo abstract) and the method is trained ("Learning

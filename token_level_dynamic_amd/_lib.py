@@ -110,6 +110,7 @@ _SIGS = {
     "logo_local_attn": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P]),
     "logo_global_attn_sparse": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P]),
     "logo_combine": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P]),
+    "logo_forward_noalloc": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "logo_forward": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                     ctypes.c_size_t, _P]),
     "logo_forward_train": (ctypes.c_int, [_PP] + [_P] * 13),
@@ -286,6 +287,26 @@ def logo_forward(p: logo_problem, q, k, v, gate, o, mask, idx, rank, workspace,
                               _ptr(idx, "idx"), _ptr(rank, "rank"),
                               _ptr(workspace, "workspace"), ws_bytes, _stream(stream)),
            "logo_forward")
+
+
+# bytes of the scratch array logo_forward_noalloc uses (include/logo.h)
+NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
+
+
+def logo_forward_noalloc(p: logo_problem, q, k, v, gate, o, mask, idx, rank,
+                         stream=None) -> None:
+    """logo_forward without a workspace (the library's own scratch array)."""
+    kk = logo_target_count(p.rho, p.n)
+    qp, kp, vp = _qkv(p, q, k, v)
+    _expect(gate, "gate", torch.float32, p.B * p.n)
+    op = _io(p, o, "o", p.Hq)
+    _expect(mask, "mask", torch.uint8, p.B * p.n)
+    _expect(idx, "idx", torch.int32, p.B * kk)
+    _expect(rank, "rank", torch.int32, p.B * p.n)
+    _check(lib().logo_forward_noalloc(ctypes.byref(p), qp, kp, vp, _ptr(gate, "gate"), op,
+                                      _ptr(mask, "mask"), _ptr(idx, "idx"), _ptr(rank, "rank"),
+                                      _stream(stream)),
+           "logo_forward_noalloc")
 
 
 def logo_forward_train(p: logo_problem, q, k, v, gate, o, mask, idx, rank, lse_local,

@@ -391,6 +391,61 @@ logo_status logo_forward(const logo_problem* p, const void* q, const void* k, co
   return LOGO_OK;
 }
 
+}  // extern "C"
+
+// ---- the forward without allocation ------------------------------------
+// logo_forward_noalloc runs logo_forward on a file-scope device array
+// instead of a caller's workspace. In host code `scratch` names a host-side
+// stand-in, not device memory: its device address on the current device
+// comes from hipGetSymbolAddress, looked up once per device and kept in
+// g_scratch_ptr; only that address is ever passed to kernels.
+namespace {
+
+__device__ __align__(256) unsigned char scratch[LOGO_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+logo_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(LOGO_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(LOGO_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LOGO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+logo_status logo_forward_noalloc(const logo_problem* p, const void* q, const void* k,
+                                 const void* v, const float* gate, void* o, uint8_t* mask,
+                                 int32_t* idx, int32_t* rank, void* stream) {
+  logo::Dims d;
+  LOGO_TRY(check_problem(p, &d));
+  if (empty(d)) return LOGO_OK;
+  const size_t need = scratch_bytes(d);
+  if (need > (size_t)LOGO_NOALLOC_SCRATCH_BYTES)
+    return fail(LOGO_ERR_WORKSPACE,
+                "this problem needs %zu bytes of scratch; logo_forward_noalloc holds %zu "
+                "(use logo_forward with a workspace)",
+                need, (size_t)LOGO_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0) LOGO_TRY(scratch_address(&ws));
+  return logo_forward(p, q, k, v, gate, o, mask, idx, rank, ws, need, stream);
+}
+
 logo_status logo_forward_train(const logo_problem* p, const void* q, const void* k,
                                const void* v, const float* gate, void* o, uint8_t* mask,
                                int32_t* idx, int32_t* rank, float* lse_local, float* lse_global,
