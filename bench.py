@@ -321,6 +321,12 @@ def record_traffic(args) -> int:
             "write_scale": round(ws, 5),
             "note": "same counters on bench.py --mode train; bwd_dq is both dQ launches"}
     path = args.traffic_out or os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(path):
+        # keep the entries these runs do not replace (e.g. the training pass)
+        with open(path) as f:
+            old = json.load(f)
+        old.update(data)
+        data = old
     with open(path, "w") as f:
         json.dump(data, f, indent=1)
         f.write("\n")
@@ -375,6 +381,7 @@ def ceilings(torch) -> int:
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     stream = torch.cuda.current_stream()
     # kind: name, work per wave per iteration, unit
+    only = os.environ.get("CEILING_KINDS")
     kinds = {0: ("mfma_32x32x16_bf16", 4 * 32768.0, "flop"),
              1: ("ds_read_b128", 8 * 1024.0, "B"),
              2: ("ds_read_b64_tr_b16", 8 * 512.0, "B"),
@@ -386,12 +393,27 @@ def ceilings(torch) -> int:
              8: ("V tile reads, stride 160", 32 * 512.0, "B"),
              9: ("V tile reads, swizzled 128", 32 * 512.0, "B"),
              10: ("K tile reads, stride 136", 16 * 1024.0, "B"),
-             11: ("K tile reads, swizzled 128", 16 * 1024.0, "B")}
+             11: ("K tile reads, swizzled 128", 16 * 1024.0, "B"),
+             # products counted for the waves that issue them (half of the
+             # waves in the split forms)
+             13: ("mfma + 2 rounds fma/exp2 per product, same wave", 4 * 32768.0, "flop"),
+             14: ("mfma only (control for 13-18)", 4 * 32768.0, "flop"),
+             15: ("fma/exp2 only, 8 per iteration", 4 * 2 * 2 * 64.0, "valu"),
+             16: ("mfma in even waves, 2 rounds fma/exp2 in odd waves", 2 * 32768.0, "flop"),
+             17: ("mfma + 4 rounds fma/exp2 per product, same wave", 4 * 32768.0, "flop"),
+             18: ("mfma in even waves, 4 rounds fma/exp2 in odd waves", 2 * 32768.0, "flop"),
+             19: ("mfma + 0.5 KiB LDS per product, random operands", 4 * 32768.0, "flop"),
+             20: ("mfma, one dependent chain", 4 * 32768.0, "flop"),
+             21: ("mfma, two dependent chains", 4 * 32768.0, "flop"),
+             22: ("as 13, accumulators in VGPRs", 4 * 32768.0, "flop"),
+             23: ("as 14, accumulators in VGPRs", 4 * 32768.0, "flop")}
+    if only:
+        kinds = {k: v for k, v in kinds.items() if str(k) in only.split(",")}
     out = {}
     for kind, (name, per_iter, unit) in kinds.items():
         for wg_per_cu in (1, 2, 4):
             blocks = cus * wg_per_cu
-            iters = 20000 if kind in (0, 4, 5, 6) else 4000 if kind >= 7 else 40000
+            iters = 20000 if kind in (0, 4, 5, 6) or kind >= 13 else 4000 if kind >= 7 else 40000
             sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
             clk = torch.zeros(blocks * 4, dtype=torch.int64, device="cuda")
             rc = lib.ceiling_launch(kind, blocks, 10, sink.data_ptr(), clk.data_ptr(), None, 0,
@@ -422,9 +444,10 @@ def ceilings(torch) -> int:
             print(json.dumps({name: out[f"{name} | {wg_per_cu} WG/CU"],
                               "wg_per_cu": wg_per_cu}), flush=True)
     # HBM: streaming 16-byte reads over 4 GiB of random bytes, 4 passes
-    nbytes = 4 << 30
-    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda")
-    for wg_per_cu in (2, 4, 8):
+    nbytes = 4 << 30 if not only else 0
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (max(nbytes, 16) // 4,), dtype=torch.int32,
+                        device="cuda")
+    for wg_per_cu in ((2, 4, 8) if nbytes else ()):
         blocks = cus * wg_per_cu
         sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
         lib.ceiling_launch(12, blocks, 1, sink.data_ptr(), None, src.data_ptr(), nbytes,

@@ -279,6 +279,150 @@ __global__ __launch_bounds__(kThreads) void tile_k_kernel(float* sink, long long
   sink[threadIdx.x + blockIdx.x * kThreads] = (float)(x0 ^ x1 ^ x2 ^ x3);
 }
 
+// Dependent matrix-core products: NC accumulator chains, each product
+// accumulating into the previous one's result (4 products per iteration).
+template <int NC>
+__global__ __launch_bounds__(kThreads) void mfma_chain_kernel(float* sink, long long* clk,
+                                                              int iters) {
+  const uint32_t t = threadIdx.x + blockIdx.x * kThreads;
+  const bf16x8 a = __builtin_bit_cast(
+      bf16x8, make_uint4(bf16_pair(t), bf16_pair(t + 1), bf16_pair(t + 2), bf16_pair(t + 3)));
+  const bf16x8 b = __builtin_bit_cast(
+      bf16x8, make_uint4(bf16_pair(t + 5), bf16_pair(t + 9), bf16_pair(t + 11), bf16_pair(t + 13)));
+  f32x16 c[NC] = {};
+  const long long t0 = __builtin_amdgcn_s_memtime();
+  const long long r0 = __builtin_amdgcn_s_memrealtime();
+#pragma unroll 1
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      c[j % NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(j & 1 ? a : b, j & 2 ? b : a, c[j % NC],
+                                                         0, 0, 0);
+  }
+  record(clk, t0, r0);
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NC; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += c[j][e];
+  sink[t] = s;
+}
+
+// Matrix-core products with independent vector work beside them in the
+// same wave: per 4 products (4 accumulator chains), NV rounds of an FMA and
+// an exp2 on each of 4 independent float chains (8 NV VALU instructions, 4 NV
+// of them transcendental). MODE 1 / 2 keep only the products / only the
+// vector work; MODE 3 runs the products in even waves and the vector work in
+// odd ones (two loops chosen once per wave), so the two kinds come from
+// different waves (of one SIMD when two workgroups share a CU).
+template <int NV, int MODE, bool VACC = false>
+__global__ __launch_bounds__(kThreads) void mfma_valu_kernel(float* sink, long long* clk,
+                                                             int iters) {
+  const uint32_t t = threadIdx.x + blockIdx.x * kThreads;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bf16x8 a = __builtin_bit_cast(
+      bf16x8, make_uint4(bf16_pair(t), bf16_pair(t + 1), bf16_pair(t + 2), bf16_pair(t + 3)));
+  const bf16x8 b = __builtin_bit_cast(
+      bf16x8, make_uint4(bf16_pair(t + 5), bf16_pair(t + 9), bf16_pair(t + 11), bf16_pair(t + 13)));
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  float x0 = -0.001f * threadIdx.x, x1 = x0 - 0.1f, x2 = x0 - 0.2f, x3 = x0 - 0.3f;
+  auto valu_round = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      x0 = __builtin_amdgcn_exp2f(fmaf(x0, -0.5f, -0.25f));
+      x1 = __builtin_amdgcn_exp2f(fmaf(x1, -0.5f, -0.25f));
+      x2 = __builtin_amdgcn_exp2f(fmaf(x2, -0.5f, -0.25f));
+      x3 = __builtin_amdgcn_exp2f(fmaf(x3, -0.5f, -0.25f));
+    }
+  };
+  auto mfma_round = [&]() __attribute__((always_inline)) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, b, c3, 0, 0, 0);
+    // VACC: keep the accumulators in architectural VGPRs (as in kernels whose
+    // vector code reads them) rather than accumulation registers
+    if (VACC) asm volatile("" : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3));
+  };
+  const long long t0 = __builtin_amdgcn_s_memtime();
+  const long long r0 = __builtin_amdgcn_s_memrealtime();
+  if (MODE == 0) {
+#pragma unroll 1
+    for (int i = 0; i < iters; ++i) {
+      mfma_round();
+      valu_round();
+    }
+  } else if (MODE == 1 || (MODE == 3 && (wave & 1) == 0)) {
+#pragma unroll 1
+    for (int i = 0; i < iters; ++i) mfma_round();
+  } else {
+#pragma unroll 1
+    for (int i = 0; i < iters; ++i) valu_round();
+  }
+  record(clk, t0, r0);
+  float s = x0 + x1 + x2 + x3;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) s += c0[e] + c1[e] + c2[e] + c3[e];
+  sink[t] = s;
+}
+
+// Matrix-core products on operands read from LDS that hold pseudo-random
+// bf16 values with every mantissa bit in play (magnitudes 2^-4 .. 2^3,
+// random signs), 0.5 KiB per product as in the 0.5 KiB case above: the
+// power, hence the clock, of products on data like the attention inputs.
+__device__ __forceinline__ uint32_t hash32(uint32_t x) {
+  x ^= x >> 16; x *= 0x7feb352du; x ^= x >> 15; x *= 0x846ca68bu; x ^= x >> 16;
+  return x;
+}
+__device__ __forceinline__ uint32_t rand_bf16_pair(uint32_t x) {
+  const uint32_t h = hash32(x), g = hash32(x ^ 0x9e3779b9u);
+  // exponent 123..130 (2^-4 .. 2^3), random sign and 7 mantissa bits
+  const uint32_t a = ((h & 1u) << 15) | ((123u + ((h >> 1) & 7u)) << 7) | ((h >> 4) & 0x7fu);
+  const uint32_t b = ((g & 1u) << 15) | ((123u + ((g >> 1) & 7u)) << 7) | ((g >> 4) & 0x7fu);
+  return a | (b << 16);
+}
+__global__ __launch_bounds__(kThreads) void mfma_lds_random_kernel(float* sink, long long* clk,
+                                                                   int iters) {
+  __shared__ uint4 buf[kLdsChunks];
+  for (int i = threadIdx.x; i < kLdsChunks; i += kThreads)
+    buf[i] = make_uint4(rand_bf16_pair(4 * i), rand_bf16_pair(4 * i + 1),
+                        rand_bf16_pair(4 * i + 2), rand_bf16_pair(4 * i + 3));
+  __syncthreads();
+  const uint32_t t = threadIdx.x + blockIdx.x * kThreads;
+  const bf16x8 b = __builtin_bit_cast(
+      bf16x8, make_uint4(rand_bf16_pair(7 * t), rand_bf16_pair(7 * t + 1),
+                         rand_bf16_pair(7 * t + 2), rand_bf16_pair(7 * t + 3)));
+  bf16x8 a[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a[j] = b;
+  f32x16 c[4] = {};
+  const int base = threadIdx.x;
+  const long long t0 = __builtin_amdgcn_s_memtime();
+  const long long r0 = __builtin_amdgcn_s_memrealtime();
+#pragma unroll 1
+  for (int i = 0; i < iters; i += 4) {
+    // fresh operands for two chains per product round, read two rounds ahead
+    // (register indices fixed at compile time)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint4 n0 = buf[(base + ((i + u) * 2) * kThreads) & (kLdsChunks - 1)];
+      const uint4 n1 = buf[(base + ((i + u) * 2 + 1) * kThreads) & (kLdsChunks - 1)];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b, c[j], 0, 0, 0);
+      a[u] = __builtin_bit_cast(bf16x8, n0);
+      a[(u + 2) & 3] = __builtin_bit_cast(bf16x8, n1);
+    }
+  }
+  record(clk, t0, r0);
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += c[j][e];
+  sink[t] = s;
+}
+
 // HBM read rate: every thread streams 16-byte loads over the buffer in a
 // grid-stride loop (indices below n16 only) and folds them into one value.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -302,7 +446,12 @@ extern "C" {
 // 7/8/9 the V^T read pattern of one tile (row stride 144, 160, or 128 with
 // chunk swizzle 4 (r & 3)), 10/11 the K read pattern (stride 136, or 128 with
 // chunk swizzle r & 15), 12 streaming reads of src (src_bytes, a multiple of
-// 16; iters and clk unused). sink: blocks * 256 floats; clk: blocks * 4
+// 16; iters and clk unused), 13-18 products beside vector work (13: both in
+// every wave, 2 FMA+exp2 rounds per product; 14 products only; 15 vector
+// only; 16 products in even waves and vector work in odd ones; 17, 18: as
+// 13, 16 with 4 rounds), 19 products on full-entropy random operands from
+// LDS (0.5 KiB per product), 20/21 products in 1 / 2 dependent accumulator
+// chains, 22/23 as 13/14 with the accumulators in architectural VGPRs. sink: blocks * 256 floats; clk: blocks * 4
 // int64. Returns a hipError_t.
 int ceiling_launch(int kind, int blocks, int iters, float* sink, long long* clk,
                    const void* src, long long src_bytes, hipStream_t stream) {
@@ -328,6 +477,17 @@ int ceiling_launch(int kind, int blocks, int iters, float* sink, long long* clk,
     case 9: hipLaunchKernelGGL((tile_v_kernel<128, 1>), g, b, 0, stream, sink, clk, iters); break;
     case 10: hipLaunchKernelGGL((tile_k_kernel<136, 0>), g, b, 0, stream, sink, clk, iters); break;
     case 11: hipLaunchKernelGGL((tile_k_kernel<128, 2>), g, b, 0, stream, sink, clk, iters); break;
+    case 13: hipLaunchKernelGGL((mfma_valu_kernel<2, 0>), g, b, 0, stream, sink, clk, iters); break;
+    case 14: hipLaunchKernelGGL((mfma_valu_kernel<2, 1>), g, b, 0, stream, sink, clk, iters); break;
+    case 15: hipLaunchKernelGGL((mfma_valu_kernel<2, 2>), g, b, 0, stream, sink, clk, iters); break;
+    case 16: hipLaunchKernelGGL((mfma_valu_kernel<2, 3>), g, b, 0, stream, sink, clk, iters); break;
+    case 17: hipLaunchKernelGGL((mfma_valu_kernel<4, 0>), g, b, 0, stream, sink, clk, iters); break;
+    case 18: hipLaunchKernelGGL((mfma_valu_kernel<4, 3>), g, b, 0, stream, sink, clk, iters); break;
+    case 19: hipLaunchKernelGGL(mfma_lds_random_kernel, g, b, 0, stream, sink, clk, iters); break;
+    case 20: hipLaunchKernelGGL(mfma_chain_kernel<1>, g, b, 0, stream, sink, clk, iters); break;
+    case 22: hipLaunchKernelGGL((mfma_valu_kernel<2, 0, true>), g, b, 0, stream, sink, clk, iters); break;
+    case 23: hipLaunchKernelGGL((mfma_valu_kernel<2, 1, true>), g, b, 0, stream, sink, clk, iters); break;
+    case 21: hipLaunchKernelGGL(mfma_chain_kernel<2>, g, b, 0, stream, sink, clk, iters); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
