@@ -406,7 +406,18 @@ def ceilings(torch) -> int:
              20: ("mfma, one dependent chain", 4 * 32768.0, "flop"),
              21: ("mfma, two dependent chains", 4 * 32768.0, "flop"),
              22: ("as 13, accumulators in VGPRs", 4 * 32768.0, "flop"),
-             23: ("as 14, accumulators in VGPRs", 4 * 32768.0, "flop")}
+             23: ("as 14, accumulators in VGPRs", 4 * 32768.0, "flop"),
+             # 512-thread workgroups: waves w and w + 4 share a SIMD; products
+             # counted for the waves that issue them
+             25: ("8 waves: products in all", 2 * 4 * 32768.0, "flop"),
+             26: ("8 waves: products in waves 0-3, 4-7 idle", 4 * 32768.0, "flop"),
+             27: ("8 waves: products in 0-3, 8 FMA per product in 4-7", 4 * 32768.0, "flop"),
+             28: ("8 waves: products in 0-3, 2 v_exp_f32 per product in 4-7", 4 * 32768.0,
+                  "flop"),
+             29: ("8 waves: products + 8 FMA per product in 0-3, 4-7 idle", 4 * 32768.0,
+                  "flop"),
+             30: ("8 waves: products + 2 v_exp_f32 per product in 0-3, 4-7 idle",
+                  4 * 32768.0, "flop")}
     if only:
         kinds = {k: v for k, v in kinds.items() if str(k) in only.split(",")}
     out = {}

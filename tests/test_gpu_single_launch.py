@@ -1,0 +1,72 @@
+"""The single-launch forward at medium sizes that take it (bf16, no key-range
+split, B * Hkv a multiple or a divisor of 8): selected rows compute both
+branches in one walk of their causal prefix, unselected rows their window.
+Every output row of three query heads (the first and last of kv group 0, the
+last of the layer) for every sequence is compared with the oracle, and the
+selection bit for bit.
+
+The cases cover ragged lengths, seven-head groups, d = 64 with bursty gates,
+windows that reach key 0 for every row (no local output is parked), a
+one-key window, every token selected (no unselected rows), and both ways the
+(b, kv head) pairs map onto the eight XCDs: several pairs per XCD, and
+several XCDs per pair."""
+import numpy as np
+import pytest
+
+import oracle
+import token_level_dynamic_amd as T
+import oracle_pool as OP
+from gpu_util import ensure_built, gather_rows, host, problem, run_forward, say, single_launch, \
+    to_dev
+from workloads import get_workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2   # bf16 output, max-abs (as every bf16 parity test)
+
+CASES = {
+    "g4_ragged_16pairs": ("gqa32k", dict(B=2, Hq=32, Hkv=8, n=5001, window=300, rho=0.2)),
+    "g7_8pairs": ("gqa128k", dict(B=1, Hq=56, Hkv=8, n=4700, window=257, rho=0.25)),
+    "d64_bursty_16pairs": ("sweep64k", dict(B=1, Hq=16, Hkv=16, n=8191, window=1000,
+                                            rho=0.5)),
+    "g7_4pairs": ("gqa128k", dict(B=1, Hq=28, Hkv=4, n=11700, window=4096, rho=0.2)),
+    "window_covers_all": ("gqa32k", dict(B=2, Hq=32, Hkv=8, n=5000, window=8000, rho=0.2)),
+    "window_one": ("gqa32k", dict(B=2, Hq=32, Hkv=8, n=5000, window=1, rho=0.2)),
+    "rho_one_d64": ("sweep64k", dict(B=1, Hq=16, Hkv=16, n=4000, window=500, rho=1.0)),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    ensure_built()
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_single_launch_matches_oracle(name):
+    base, over = CASES[name]
+    w = get_workload(base, **over)
+    p = problem(w)
+    assert single_launch(p), "case does not take the single launch"
+    inp = make_inputs(w, 0)
+    say(f"[single] {name}: {w}")
+    q, k, v, gate = to_dev(inp)
+    got = run_forward(p, q, k, v, gate)
+    del q, k, v
+    rm, ri, rr = oracle.select_queries(inp.gate, w.rho)
+    assert np.array_equal(host(got["mask"]), rm)
+    assert np.array_equal(host(got["idx"]), ri)
+    assert np.array_equal(host(got["rank"]), rr)
+    G = w.Hq // w.Hkv
+    heads = sorted({0, G - 1, w.Hq - 1})
+    rows = [(b, h, i) for b in range(w.B) for h in heads for i in range(w.n)]
+    with OP.SharedInputs(q=inp.q, k=inp.k, v=inp.v, gate=inp.gate) as sh:
+        parts = OP.map_chunks(sh, "oracle.forward_rows",
+                              lambda c: ("@q", "@k", "@v", "@gate", w.window, w.rho, list(c)),
+                              rows, chunk=256)
+    ref = np.concatenate([x["o_rows"] for x in parts])
+    vals = gather_rows(got["o"], rows)
+    err = np.abs(vals - ref)
+    worst = rows[int(err.max(axis=1).argmax())]
+    say(f"  {len(rows)} rows, max_abs={err.max():.3e} at {worst} "
+        f"(selected: {bool(rm[worst[0], worst[2]])}), rms {np.sqrt((err ** 2).mean()):.2e}")
+    assert err.max() <= TOL

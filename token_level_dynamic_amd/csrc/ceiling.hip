@@ -439,6 +439,80 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __re
 
 }  // namespace
 
+// Matrix-core and vector work on the two waves that share a SIMD (512-thread
+// workgroups: waves w and w + 4 run on one SIMD). MODE 0: all eight waves
+// issue products; 1: waves 0-3 issue products, 4-7 nothing; 2: waves 0-3
+// products, 4-7 NV rounds of 4 independent FMA chains per iteration; 3: as 2
+// with v_exp_f32 chains; 4: waves 0-3 products and the FMA rounds in the same
+// wave, 4-7 nothing; 5: as 4 with v_exp_f32. Per iteration a product wave
+// issues 4 v_mfma_f32_32x32x16_bf16 (4 x 32 cycles of one SIMD's matrix core).
+template <int MODE, int NV>
+__global__ __launch_bounds__(512) void simd_pair_kernel(float* sink, long long* clk, int iters) {
+  const uint32_t t = threadIdx.x + blockIdx.x * 512;
+  const int team = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
+  const bf16x8 a = __builtin_bit_cast(
+      bf16x8, make_uint4(bf16_pair(t), bf16_pair(t + 1), bf16_pair(t + 2), bf16_pair(t + 3)));
+  const bf16x8 b = __builtin_bit_cast(
+      bf16x8, make_uint4(bf16_pair(t + 5), bf16_pair(t + 9), bf16_pair(t + 11), bf16_pair(t + 13)));
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  float x0 = -0.001f * threadIdx.x, x1 = x0 - 0.1f, x2 = x0 - 0.2f, x3 = x0 - 0.3f;
+  auto fma_round = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      x0 = fmaf(x0, 0.999f, 0.25f);
+      x1 = fmaf(x1, 0.999f, 0.25f);
+      x2 = fmaf(x2, 0.999f, 0.25f);
+      x3 = fmaf(x3, 0.999f, 0.25f);
+    }
+  };
+  auto exp_round = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      x0 = __builtin_amdgcn_exp2f(-x0);
+      x1 = __builtin_amdgcn_exp2f(-x1);
+      x2 = __builtin_amdgcn_exp2f(-x2);
+      x3 = __builtin_amdgcn_exp2f(-x3);
+    }
+  };
+  auto mfma_round = [&]() __attribute__((always_inline)) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, b, c3, 0, 0, 0);
+  };
+  const long long t0 = __builtin_amdgcn_s_memtime();
+  const long long r0 = __builtin_amdgcn_s_memrealtime();
+  const bool products = MODE == 0 || team == 0;
+  if (products) {
+#pragma unroll 1
+    for (int i = 0; i < iters; ++i) {
+      mfma_round();
+      if (MODE == 4) fma_round();
+      if (MODE == 5) exp_round();
+    }
+  } else if (MODE == 2) {
+#pragma unroll 1
+    for (int i = 0; i < iters; ++i) fma_round();
+  } else if (MODE == 3) {
+#pragma unroll 1
+    for (int i = 0; i < iters; ++i) exp_round();
+  }
+  __syncthreads();
+  record(clk, t0, r0);
+  float s = x0 + x1 + x2 + x3;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) s += c0[e] + c1[e] + c2[e] + c3[e];
+  if (s == 1.2345f) sink[t & 255] = s;
+}
+
+// Wave placement: every wave of a 512-thread workgroup writes the SIMD it
+// runs on (bits 5:4 of its HW_ID register) to sink[8 * block + wave].
+__global__ __launch_bounds__(512) void wave_simd_kernel(float* sink) {
+  const int wave = threadIdx.x >> 6;
+  const int simd = __builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4);   // hwreg(HW_ID, 4, 2)
+  if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 8 + wave] = (float)simd;
+}
+
 extern "C" {
 
 // kind: 0 matrix-core products, 1 ds_read_b128, 2 ds_read_b64_tr_b16,
@@ -451,7 +525,11 @@ extern "C" {
 // only; 16 products in even waves and vector work in odd ones; 17, 18: as
 // 13, 16 with 4 rounds), 19 products on full-entropy random operands from
 // LDS (0.5 KiB per product), 20/21 products in 1 / 2 dependent accumulator
-// chains, 22/23 as 13/14 with the accumulators in architectural VGPRs. sink: blocks * 256 floats; clk: blocks * 4
+// chains, 22/23 as 13/14 with the accumulators in architectural VGPRs, 24
+// the SIMD of each wave of 512-thread workgroups (sink[8 * block + wave]),
+// 25-30 matrix-core and vector work on the two waves that share a SIMD
+// (simd_pair_kernel modes 0-5).
+// sink: blocks * 256 floats; clk: blocks * 4
 // int64. Returns a hipError_t.
 int ceiling_launch(int kind, int blocks, int iters, float* sink, long long* clk,
                    const void* src, long long src_bytes, hipStream_t stream) {
@@ -488,6 +566,13 @@ int ceiling_launch(int kind, int blocks, int iters, float* sink, long long* clk,
     case 22: hipLaunchKernelGGL((mfma_valu_kernel<2, 0, true>), g, b, 0, stream, sink, clk, iters); break;
     case 23: hipLaunchKernelGGL((mfma_valu_kernel<2, 1, true>), g, b, 0, stream, sink, clk, iters); break;
     case 21: hipLaunchKernelGGL(mfma_chain_kernel<2>, g, b, 0, stream, sink, clk, iters); break;
+    case 24: hipLaunchKernelGGL(wave_simd_kernel, g, dim3(512), 0, stream, sink); break;
+    case 25: hipLaunchKernelGGL((simd_pair_kernel<0, 8>), g, dim3(512), 0, stream, sink, clk, iters); break;
+    case 26: hipLaunchKernelGGL((simd_pair_kernel<1, 8>), g, dim3(512), 0, stream, sink, clk, iters); break;
+    case 27: hipLaunchKernelGGL((simd_pair_kernel<2, 8>), g, dim3(512), 0, stream, sink, clk, iters); break;
+    case 28: hipLaunchKernelGGL((simd_pair_kernel<3, 2>), g, dim3(512), 0, stream, sink, clk, iters); break;
+    case 29: hipLaunchKernelGGL((simd_pair_kernel<4, 8>), g, dim3(512), 0, stream, sink, clk, iters); break;
+    case 30: hipLaunchKernelGGL((simd_pair_kernel<5, 2>), g, dim3(512), 0, stream, sink, clk, iters); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
