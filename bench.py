@@ -417,7 +417,15 @@ def ceilings(torch) -> int:
              29: ("8 waves: products + 8 FMA per product in 0-3, 4-7 idle", 4 * 32768.0,
                   "flop"),
              30: ("8 waves: products + 2 v_exp_f32 per product in 0-3, 4-7 idle",
-                  4 * 32768.0, "flop")}
+                  4 * 32768.0, "flop"),
+             31: ("tile model, 1 wave/SIMD: 0.5 KiB LDS + 3.5 FMA per product", 4 * 32768.0,
+                  "flop"),
+             32: ("tile model, 2 waves/SIMD: 1 KiB LDS + 3.5 FMA per product",
+                  2 * 4 * 32768.0, "flop"),
+             33: ("tile model, 1 wave/SIMD: 0.5 KiB LDS per product", 4 * 32768.0, "flop"),
+             34: ("tile model, 1 wave/SIMD: 3.5 FMA per product", 4 * 32768.0, "flop"),
+             35: ("tile model, 2 waves/SIMD: 1 KiB LDS per product", 2 * 4 * 32768.0, "flop"),
+             36: ("tile model, 2 waves/SIMD: 3.5 FMA per product", 2 * 4 * 32768.0, "flop")}
     if only:
         kinds = {k: v for k, v in kinds.items() if str(k) in only.split(",")}
     out = {}

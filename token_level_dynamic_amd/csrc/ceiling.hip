@@ -439,6 +439,61 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __re
 
 }  // namespace
 
+// Models of a tile loop (512-thread workgroups, one per CU for the LDS it
+// takes): the product waves issue, per iteration, NR ds_read_b128 (1 KiB
+// each per wave, landing in the A operands of the next iteration's
+// products), 4 v_mfma_f32_32x32x16_bf16 and NF FMAs in 4 chains. BOTH:
+// all eight waves (two per SIMD) issue, else waves 0-3 only (one per SIMD).
+template <int NR, int NF, bool BOTH>
+__global__ __launch_bounds__(512) void tile_model_kernel(float* sink, long long* clk, int iters) {
+  __shared__ uint4 buf[2 * kLdsChunks];
+  for (int i = threadIdx.x; i < 2 * kLdsChunks; i += 512)
+    buf[i] = make_uint4(bf16_pair(i), bf16_pair(i + 1), bf16_pair(i + 2), bf16_pair(i + 3));
+  __syncthreads();
+  const uint32_t t = threadIdx.x + blockIdx.x * 512;
+  const int team = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
+  const bf16x8 b = __builtin_bit_cast(
+      bf16x8, make_uint4(bf16_pair(t + 5), bf16_pair(t + 9), bf16_pair(t + 11), bf16_pair(t + 13)));
+  bf16x8 a[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a[j] = b;
+  f32x16 c[4] = {};
+  float x0 = -0.001f * threadIdx.x, x1 = x0 - 0.1f, x2 = x0 - 0.2f, x3 = x0 - 0.3f;
+  const int base = threadIdx.x;
+  const long long t0 = __builtin_amdgcn_s_memtime();
+  const long long r0 = __builtin_amdgcn_s_memrealtime();
+  if (BOTH || team == 0) {
+#pragma unroll 1
+    for (int i = 0; i < iters; ++i) {
+      bf16x8 na[4];
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+        na[r & 3] = __builtin_bit_cast(bf16x8, buf[(base + (i * NR + r) * 512) & (2 * kLdsChunks - 1)]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b, c[j], 0, 0, 0);
+#pragma unroll
+      for (int f = 0; f < NF; f += 4) {
+        x0 = fmaf(x0, 0.999f, 0.25f);
+        if (f + 1 < NF) x1 = fmaf(x1, 0.999f, 0.25f);
+        if (f + 2 < NF) x2 = fmaf(x2, 0.999f, 0.25f);
+        if (f + 3 < NF) x3 = fmaf(x3, 0.999f, 0.25f);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j < NR) a[j] = na[j];
+    }
+  }
+  __syncthreads();
+  record(clk, t0, r0);
+  float s = x0 + x1 + x2 + x3;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += c[j][e];
+  if (s == 1.2345f) sink[t & 255] = s;
+}
+
 // Matrix-core and vector work on the two waves that share a SIMD (512-thread
 // workgroups: waves w and w + 4 run on one SIMD). MODE 0: all eight waves
 // issue products; 1: waves 0-3 issue products, 4-7 nothing; 2: waves 0-3
@@ -528,7 +583,10 @@ extern "C" {
 // chains, 22/23 as 13/14 with the accumulators in architectural VGPRs, 24
 // the SIMD of each wave of 512-thread workgroups (sink[8 * block + wave]),
 // 25-30 matrix-core and vector work on the two waves that share a SIMD
-// (simd_pair_kernel modes 0-5).
+// (simd_pair_kernel modes 0-5), 31-36 tile-loop models (tile_model_kernel:
+// 31 one wave per SIMD, 0.5 KiB LDS + 3.5 FMA per product; 32 two waves per
+// SIMD, 1 KiB + 3.5; 33 as 31 without FMAs; 34 as 31 without LDS; 35 as 32
+// without FMAs; 36 as 32 without LDS).
 // sink: blocks * 256 floats; clk: blocks * 4
 // int64. Returns a hipError_t.
 int ceiling_launch(int kind, int blocks, int iters, float* sink, long long* clk,
@@ -573,6 +631,12 @@ int ceiling_launch(int kind, int blocks, int iters, float* sink, long long* clk,
     case 28: hipLaunchKernelGGL((simd_pair_kernel<3, 2>), g, dim3(512), 0, stream, sink, clk, iters); break;
     case 29: hipLaunchKernelGGL((simd_pair_kernel<4, 8>), g, dim3(512), 0, stream, sink, clk, iters); break;
     case 30: hipLaunchKernelGGL((simd_pair_kernel<5, 2>), g, dim3(512), 0, stream, sink, clk, iters); break;
+    case 31: hipLaunchKernelGGL((tile_model_kernel<2, 14, false>), g, dim3(512), 0, stream, sink, clk, iters); break;
+    case 32: hipLaunchKernelGGL((tile_model_kernel<4, 14, true>), g, dim3(512), 0, stream, sink, clk, iters); break;
+    case 33: hipLaunchKernelGGL((tile_model_kernel<2, 0, false>), g, dim3(512), 0, stream, sink, clk, iters); break;
+    case 34: hipLaunchKernelGGL((tile_model_kernel<0, 14, false>), g, dim3(512), 0, stream, sink, clk, iters); break;
+    case 35: hipLaunchKernelGGL((tile_model_kernel<4, 0, true>), g, dim3(512), 0, stream, sink, clk, iters); break;
+    case 36: hipLaunchKernelGGL((tile_model_kernel<0, 14, true>), g, dim3(512), 0, stream, sink, clk, iters); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
