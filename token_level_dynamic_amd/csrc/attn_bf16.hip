@@ -354,34 +354,59 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
     const uint2 h2 = __builtin_bit_cast(uint2, hi);
     return __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
   };
-  // Row max of one 32-key block in log2 units, and the lazily moved running
-  // max: it only moves when the block max exceeds it by more than kLazy, so
-  // probabilities stay below 2^kLazy and the output is rescaled rarely.
-  // Returns the factor for the output accumulator (1 when unmoved).
-  auto block_max = [&] __device__ (const f32x16& s) __attribute__((always_inline)) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                      false, false);
-    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    mx = PRE ? mx + base : mx * p.scale_log2;
-    const float m_new = mx > m_run + kLazy ? mx : m_run;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
-    return alpha;
-  };
-  // two probabilities: exp2, partial row sum, bf16 pack
-  auto prob_pair = [&] __device__ (float s0, float s1) __attribute__((always_inline)) {
+  // The running max (log2 units) moves lazily: only when a block's max
+  // exceeds it by more than kLazy, so probabilities stay below 2^kLazy and
+  // the output is rescaled rarely.
+  // two probabilities: exp2, this lane's sum over the block, bf16 pack
+  auto prob_pair = [&] __device__ (float s0, float s1, float& bsum)
+      __attribute__((always_inline)) {
     const float p0 = __builtin_amdgcn_exp2f(PRE ? s0 : fmaf(s0, p.scale_log2, -m_run));
     const float p1 = __builtin_amdgcn_exp2f(PRE ? s1 : fmaf(s1, p.scale_log2, -m_run));
-    l_run += p0 + p1;
+    bsum += p0 + p1;
     uint32_t pk = pack_bf16x2(p0, p1);
     // an empty asm that "reads and writes" the result pins the pair where it
     // is written (the optimiser would otherwise cluster all exponentials)
-    asm volatile("" : "+v"(pk), "+v"(l_run));
+    asm volatile("" : "+v"(pk), "+v"(bsum));
     return pk;
+  };
+  // After a block's probabilities were made against the current reference
+  // (the running max; PRE: base or the moved max): the lazy max may only
+  // move if some probability exceeds 2^kLazy, which a lane's block sum at
+  // or below 2^kLazy excludes; so the block max is computed only when some
+  // lane's sum exceeds it (or, PRE, a row gets its first scores). Then the
+  // max moves as before and, where it moved, the probabilities are made
+  // again. Returns the accumulator's rescale factor; adds the block to l.
+  auto settle = [&] __device__ (f32x16& s, uint32_t* pk, float bsum)
+      __attribute__((always_inline)) {
+    const bool unset = !(m_run > 0.5f * kNegInit);
+    float alpha = 1.0f;
+    if (__builtin_amdgcn_ballot_w64(bsum > 256.0f || (PRE && unset && bsum > 0.0f)) != 0) {
+      const float ref = PRE ? (unset ? base : m_run) : 0.0f;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
+                                                        __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      mx = PRE ? mx + ref : mx * p.scale_log2;
+      const float m_new = mx > m_run + kLazy ? mx : m_run;
+      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+      // PRE: the scores are s - ref; where the max is set now, make them s - m
+      const float d = PRE && m_run > 0.5f * kNegInit ? m_run - ref : 0.0f;
+      if (__builtin_amdgcn_ballot_w64(PRE ? d != 0.0f : alpha != 1.0f) != 0) {
+        if (PRE) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s[e] -= d;
+        }
+        bsum = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) pk[c] = prob_pair(s[2 * c], s[2 * c + 1], bsum);
+      }
+    }
+    l_run += bsum;
+    return alpha;
   };
   auto mask_block = [&] __device__ (int key0, f32x16& s, int mode)
       __attribute__((always_inline)) {
@@ -404,8 +429,8 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
   // exponentials need no arithmetic. Rows with no max yet hold only -inf.
   auto shift_block = [&] __device__ (f32x16& s) __attribute__((always_inline)) {
     if (!PRE) return;
-    const float sh = m_run - base;
-    if (__builtin_amdgcn_ballot_w64(m_run > 0.5f * kNegInit && sh != 0.0f) != 0) {
+    const float sh = m_run > 0.5f * kNegInit ? m_run - base : 0.0f;
+    if (__builtin_amdgcn_ballot_w64(sh != 0.0f) != 0) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[e] -= sh;
     }
@@ -453,10 +478,10 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
     for (int s = 0; s < QS; ++s)
       kf1[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow1 + s * 16));
     if (!full) mask_block(key0, sc0, mode);
-    const float alpha0 = block_max(sc0);
     shift_block(sc0);
     __builtin_amdgcn_sched_barrier(0);
     // QK(kb1), 8 pairs of block 0 spread over its QS MFMAs
+    float bsum0 = 0.0f, bsum1 = 0.0f;
 #pragma unroll
     for (int s = 0; s < QS; ++s) {
       sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1[s], qreg[s], s ? sc1 : PRE ? cm : (f32x16){},
@@ -464,13 +489,12 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
 #pragma unroll
       for (int i = 0; i < 8 / QS; ++i) {
         const int c = s * (8 / QS) + i;
-        pk0[c] = prob_pair(sc0[2 * c], sc0[2 * c + 1]);
+        pk0[c] = prob_pair(sc0[2 * c], sc0[2 * c + 1], bsum0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    rescale(alpha0);
+    rescale(settle(sc0, pk0, bsum0));
     if (!full) mask_block(key0 + 32, sc1, mode);
-    const float alpha1 = block_max(sc1);
     shift_block(sc1);
     __builtin_amdgcn_sched_barrier(0);
     // PV(kb0), 8 pairs of block 1 spread over its 2*DB MFMAs
@@ -487,12 +511,12 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
 #pragma unroll
       for (int i = 0; i < 8 / DB; ++i) {
         const int c = db * (8 / DB) + i;
-        pk1[c] = prob_pair(sc1[2 * c], sc1[2 * c + 1]);
+        pk1[c] = prob_pair(sc1[2 * c], sc1[2 * c + 1], bsum1);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     // block 0's products were made before block 1 moved the max
-    rescale(alpha1);
+    rescale(settle(sc1, pk1, bsum1));
     // PV(kb1)
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
