@@ -70,14 +70,19 @@ def input_sha256(*arrays) -> str:
 
 
 def effective_flops(w, idx: np.ndarray) -> dict:
-    """Effective FLOPs of the layer from the realised selection idx [B, k]."""
+    """Effective FLOPs of the layer from the realised selection idx [B, k];
+    `distinct` counts each (query, key) pair once: a selected row's window
+    pairs are part of its prefix (what the single launch computes)."""
     i = np.arange(w.n, dtype=np.float64)
     band_pairs = float(np.minimum(w.window, i + 1).sum())          # per (b, h)
     glob_pairs = [float((idx[b].astype(np.float64) + 1).sum()) for b in range(w.B)]
+    sel_band = [float(np.minimum(w.window, idx[b].astype(np.float64) + 1).sum())
+                for b in range(w.B)]
     per_pair = 4.0 * w.d
     local = per_pair * w.Hq * w.B * band_pairs
     glob = per_pair * w.Hq * sum(glob_pairs)
-    return {"local": local, "global": glob, "total": local + glob}
+    distinct = local + glob - per_pair * w.Hq * sum(sel_band)
+    return {"local": local, "global": glob, "total": local + glob, "distinct": distinct}
 
 
 # The CPU oracle's worker processes: forked in main() before the GPU is
@@ -1048,6 +1053,12 @@ def main() -> int:
             "avg_launch_ms": round(dom_ms, 4) if dom_ms else None,
         },
     }
+    if dom == "fused" and dom_ms:
+        # the single launch derives both outputs of a selected row's window
+        # pairs from one product each: its distinct pair work, and the rate on it
+        result["roofline"]["distinct_pair_flops_per_launch"] = F["distinct"]
+        result["roofline"]["frac_of_distinct_pairs"] = round(
+            F["distinct"] / (dom_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, buf["o"], budget_s=args.cpu_budget)
         result["parity"] = result["cpu_baseline"]["parity"]
