@@ -1006,6 +1006,12 @@ def main() -> int:
         # one launch computes both branches: its FLOPs are the layer's
         dom, dom_flops = "fused", F["total"]
         kname = "attn_bf16_fused_kernel (both branches, one launch)"
+    elif avg.get("pair"):
+        # the local band and the key-range-split global branch in one launch,
+        # then their merge: the layer's FLOPs over both kernels' time
+        dom, dom_flops = "pair", F["total"]
+        kname = ("attn_bf16_pair_kernel + global_merge_kernel (both branches, one launch, "
+                 "split key ranges)")
     else:
         dom = "global" if F["global"] >= F["local"] else "local"
         dom_flops = F[dom]

@@ -155,8 +155,9 @@ logo_status logo_combine(const logo_problem* p, const float* o_local,
  * rounding order. Two bf16 forms take another order and then agree with
  * those calls to the bf16 parity tolerance rather than bit for bit: a
  * global branch split into key ranges (see logo_workspace_size), where each
- * range rounds its probabilities to bf16 against its own running maximum;
- * and the single launch (see logo_workspace_size for when it applies),
+ * range rounds its probabilities to bf16 against its own running maximum
+ * (such a problem runs the split global branch and the local branch in one
+ * launch, then merges the ranges); and the single launch (see logo_workspace_size for when it applies),
  * where one kernel does every row: a selected row walks its causal prefix
  * once, from the diagonal down, its window's keys first, so the running
  * state after the window is its local output and at the end its global
@@ -377,7 +378,9 @@ const char* logo_last_error(void);
  * logo_forward_routed and logo_decode_step. logo_profile_end() waits for those events and writes,
  * per stage (0 select, 1 local, 2 global, 3 combine, 4 backward row terms and
  * dgate, 5 backward dk/dv, 6 backward dq, 7 router logits, 8 decode: chunk
- * partials and their reduction, 9 both attention branches in one launch),
+ * partials and their reduction, 9 both attention branches in one launch,
+ * 10 the local band and the key-range-split global branch in one launch
+ * plus their merge),
  * the summed milliseconds
  * and the number of launches into arrays of `n_stages` entries. */
 logo_status logo_profile_begin(void);

@@ -27,7 +27,7 @@ LOGO_ERR_HIP = 4
 LOGO_F32 = 0
 LOGO_BF16 = 1
 STAGES = ("select", "local", "global", "combine", "bwd_prep", "bwd_dkdv", "bwd_dq",
-          "router", "decode", "fused")
+          "router", "decode", "fused", "pair")
 
 
 class LogoError(RuntimeError):

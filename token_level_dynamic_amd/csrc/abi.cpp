@@ -378,6 +378,13 @@ logo_status logo_forward(const logo_problem* p, const void* q, const void* k, co
       a.split_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                               scratch_only_bytes(d) + queue_bytes(d));
   }
+  if (a.split_part && logo::attn_bf16_pair_ok(d)) {
+    // split global branch and local band in one launch, then the merge
+    StageTimer tm(10, s);
+    e = logo::launch_attn_bf16_pair(d, a, s);
+    if (e != hipSuccess) return hip_fail(e, "paired attention launch");
+    return LOGO_OK;
+  }
   {
     StageTimer tm(1, s);
     e = run_attn(d, logo::Epi::LocalFused, a, s);

@@ -820,6 +820,39 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_fused_kernel(Params pg
     attn_block<D, false, 7, false>(pl, unit, rank, 0, K0, K1, V0, V1);
 }
 
+// Small problems (the global branch split over key ranges): the split global
+// branch (EPI 3, partials) and the local band (EPI 1) in one grid, global
+// workgroups first; neither reads the other's results, and a merge kernel
+// combines them after. Each part keeps its own XCD-aware order (the global
+// part's grid is a multiple of 8, so the local part's workgroups are dealt
+// to the XCDs as in a launch of their own).
+template <int D>
+__global__ __launch_bounds__(kThreads, 2)
+__attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_pair_kernel(Params pg, Params pl,
+                                                                      int g_grid) {
+  using SM = Smem<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t K0[SM::kElems];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[SM::kElems];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[SM::vElems];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[SM::vElems];
+  const int bid = blockIdx.x;
+  if (bid < g_grid) {
+    const int Lx = (bid % kNumXcd) * pg.per_xcd + bid / kNumXcd;
+    if (Lx >= pg.total_wg * pg.nsplit) return;
+    const int split = Lx % pg.nsplit;
+    const int L = Lx / pg.nsplit;
+    attn_block<D, true, 3, false>(pg, L / pg.wg_per_unit,
+                                  pg.wg_per_unit - 1 - L % pg.wg_per_unit, split, K0, K1, V0,
+                                  V1);
+  } else {
+    const int b2 = bid - g_grid;
+    const int Lx = (b2 % kNumXcd) * pl.per_xcd + b2 / kNumXcd;
+    if (Lx >= pl.total_wg) return;
+    attn_block<D, false, 1, false>(pl, Lx / pl.wg_per_unit, Lx % pl.wg_per_unit, 0, K0, K1, V0,
+                                   V1);
+  }
+}
+
 // Work order of the global branch's workgroups over packed examples: the
 // keys a workgroup streams (from its first row's example start to its last
 // row) estimate its work; slots are bucketed by that estimate (1024 buckets,
@@ -1047,11 +1080,13 @@ size_t attn_bf16_sched_ints(const Dims& d, bool packed) {
   return (packed ? (units + kWaves - 1) / kWaves : 0) + (size_t)d.B * d.Hkv;
 }
 
-hipError_t launch_attn_bf16(const Dims& d, Epi epi, const AttnArgs& a, hipStream_t s) {
+namespace {
+
+// The launch parameters of one branch (everything but the work queues).
+Params branch_params(const Dims& d, Epi epi, const AttnArgs& a) {
   const bool global =
       epi == Epi::GlobalAll || epi == Epi::GlobalFused || epi == Epi::GlobalRouted;
   const int R = global ? d.k : d.n;
-  if (d.B == 0 || R == 0) return hipSuccess;
   Params prm;
   prm.q = static_cast<const uint16_t*>(a.q);
   prm.k = static_cast<const uint16_t*>(a.k);
@@ -1095,6 +1130,27 @@ hipError_t launch_attn_bf16(const Dims& d, Epi epi, const AttnArgs& a, hipStream
     else prm.nsplit = 1;
   }
   prm.per_xcd = (prm.total_wg * prm.nsplit + kNumXcd - 1) / kNumXcd;
+  return prm;
+}
+
+template <int D>
+hipError_t launch_merge(const Dims& d, const AttnArgs& a, const Params& prm, hipStream_t s) {
+  const long long rows = (long long)d.B * d.Hq * d.k;
+  const dim3 mgrid((unsigned)((rows + 3) / 4));
+  hipLaunchKernelGGL(global_merge_kernel<D>, mgrid, dim3(256), 0, s, prm.part, prm.nsplit, d.B,
+                     d.Hq, d.k, d.n, a.idx, a.gate, a.scratch, prm.out_io, d.vo);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_bf16(const Dims& d, Epi epi, const AttnArgs& a, hipStream_t s) {
+  const bool global =
+      epi == Epi::GlobalAll || epi == Epi::GlobalFused || epi == Epi::GlobalRouted;
+  const int R = global ? d.k : d.n;
+  if (d.B == 0 || R == 0) return hipSuccess;
+  Params prm = branch_params(d, epi, a);
+  const int G = d.Hq / d.Hkv;
   if (global && a.sched && prm.nsplit == 1) {
     // the queues' counters are zeroed by a kernel on the stream (no memset
     // node, so the sequence can be captured in a graph)
@@ -1117,15 +1173,30 @@ hipError_t launch_attn_bf16(const Dims& d, Epi epi, const AttnArgs& a, hipStream
   else if (d.d == 128) e = dispatch_epi<128>(epi, prm, s);
   else return hipErrorInvalidValue;
   if (e != hipSuccess || prm.nsplit == 1) return e;
-  const long long rows = (long long)d.B * d.Hq * d.k;
-  const dim3 mgrid((unsigned)((rows + 3) / 4));
+  return d.d == 64 ? launch_merge<64>(d, a, prm, s) : launch_merge<128>(d, a, prm, s);
+}
+
+bool attn_bf16_pair_ok(const Dims& d) {
+  return d.dtype == 1 && d.k > 0 && (d.d == 64 || d.d == 128) && attn_bf16_splits(d) > 1;
+}
+
+hipError_t launch_attn_bf16_pair(const Dims& d, const AttnArgs& a, hipStream_t s) {
+  if (d.B == 0 || d.k == 0) return hipSuccess;
+  if (!a.split_part || a.seg_start || a.lse_out || a.og_out) return hipErrorInvalidValue;
+  const Params pg = branch_params(d, Epi::GlobalFused, a);
+  const Params pl = branch_params(d, Epi::LocalFused, a);
+  if (pg.nsplit < 2) return hipErrorInvalidValue;
+  const int g_grid = pg.per_xcd * kNumXcd;
+  const int grid = g_grid + pl.per_xcd * kNumXcd;
   if (d.d == 64)
-    hipLaunchKernelGGL(global_merge_kernel<64>, mgrid, dim3(256), 0, s, prm.part, prm.nsplit,
-                       d.B, d.Hq, d.k, d.n, a.idx, a.gate, a.scratch, prm.out_io, d.vo);
+    hipLaunchKernelGGL(attn_bf16_pair_kernel<64>, dim3(grid), dim3(kThreads), 0, s, pg, pl,
+                       g_grid);
   else
-    hipLaunchKernelGGL(global_merge_kernel<128>, mgrid, dim3(256), 0, s, prm.part, prm.nsplit,
-                       d.B, d.Hq, d.k, d.n, a.idx, a.gate, a.scratch, prm.out_io, d.vo);
-  return hipGetLastError();
+    hipLaunchKernelGGL(attn_bf16_pair_kernel<128>, dim3(grid), dim3(kThreads), 0, s, pg, pl,
+                       g_grid);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return d.d == 64 ? launch_merge<64>(d, a, pg, s) : launch_merge<128>(d, a, pg, s);
 }
 
 }  // namespace logo

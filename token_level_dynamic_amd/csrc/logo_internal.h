@@ -128,6 +128,11 @@ bool attn_bf16_fused_ok(const Dims& d);
 hipError_t launch_attn_bf16_fused(const Dims& d, const AttnArgs& a, const int32_t* nidx,
                                   hipStream_t s);
 size_t attn_bf16_split_floats(const Dims& d);
+// Problems whose global branch is split over key ranges (attn_bf16_splits(d)
+// > 1): the split global branch and the local band in one launch, then the
+// merge (a.split_part, a.scratch and a.out_f32 as for the two launches).
+bool attn_bf16_pair_ok(const Dims& d);
+hipError_t launch_attn_bf16_pair(const Dims& d, const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_bf16(const Dims& d, Epi epi, const AttnArgs& a,
                             hipStream_t s);
 
