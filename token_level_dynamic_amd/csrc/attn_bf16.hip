@@ -169,12 +169,6 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
   using SM = Smem<D>;
   // rows come from a position list (idx) rather than being 0..n-1
   constexpr bool GATHER = GLOBAL || EPI == 7;
-  // The single launch at d = 128 (EPI 6, 7) takes the softmax scale into Q (rounded to
-  // bf16 after scaling) and starts each score product from -base, the row's
-  // running max as of its last change: the products are then the
-  // exponents themselves, and the per-score scale-and-subtract disappears
-  // from every tile on which the running max does not move.
-  constexpr bool PRE = (EPI == 6 || EPI == 7) && D == 128;
   // the walk goes from the diagonal down to key 0
   constexpr bool BACKWARD = EPI == 6;
   const int b = unit_bh / p.Hkv;
@@ -256,22 +250,6 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
                    : make_uint4(0, 0, 0, 0);
       qreg[s] = __builtin_bit_cast(bf16x8, x);
     }
-    if (PRE) {
-      // q * scale * log2(e), rounded to bf16 (nearest even): the products
-      // then come out in log2 units
-#pragma unroll
-      for (int s = 0; s < QS; ++s) {
-        bf16x8 y;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const f32x2 f = {(float)qreg[s][e] * p.scale_log2, (float)qreg[s][e + 1] * p.scale_log2};
-          const bf16x2 r = __builtin_convertvector(f, bf16x2);
-          y[e] = r[0];
-          y[e + 1] = r[1];
-        }
-        qreg[s] = y;
-      }
-    }
   }
 
   // ---- tile staging: buffer loads straight into LDS ----------------------
@@ -317,10 +295,6 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc_o[i] = (f32x16){};
   float m_run = kNegInit;   // running row max, log2 units
-  // PRE: the scores come out of the products less `base` (cm = -base in
-  // every element); 0 until the row's max is first set
-  float base = 0.0f;
-  f32x16 cm = {};
   float l_run = 0.0f;       // this lane's half of the row sum
   bool snapped = false;     // EPI 6: this lane's local output is parked
 
@@ -357,49 +331,47 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
   // The running max (log2 units) moves lazily: only when a block's max
   // exceeds it by more than kLazy, so probabilities stay below 2^kLazy and
   // the output is rescaled rarely.
-  // two probabilities: exp2, this lane's sum over the block, bf16 pack
+  // two probabilities: exp2, bf16 pack, this lane's sum over the block. The
+  // sum adds the rounded values the P V products use (a dot product with
+  // (1, 1)), so the output is a weighted mean of V rows with exactly those
+  // weights: with a lazy max the largest probability is not 1 but up to
+  // 2^kLazy, and its rounding would otherwise bias every element of o by
+  // up to 2^-9 of the dominant V row.
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   auto prob_pair = [&] __device__ (float s0, float s1, float& bsum)
       __attribute__((always_inline)) {
-    const float p0 = __builtin_amdgcn_exp2f(PRE ? s0 : fmaf(s0, p.scale_log2, -m_run));
-    const float p1 = __builtin_amdgcn_exp2f(PRE ? s1 : fmaf(s1, p.scale_log2, -m_run));
-    bsum += p0 + p1;
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(s0, p.scale_log2, -m_run));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(s1, p.scale_log2, -m_run));
     uint32_t pk = pack_bf16x2(p0, p1);
+    bsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, bsum, false);
     // an empty asm that "reads and writes" the result pins the pair where it
     // is written (the optimiser would otherwise cluster all exponentials)
     asm volatile("" : "+v"(pk), "+v"(bsum));
     return pk;
   };
-  // After a block's probabilities were made against the current reference
-  // (the running max; PRE: base or the moved max): the lazy max may only
-  // move if some probability exceeds 2^kLazy, which a lane's block sum at
-  // or below 2^kLazy excludes; so the block max is computed only when some
-  // lane's sum exceeds it (or, PRE, a row gets its first scores). Then the
-  // max moves as before and, where it moved, the probabilities are made
-  // again. Returns the accumulator's rescale factor; adds the block to l.
+  // After a block's probabilities were made against the running max: the
+  // lazy max may only move if some probability exceeds 2^kLazy, which a
+  // lane's block sum at or below 2^kLazy excludes; so the block max is
+  // computed only when some lane's sum exceeds it. A row without a max yet
+  // (m_run = kNegInit) gets infinite probabilities for every unmasked key
+  // and so always takes this path; a fully masked block leaves it unset.
+  // Then the max moves as before and, where it moved, the probabilities are
+  // made again. Returns the accumulator's rescale factor; adds the block to l.
   auto settle = [&] __device__ (f32x16& s, uint32_t* pk, float bsum)
       __attribute__((always_inline)) {
-    const bool unset = !(m_run > 0.5f * kNegInit);
     float alpha = 1.0f;
-    if (__builtin_amdgcn_ballot_w64(bsum > 256.0f || (PRE && unset && bsum > 0.0f)) != 0) {
-      const float ref = PRE ? (unset ? base : m_run) : 0.0f;
+    if (__builtin_amdgcn_ballot_w64(bsum > 256.0f) != 0) {
       float mx = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
                                                         __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      mx = PRE ? mx + ref : mx * p.scale_log2;
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * p.scale_log2;
       const float m_new = mx > m_run + kLazy ? mx : m_run;
       alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
-      // PRE: the scores are s - ref; where the max is set now, make them s - m
-      const float d = PRE && m_run > 0.5f * kNegInit ? m_run - ref : 0.0f;
-      if (__builtin_amdgcn_ballot_w64(PRE ? d != 0.0f : alpha != 1.0f) != 0) {
-        if (PRE) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) s[e] -= d;
-        }
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
         bsum = 0.0f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) pk[c] = prob_pair(s[2 * c], s[2 * c + 1], bsum);
@@ -422,26 +394,6 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
         if (!GLOBAL || EPI == 6) ok = ok && key >= lb;
       }
       s[e] = ok ? s[e] : -INFINITY;
-    }
-  };
-  // PRE: a block's scores are s - base; where the row's max has moved away
-  // from base (rare: the max is lazy), take the difference off here so the
-  // exponentials need no arithmetic. Rows with no max yet hold only -inf.
-  auto shift_block = [&] __device__ (f32x16& s) __attribute__((always_inline)) {
-    if (!PRE) return;
-    const float sh = m_run > 0.5f * kNegInit ? m_run - base : 0.0f;
-    if (__builtin_amdgcn_ballot_w64(sh != 0.0f) != 0) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[e] -= sh;
-    }
-  };
-  // PRE, after a tile: the products of the next start from -m_run
-  auto rebase = [&] __device__ () __attribute__((always_inline)) {
-    if (!PRE) return;
-    if (__builtin_amdgcn_ballot_w64(m_run > 0.5f * kNegInit && m_run != base) != 0) {
-      base = m_run > 0.5f * kNegInit ? m_run : base;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) cm[e] = -base;
     }
   };
   auto rescale = [&] __device__ (float alpha) __attribute__((always_inline)) {
@@ -469,7 +421,7 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
         kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + s * 16));
 #pragma unroll
       for (int s = 0; s < QS; ++s)
-        sc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qreg[s], s ? sc0 : PRE ? cm : (f32x16){},
+        sc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qreg[s], s ? sc0 : (f32x16){},
                                                        0, 0, 0);
     }
     const uint16_t* krow1 = ks + (32 + col) * SM::kStride + half * 8;
@@ -478,13 +430,12 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
     for (int s = 0; s < QS; ++s)
       kf1[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow1 + s * 16));
     if (!full) mask_block(key0, sc0, mode);
-    shift_block(sc0);
     __builtin_amdgcn_sched_barrier(0);
     // QK(kb1), 8 pairs of block 0 spread over its QS MFMAs
     float bsum0 = 0.0f, bsum1 = 0.0f;
 #pragma unroll
     for (int s = 0; s < QS; ++s) {
-      sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1[s], qreg[s], s ? sc1 : PRE ? cm : (f32x16){},
+      sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1[s], qreg[s], s ? sc1 : (f32x16){},
                                                      0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 8 / QS; ++i) {
@@ -495,7 +446,6 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
     }
     rescale(settle(sc0, pk0, bsum0));
     if (!full) mask_block(key0 + 32, sc1, mode);
-    shift_block(sc1);
     __builtin_amdgcn_sched_barrier(0);
     // PV(kb0), 8 pairs of block 1 spread over its 2*DB MFMAs
 #pragma unroll
@@ -529,7 +479,6 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
           v1, __builtin_bit_cast(bf16x8, make_uint4(pk1[4], pk1[5], pk1[6], pk1[7])), acc_o[db],
           0, 0, 0);
     }
-    rebase();
   };
   // EPI 6: rows whose window's lowest key lies in tile t have now seen
   // exactly their window: park acc / l (float32) in the row's scratch row.

@@ -652,16 +652,20 @@ __global__ __launch_bounds__(kStWaves * 64, 1) void decode_stream_kernel(StParam
 #pragma unroll
       for (int j = 0; j < DBW; ++j) acc[j] *= alpha;
     }
+    // the row sum adds the bf16 values the products use (a dot product with
+    // (1, 1)): with the lazy max a probability can reach 2^kLazy, and the
+    // sum of the unrounded values would bias o by that weight's rounding
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       float pr[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < 4; ++e)
         pr[e] = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], p.scale_log2, -m_run));
-        l_run += pr[e];
-      }
-      const bf16x4 pt = __builtin_bit_cast(
-          bf16x4, make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])));
+      const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p01), ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p23), ones, l_run, false);
+      const bf16x4 pt = __builtin_bit_cast(bf16x4, make_uint2(p01, p23));
 #pragma unroll
       for (int j = 0; j < DBW; ++j)
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(read_v(tb, kb, wave * DBW + j), pt,
