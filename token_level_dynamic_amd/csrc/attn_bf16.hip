@@ -419,6 +419,9 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
 #pragma unroll
       for (int s = 0; s < QS; ++s)
         kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + s * 16));
+      // all eight reads in flight before the first product (otherwise they
+      // are issued two at a time, each pair waited for)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < QS; ++s)
         sc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qreg[s], s ? sc0 : (f32x16){},
@@ -444,19 +447,25 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    // V fragments are read one d block ahead of their products (the last
+    // reads of PV(kb0) fetch the first of PV(kb1)), so no product waits on
+    // the LDS read issued just before it; the first two are read before
+    // block 0 settles
+    bf16x8 va0 = read_vf(vs, 0, 0, 0), va1 = read_vf(vs, 0, 1, 0);
     rescale(settle(sc0, pk0, bsum0));
     if (!full) mask_block(key0 + 32, sc1, mode);
     __builtin_amdgcn_sched_barrier(0);
     // PV(kb0), 8 pairs of block 1 spread over its 2*DB MFMAs
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const bf16x8 v0 = read_vf(vs, 0, 0, db);
-      const bf16x8 v1 = read_vf(vs, 0, 1, db);
+      const int nkb = db + 1 < DB ? 0 : 1, ndb = db + 1 < DB ? db + 1 : 0;
+      const bf16x8 vn0 = read_vf(vs, nkb, 0, ndb);
+      const bf16x8 vn1 = read_vf(vs, nkb, 1, ndb);
       acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          v0, __builtin_bit_cast(bf16x8, make_uint4(pk0[0], pk0[1], pk0[2], pk0[3])), acc_o[db],
+          va0, __builtin_bit_cast(bf16x8, make_uint4(pk0[0], pk0[1], pk0[2], pk0[3])), acc_o[db],
           0, 0, 0);
       acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          v1, __builtin_bit_cast(bf16x8, make_uint4(pk0[4], pk0[5], pk0[6], pk0[7])), acc_o[db],
+          va1, __builtin_bit_cast(bf16x8, make_uint4(pk0[4], pk0[5], pk0[6], pk0[7])), acc_o[db],
           0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 8 / DB; ++i) {
@@ -464,20 +473,28 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
         pk1[c] = prob_pair(sc1[2 * c], sc1[2 * c + 1], bsum1);
       }
       __builtin_amdgcn_sched_barrier(0);
+      va0 = vn0;
+      va1 = vn1;
     }
     // block 0's products were made before block 1 moved the max
     rescale(settle(sc1, pk1, bsum1));
     // PV(kb1)
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const bf16x8 v0 = read_vf(vs, 1, 0, db);
-      const bf16x8 v1 = read_vf(vs, 1, 1, db);
+      bf16x8 vn0 = va0, vn1 = va1;
+      if (db + 1 < DB) {
+        vn0 = read_vf(vs, 1, 0, db + 1);
+        vn1 = read_vf(vs, 1, 1, db + 1);
+      }
       acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          v0, __builtin_bit_cast(bf16x8, make_uint4(pk1[0], pk1[1], pk1[2], pk1[3])), acc_o[db],
+          va0, __builtin_bit_cast(bf16x8, make_uint4(pk1[0], pk1[1], pk1[2], pk1[3])), acc_o[db],
           0, 0, 0);
       acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          v1, __builtin_bit_cast(bf16x8, make_uint4(pk1[4], pk1[5], pk1[6], pk1[7])), acc_o[db],
+          va1, __builtin_bit_cast(bf16x8, make_uint4(pk1[4], pk1[5], pk1[6], pk1[7])), acc_o[db],
           0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      va0 = vn0;
+      va1 = vn1;
     }
   };
   // EPI 6: rows whose window's lowest key lies in tile t have now seen
