@@ -18,7 +18,7 @@ import token_level_dynamic_amd as T
 import oracle_pool as OP
 from gpu_util import ensure_built, gather_rows, host, problem, run_forward, say, single_launch, \
     to_dev
-from workloads import get_workload, make_inputs
+from workloads import get_workload, make_far_below, make_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -94,20 +94,12 @@ FAR_BELOW = {
 
 @pytest.mark.parametrize("name", sorted(FAR_BELOW))
 def test_single_launch_scores_far_below_zero(name):
-    from workloads import bf16_bits, bits_to_f32
     base, over = FAR_BELOW[name]
     w = get_workload(base, **over)
     p = problem(w)
     assert single_launch(p), "case does not take the single launch"
-    inp = make_inputs(w, 3)
+    inp = make_far_below(make_inputs(w, 3))
     G = w.Hq // w.Hkv
-    rng = np.random.default_rng(11)
-    q = inp.q.copy()
-    k = inp.k.copy()
-    q[:, :G] = 8.0 + 0.5 * rng.standard_normal(q[:, :G].shape, dtype=np.float32)
-    k[:, 0] = -8.0 + 0.5 * rng.standard_normal(k[:, 0].shape, dtype=np.float32)
-    inp.q_bits, inp.k_bits = bf16_bits(q), bf16_bits(k)
-    inp.q, inp.k = bits_to_f32(inp.q_bits), bits_to_f32(inp.k_bits)
     say(f"[single] {name}: {w}")
     qd, kd, vd, gate = to_dev(inp)
     got = run_forward(p, qd, kd, vd, gate)

@@ -41,6 +41,7 @@ __all__ = [
     "round_to_bf16",
     "bf16_bits",
     "make_inputs",
+    "make_far_below",
     "bursty_gate_runs",
 ]
 
@@ -196,6 +197,26 @@ VARLEN_WORKLOADS = {
     "varlen64k": dict(lens=[32768, 16384, 8192, 4096, 2048, 1024, 512, 256, 256], Hq=16, Hkv=4,
                       d=128, window=1024, rho=0.2, dtype="bf16"),
 }
+
+
+def make_far_below(inp: Inputs, seed: int = 11) -> Inputs:
+    """Inputs whose kv group 0 has every score far below zero: the query
+    heads of group 0 get entries 8 + 0.5 N(0,1) and kv head 0's keys
+    -8 + 0.5 N(0,1) (then bf16-rounded like every bf16 input), so the scaled
+    scores sit near -1000 in log2 units at d = 128 and the query norm is
+    eight times the standard draw's. Other heads, v and the gate are kept."""
+    w = inp.workload
+    G = w.Hq // w.Hkv
+    rng = np.random.default_rng(seed)
+    q = inp.q.copy()
+    k = inp.k.copy()
+    q[:, :G] = 8.0 + 0.5 * rng.standard_normal(q[:, :G].shape, dtype=np.float32)
+    k[:, 0] = -8.0 + 0.5 * rng.standard_normal(k[:, 0].shape, dtype=np.float32)
+    out = Inputs(w, inp.seed, q, k, inp.v, inp.gate)
+    if w.dtype == "bf16":
+        out.q_bits, out.k_bits, out.v_bits = bf16_bits(q), bf16_bits(k), inp.v_bits
+        out.q, out.k = bits_to_f32(out.q_bits), bits_to_f32(out.k_bits)
+    return out
 
 
 def make_varlen_inputs(lens, Hq, Hkv, d, dtype="bf16", seed=0):
