@@ -430,7 +430,10 @@ def ceilings(torch) -> int:
              33: ("tile model, 1 wave/SIMD: 0.5 KiB LDS per product", 4 * 32768.0, "flop"),
              34: ("tile model, 1 wave/SIMD: 3.5 FMA per product", 4 * 32768.0, "flop"),
              35: ("tile model, 2 waves/SIMD: 1 KiB LDS per product", 2 * 4 * 32768.0, "flop"),
-             36: ("tile model, 2 waves/SIMD: 3.5 FMA per product", 2 * 4 * 32768.0, "flop")}
+             36: ("tile model, 2 waves/SIMD: 3.5 FMA per product", 2 * 4 * 32768.0, "flop"),
+             37: ("8 waves: products in 0-3, 4 v_dot2_f32_bf16 per product in 4-7",
+                  4 * 32768.0, "flop"),
+             38: ("8 waves: products in 0-3, 4 FMA per product in 4-7", 4 * 32768.0, "flop")}
     if only:
         kinds = {k: v for k, v in kinds.items() if str(k) in only.split(",")}
     out = {}

@@ -499,7 +499,8 @@ __global__ __launch_bounds__(512) void tile_model_kernel(float* sink, long long*
 // issue products; 1: waves 0-3 issue products, 4-7 nothing; 2: waves 0-3
 // products, 4-7 NV rounds of 4 independent FMA chains per iteration; 3: as 2
 // with v_exp_f32 chains; 4: waves 0-3 products and the FMA rounds in the same
-// wave, 4-7 nothing; 5: as 4 with v_exp_f32. Per iteration a product wave
+// wave, 4-7 nothing; 5: as 4 with v_exp_f32; 6: as 2 with v_dot2_f32_bf16
+// chains. Per iteration a product wave
 // issues 4 v_mfma_f32_32x32x16_bf16 (4 x 32 cycles of one SIMD's matrix core).
 template <int MODE, int NV>
 __global__ __launch_bounds__(512) void simd_pair_kernel(float* sink, long long* clk, int iters) {
@@ -529,6 +530,19 @@ __global__ __launch_bounds__(512) void simd_pair_kernel(float* sink, long long* 
       x3 = __builtin_amdgcn_exp2f(-x3);
     }
   };
+  // v_dot2_f32_bf16 of a packed pair with (1, 1): the attention kernels' row sums
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const bf16x2 pr = __builtin_bit_cast(bf16x2, bf16_pair(t + 7));
+  auto dot_round = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      x0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, x0, false);
+      x1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, x1, false);
+      x2 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, x2, false);
+      x3 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, x3, false);
+    }
+  };
   auto mfma_round = [&]() __attribute__((always_inline)) {
     c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
     c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c1, 0, 0, 0);
@@ -551,6 +565,9 @@ __global__ __launch_bounds__(512) void simd_pair_kernel(float* sink, long long* 
   } else if (MODE == 3) {
 #pragma unroll 1
     for (int i = 0; i < iters; ++i) exp_round();
+  } else if (MODE == 6) {
+#pragma unroll 1
+    for (int i = 0; i < iters; ++i) dot_round();
   }
   __syncthreads();
   record(clk, t0, r0);
@@ -586,7 +603,9 @@ extern "C" {
 // (simd_pair_kernel modes 0-5), 31-36 tile-loop models (tile_model_kernel:
 // 31 one wave per SIMD, 0.5 KiB LDS + 3.5 FMA per product; 32 two waves per
 // SIMD, 1 KiB + 3.5; 33 as 31 without FMAs; 34 as 31 without LDS; 35 as 32
-// without FMAs; 36 as 32 without LDS).
+// without FMAs; 36 as 32 without LDS), 37/38 products in waves 0-3 beside 4
+// v_dot2_f32_bf16 / 4 FMA per product in waves 4-7 (simd_pair_kernel modes
+// 6 and 2).
 // sink: blocks * 256 floats; clk: blocks * 4
 // int64. Returns a hipError_t.
 int ceiling_launch(int kind, int blocks, int iters, float* sink, long long* clk,
@@ -637,6 +656,8 @@ int ceiling_launch(int kind, int blocks, int iters, float* sink, long long* clk,
     case 34: hipLaunchKernelGGL((tile_model_kernel<0, 14, false>), g, dim3(512), 0, stream, sink, clk, iters); break;
     case 35: hipLaunchKernelGGL((tile_model_kernel<4, 0, true>), g, dim3(512), 0, stream, sink, clk, iters); break;
     case 36: hipLaunchKernelGGL((tile_model_kernel<0, 14, true>), g, dim3(512), 0, stream, sink, clk, iters); break;
+    case 37: hipLaunchKernelGGL((simd_pair_kernel<6, 4>), g, dim3(512), 0, stream, sink, clk, iters); break;
+    case 38: hipLaunchKernelGGL((simd_pair_kernel<2, 4>), g, dim3(512), 0, stream, sink, clk, iters); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
