@@ -352,12 +352,20 @@ logo_status logo_decode_step(const logo_decode_problem* p, const void* q,
 int64_t logo_varlen_selected_count(double rho, const int32_t* cu_seqlens_host,
                                    int64_t n_examples);
 
-/* Workspace of logo_forward_varlen: 16 B per example, 4 B per token and the
- * float32 local outputs of the selected rows (Hq*K*d*4), each 256-aligned. */
+/* Workspace of logo_forward_varlen: 16 B per example, 4 B per token, the
+ * float32 local outputs of the selected rows (Hq*K*d*4), the bf16 work
+ * order, and, where the single launch runs the stream, 4 B per unselected
+ * token; each part 256-aligned. */
 logo_status logo_varlen_workspace_size(const logo_problem* p, int64_t n_examples,
                                        int64_t total_selected, size_t* bytes);
 
-/* The forward over a packed batch (cu_seqlens is a device pointer). */
+/* The forward over a packed batch (cu_seqlens is a device pointer). Where
+ * logo_forward would take its single launch for a stream of this size
+ * (bf16, d in {64, 128}, K > 0, no key-range split, Hkv a multiple or a
+ * divisor of 8), so does this call: the selection also lists the unselected
+ * tokens, and one launch computes every row, the selected ones walking their
+ * example's prefix once for both branches (results then agree with the two
+ * launches to the parity tolerance, not bit for bit). */
 logo_status logo_forward_varlen(const logo_problem* p, const int32_t* cu_seqlens,
                                 int64_t n_examples, int64_t total_selected,
                                 const void* q, const void* k, const void* v,

@@ -139,3 +139,65 @@ def test_varlen_full_64k():
         worst = max(worst, float(np.abs(vals - ref["o_rows"]).max()))
     say(f"  sampled rows max_abs={worst:.3e}")
     assert worst <= TOL["bf16"]
+
+
+def _takes_single_launch(Hq, Hkv, d, Tn, K, dtype):
+    """logo_forward_varlen's single launch applies as logo_forward's does
+    (include/logo.h): bf16, d in {64, 128}, something selected, no key-range
+    split (512 or more row-block workgroups, or too few keys to split), and
+    Hkv a multiple or a divisor of 8."""
+    if dtype != "bf16" or K == 0 or d not in (64, 128):
+        return False
+    wg = Hkv * -(-(-(-K // 32) * (Hq // Hkv)) // 4)
+    if wg < 512 and min(8, -(-512 // wg), (-(-Tn // 64)) // 4) >= 2:
+        return False
+    return Hkv % 8 == 0 or 8 % Hkv == 0
+
+
+# Packed streams that take the single launch: every row of three query heads
+# of every example is compared with the oracle (run per example, as the
+# sequences they are), so example starts inside row blocks, inside tiles and
+# inside a selected row's window all occur, with empty and one-token examples.
+SINGLE = {
+    "single_d128": dict(lens=[3001, 1, 700, 0, 64, 2500, 33, 1900, 2, 1999], Hq=32, Hkv=8,
+                        d=128, window=500, rho=0.2),
+    "single_d64": dict(lens=[4095, 7, 1, 2100, 1, 129, 1800], Hq=16, Hkv=16, d=64,
+                       window=300, rho=0.5),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SINGLE))
+def test_varlen_single_launch_matches_oracle(name):
+    import oracle_pool as OP
+    cfg = SINGLE[name]
+    inp = make_varlen_inputs(cfg["lens"], cfg["Hq"], cfg["Hkv"], cfg["d"], "bf16", seed=4)
+    cu = inp["cu"]
+    Tn = int(cu[-1])
+    K = T.logo_varlen_selected_count(cfg["rho"], cu)
+    assert _takes_single_launch(cfg["Hq"], cfg["Hkv"], cfg["d"], Tn, K, "bf16")
+    say(f"[varlen single] {name}: lens={cfg['lens']} K={K}")
+    got = run_varlen(inp, cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["window"], cfg["rho"], "bf16")
+    G = cfg["Hq"] // cfg["Hkv"]
+    heads = sorted({0, G - 1, cfg["Hq"] - 1})
+    worst = 0.0
+    for e in range(len(cfg["lens"])):
+        a, b = int(cu[e]), int(cu[e + 1])
+        if b == a:
+            continue
+        g = np.ascontiguousarray(inp["gate"][a:b][None])
+        rm, ri, _ = oracle.select_queries(g, cfg["rho"])
+        assert np.array_equal(got["mask"][a:b], rm[0]), e
+        sel = got["idx"][(got["idx"] >= a) & (got["idx"] < b)] - a
+        assert np.array_equal(sel, ri[0]), e
+        rows = [(0, h, i) for h in heads for i in range(b - a)]
+        with OP.SharedInputs(q=np.ascontiguousarray(inp["q"][None, :, a:b]),
+                             k=np.ascontiguousarray(inp["k"][None, :, a:b]),
+                             v=np.ascontiguousarray(inp["v"][None, :, a:b]), gate=g) as sh:
+            parts = OP.map_chunks(sh, "oracle.forward_rows",
+                                  lambda c: ("@q", "@k", "@v", "@gate", cfg["window"],
+                                             cfg["rho"], list(c)), rows, chunk=256)
+        ref = np.concatenate([x["o_rows"] for x in parts])
+        vals = np.stack([got["o"][h, a + i] for _, h, i in rows])
+        worst = max(worst, float(np.abs(vals - ref).max()))
+    say(f"  {len(heads)} heads x {Tn} tokens, max_abs={worst:.3e}")
+    assert worst <= TOL["bf16"]

@@ -803,7 +803,8 @@ logo_status logo_select_threshold(const logo_problem* p, const float* gate, cons
 // float32 local outputs of the selected rows and the global branch's
 // workgroup order.
 struct VarlenWs {
-  size_t seg, seg_start, scratch, sched, total;
+  size_t seg, seg_start, scratch, sched, nidx, total;
+  bool fused;   // the single launch runs the stream (nidx: its unselected positions)
 };
 VarlenWs varlen_ws(const logo::Dims& d, int64_t E, int64_t K) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -814,7 +815,9 @@ VarlenWs varlen_ws(const logo::Dims& d, int64_t E, int64_t K) {
   w.sched = w.scratch + up((size_t)d.Hq * (size_t)K * d.d * sizeof(float));
   logo::Dims dk = d;
   dk.k = (int)K;
-  w.total = w.sched + up(logo::attn_bf16_sched_ints(dk, true) * sizeof(int32_t));
+  w.nidx = w.sched + up(logo::attn_bf16_sched_ints(dk, true) * sizeof(int32_t));
+  w.fused = logo::attn_bf16_fused_ok(dk);
+  w.total = w.nidx + (w.fused ? up((size_t)(d.n - K) * sizeof(int32_t)) : 0);
   return w;
 }
 
@@ -878,12 +881,15 @@ logo_status logo_forward_varlen(const logo_problem* p, const int32_t* cu_seqlens
   float* scratch = reinterpret_cast<float*>(w + ws.scratch);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
+  // bf16 streams with enough selected rows: the selection also lists the
+  // unselected positions, then one launch computes every row (as logo_forward)
+  int32_t* nidx = ws.fused ? reinterpret_cast<int32_t*>(w + ws.nidx) : nullptr;
   {
     StageTimer tm(0, s);
     e = logo::launch_varlen_prep(cu_seqlens, (int)n_examples, d.n, p->rho, seg, seg_start, s);
     if (e == hipSuccess)
       e = logo::launch_select_segments((int)n_examples, seg, gate, mask, d.k > 0 ? idx : nullptr,
-                                       rank, d.k, s);
+                                       rank, d.k, s, nidx, d.n - d.k);
   }
   if (e != hipSuccess) return hip_fail(e, "select launch");
   logo::AttnArgs a{};
@@ -898,6 +904,12 @@ logo_status logo_forward_varlen(const logo_problem* p, const int32_t* cu_seqlens
   a.out_io = o;
   a.seg_start = seg_start;
   a.sched = d.dtype == LOGO_BF16 ? reinterpret_cast<int32_t*>(w + ws.sched) : nullptr;
+  if (ws.fused) {
+    StageTimer tm(9, s);
+    e = logo::launch_attn_bf16_fused(d, a, nidx, s);
+    if (e != hipSuccess) return hip_fail(e, "fused attention launch");
+    return LOGO_OK;
+  }
   {
     StageTimer tm(1, s);
     e = run_attn(d, logo::Epi::LocalFused, a, s);

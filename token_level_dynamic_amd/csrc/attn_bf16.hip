@@ -388,6 +388,7 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
       bool ok;
       if (EPI == 6 && mode == kBelow) {
         ok = key < lb;                      // below the window (so also causal)
+        if (SEG) ok = ok && key >= ss;
       } else {
         ok = key <= pos;
         if (SEG) ok = ok && key >= ss;
@@ -749,8 +750,12 @@ struct FusedPlan {
 // local blocks fill the gaps the long global ones leave at the end. The
 // global rows (selected) compute their local branch too (EPI 6); the local
 // rows are the unselected ones (EPI 7). Nothing depends on anything else
-// in the launch.
-template <int D>
+// in the launch. Packed examples (SEG): a row's prefix starts at its
+// example's first token, so the global row blocks' work varies widely;
+// each global workgroup takes the next of its unit's blocks in the order of
+// pg.sched_perm (most keys to stream first) from a counter, so the XCDs
+// that share a unit stay balanced.
+template <int D, bool SEG>
 __global__ __launch_bounds__(kThreads, 2)
 __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_fused_kernel(Params pg, Params pl,
                                                                        FusedPlan plan) {
@@ -780,10 +785,19 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_fused_kernel(Params pg
     unit = x % plan.U;
     rank = j + sl * c;
   }
-  if (s < ng)
-    attn_block<D, true, 6, false>(pg, unit, plan.gw - 1 - rank, 0, K0, K1, V0, V1);
-  else
-    attn_block<D, false, 7, false>(pl, unit, rank, 0, K0, K1, V0, V1);
+  if (s < ng) {
+    int w = plan.gw - 1 - rank;   // longest causal prefix first
+    if (SEG) {
+      __shared__ int ticket;
+      if (threadIdx.x == 0) ticket = atomicAdd(pg.sched_count + unit, 1);
+      __syncthreads();
+      // exactly plan.gw global workgroups serve a unit; the clamp only
+      // keeps a miscount in bounds
+      w = pg.sched_perm[min(ticket, plan.gw - 1)];
+    }
+    attn_block<D, true, 6, SEG>(pg, unit, w, 0, K0, K1, V0, V1);
+  } else
+    attn_block<D, false, 7, SEG>(pl, unit, rank, 0, K0, K1, V0, V1);
 }
 
 // Small problems (the global branch split over key ranges): the split global
@@ -952,7 +966,12 @@ hipError_t dispatch_epi(Epi epi, const Params& prm, hipStream_t s) {
 template <int D>
 hipError_t launch_fused(const Params& pg, const Params& pl, const FusedPlan& plan, int grid,
                         hipStream_t s) {
-  hipLaunchKernelGGL(attn_bf16_fused_kernel<D>, dim3(grid), dim3(kThreads), 0, s, pg, pl, plan);
+  if (pg.seg_start)
+    hipLaunchKernelGGL((attn_bf16_fused_kernel<D, true>), dim3(grid), dim3(kThreads), 0, s, pg,
+                       pl, plan);
+  else
+    hipLaunchKernelGGL((attn_bf16_fused_kernel<D, false>), dim3(grid), dim3(kThreads), 0, s, pg,
+                       pl, plan);
   return hipGetLastError();
 }
 
@@ -993,6 +1012,19 @@ hipError_t launch_attn_bf16_fused(const Dims& d, const AttnArgs& a, const int32_
   pg.units = (d.k + kRows - 1) / kRows * G;
   pg.wg_per_unit = (pg.units + kWaves - 1) / kWaves;
   pg.total_wg = d.B * d.Hkv * pg.wg_per_unit;
+  pg.seg_start = a.seg_start;
+  if (a.seg_start) {
+    // packed examples (one stream): the global row blocks' work order
+    if (d.B != 1 || !a.sched) return hipErrorInvalidValue;
+    int32_t* const perm = a.sched;
+    hipLaunchKernelGGL(global_sched_kernel, dim3(1), dim3(1024), 0, s, a.idx, a.seg_start, d.n,
+                       d.k, G, pg.units, pg.wg_per_unit, d.B * d.Hkv, perm,
+                       a.sched + pg.wg_per_unit);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    pg.sched_perm = perm;
+    pg.sched_count = a.sched + pg.wg_per_unit;   // zeroed by the kernel above
+  }
   Params pl = pg;
   const int nl = d.n - d.k;          // unselected rows per sequence
   pl.idx = nidx;

@@ -107,10 +107,12 @@ hipError_t launch_select(const Dims& d, const float* gate, uint8_t* mask,
                          int32_t* idx, int32_t* rank, hipStream_t s, int32_t* nidx = nullptr);
 
 // Packed examples: select per example (see select.hip) and build the
-// per-example table and per-token example starts from cu_seqlens.
+// per-example table and per-token example starts from cu_seqlens. nidx
+// (optional, nidx_cap entries): the unselected positions of the stream,
+// ascending.
 hipError_t launch_select_segments(int n_segments, const int4* seg, const float* gate,
                                   uint8_t* mask, int32_t* idx, int32_t* rank, int idx_cap,
-                                  hipStream_t s);
+                                  hipStream_t s, int32_t* nidx = nullptr, int nidx_cap = 0);
 hipError_t launch_varlen_prep(const int32_t* cu, int E, int T, double rho, int4* seg,
                               int32_t* seg_start, hipStream_t s);
 
@@ -123,7 +125,9 @@ size_t attn_bf16_sched_ints(const Dims& d, bool packed);
 int attn_bf16_splits(const Dims& d);
 // The single-launch fused bf16 forward: selected rows compute both
 // branches, unselected rows (nidx [B][n-k], ascending) the local one; a
-// kernel of its own writes o. Applies when attn_bf16_fused_ok(d).
+// kernel of its own writes o. Applies when attn_bf16_fused_ok(d). Packed
+// examples (a.seg_start set, B = 1): a.sched holds the work order the
+// launch computes first (attn_bf16_sched_ints(d, true) ints).
 bool attn_bf16_fused_ok(const Dims& d);
 hipError_t launch_attn_bf16_fused(const Dims& d, const AttnArgs& a, const int32_t* nidx,
                                   hipStream_t s);

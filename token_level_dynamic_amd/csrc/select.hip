@@ -73,13 +73,16 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* w
 // is seg[e] = {start, length, k_e, offset}; positions written to idx (at
 // idx[offset ..]) are absolute token positions and rank is the index in the
 // concatenated list; writes past `idx_cap` are dropped.
-// Batched rows may also write nidx[b*(n-k) ..]: the positions not selected,
-// ascending (the rows the local-only work of a fused forward gathers).
+// nidx (optional): the positions not selected, ascending (the rows the
+// local-only work of a fused forward gathers): batched rows at
+// nidx[b*(n-k) ..]; packed examples at nidx[start - offset ..] (the tokens
+// before the example less its selected predecessors), absolute positions,
+// writes past `nidx_cap` dropped.
 template <bool SEG>
 __global__ __launch_bounds__(kThreads) void select_kernel(
     const float* __restrict__ gate, int n_rows, int k_rows, uint8_t* __restrict__ mask,
     int32_t* __restrict__ idx, int32_t* __restrict__ rank, const int4* __restrict__ seg,
-    int idx_cap, int32_t* __restrict__ nidx) {
+    int idx_cap, int32_t* __restrict__ nidx, int nidx_cap) {
   __shared__ uint32_t hist[4096];
   __shared__ uint32_t scan_ws[kWaves + 1];
   __shared__ uint32_t s_digit, s_before;
@@ -105,8 +108,11 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   uint8_t* mrow = mask + (size_t)start;
   int32_t* rrow = rank + (size_t)start;
   int32_t* irow = idx ? idx + (size_t)koff : nullptr;
-  int32_t* nrow = (!SEG && nidx) ? nidx + (size_t)b * (n_rows - k_rows) : nullptr;
+  // unselected tokens before this row / example: its first entry of nidx
+  const long long nbase = SEG ? (long long)start - koff : (long long)b * (n_rows - k_rows);
+  int32_t* nrow = nidx && nbase >= 0 ? nidx + nbase : nullptr;
   const int icap = SEG ? idx_cap - koff : k;  // entries of irow that may be written
+  const long long ncap = SEG ? nidx_cap - nbase : n_rows - k_rows;  // of nrow
 
   // This thread's positions c * kChunk + t * kItems + j, as order images,
   // read once (every radix pass and the compaction use them); longer
@@ -219,7 +225,8 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       rv[j] = sel ? (int32_t)r + rank_add : -1;
       if (sel && p0 + j < n && (int)r < icap) irow[r] = p0 + j + pos_add;
       // unselected: p - r tokens before it are unselected too (r of them are selected)
-      if (!sel && nrow && p0 + j < n) nrow[p0 + j - (int)r] = p0 + j;
+      if (!sel && nrow && p0 + j < n && p0 + j - (int)r < ncap)
+        nrow[p0 + j - (int)r] = p0 + j + pos_add;
       gt_before += gt ? 1u : 0u;
       tie_before += tie ? 1u : 0u;
     }
@@ -265,16 +272,16 @@ hipError_t launch_select(const Dims& d, const float* gate, uint8_t* mask,
                          int32_t* idx, int32_t* rank, hipStream_t s, int32_t* nidx) {
   if (d.B == 0 || d.n == 0) return hipSuccess;
   hipLaunchKernelGGL(select_kernel<false>, dim3(d.B), dim3(kThreads), 0, s, gate, d.n, d.k, mask,
-                     idx, rank, nullptr, 0, nidx);
+                     idx, rank, nullptr, 0, nidx, 0);
   return hipGetLastError();
 }
 
 hipError_t launch_select_segments(int n_segments, const int4* seg, const float* gate,
                                   uint8_t* mask, int32_t* idx, int32_t* rank, int idx_cap,
-                                  hipStream_t s) {
+                                  hipStream_t s, int32_t* nidx, int nidx_cap) {
   if (n_segments == 0) return hipSuccess;
   hipLaunchKernelGGL(select_kernel<true>, dim3(n_segments), dim3(kThreads), 0, s, gate, 0, 0,
-                     mask, idx, rank, seg, idx_cap, nullptr);
+                     mask, idx, rank, seg, idx_cap, nidx, nidx_cap);
   return hipGetLastError();
 }
 
