@@ -147,7 +147,8 @@ __device__ __forceinline__ void issue_tile(const uint16_t* base, int nbytes, uin
 // forward:
 //   6 (global rows, gathered through idx): the selected rows' local branch
 //     and global branch from one walk over their causal prefix. The walk
-//     goes from the diagonal down to key 0. Keys inside a row's window
+//     goes from the diagonal down to key 0 (SEG: to the first token of the
+//     lowest example in the block). Keys inside a row's window
 //     [i-W+1, i] come first, so after the tile holding the window's lowest
 //     key the running output is that row's local output: it is normalised
 //     and parked in the scratch rows (this lane's row only). The walk then
@@ -158,7 +159,8 @@ __device__ __forceinline__ void issue_tile(const uint16_t* base, int nbytes, uin
 //   7 (unselected rows, gathered through idx = the unselected positions,
 //     ksel = their count): the local branch only; writes o.
 // SEG: packed examples (p.seg_start set): keys before a row's example start
-// are masked and tile ranges start at the example; positions read from idx
+// are masked (in both of EPI 6's walks) and tile ranges start at the
+// example; positions read from idx
 // are clamped and ranks beyond the scratch rows ignored, so inconsistent
 // example offsets cannot address outside the buffers. Compiled separately so
 // the plain path carries none of it.
