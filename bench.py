@@ -471,7 +471,8 @@ def ceilings(torch) -> int:
             print(json.dumps({name: out[f"{name} | {wg_per_cu} WG/CU"],
                               "wg_per_cu": wg_per_cu}), flush=True)
     # HBM: streaming 16-byte reads over 4 GiB of random bytes, 4 passes
-    nbytes = 4 << 30 if not only else 0
+    # the HBM streams run with every kind, or alone with CEILING_KINDS=stream
+    nbytes = 4 << 30 if not only or "stream" in only.split(",") else 0
     src = torch.randint(-2 ** 31, 2 ** 31 - 1, (max(nbytes, 16) // 4,), dtype=torch.int32,
                         device="cuda")
     for wg_per_cu in ((2, 4, 8) if nbytes else ()):
@@ -492,6 +493,28 @@ def ceilings(torch) -> int:
         gbs = 4 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
         out[f"hbm stream read 4 GiB | {wg_per_cu} WG/CU"] = {"GB_per_s": round(gbs, 1)}
         print(json.dumps({"hbm stream read": round(gbs, 1), "wg_per_cu": wg_per_cu}), flush=True)
+    # the same over 1 GiB, into registers (12) and through the LDS DMA (39)
+    for kind, name in ((12, "registers"), (39, "LDS DMA")):
+        for wg_per_cu in ((2, 4) if nbytes else ()):
+            blocks = cus * wg_per_cu
+            sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+            sub = 1 << 30
+            rc = lib.ceiling_launch(kind, blocks, 1, sink.data_ptr(), None, src.data_ptr(), sub,
+                                    stream.cuda_stream)
+            if rc != 0:
+                raise SystemExit(f"stream kernel {kind} failed: hip error {rc}")
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(8):
+                lib.ceiling_launch(kind, blocks, 1, sink.data_ptr(), None, src.data_ptr(), sub,
+                                   stream.cuda_stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            gbs = 8 * sub / (e0.elapsed_time(e1) * 1e-3) / 1e9
+            out[f"hbm stream read 1 GiB, {name} | {wg_per_cu} WG/CU"] = {"GB_per_s": round(gbs, 1)}
+            print(json.dumps({f"hbm stream read 1 GiB, {name}": round(gbs, 1),
+                              "wg_per_cu": wg_per_cu}), flush=True)
     del src
     print(json.dumps({"ceilings": out, "cus": cus,
                       "source": "token_level_dynamic_amd/csrc/ceiling.hip"}))

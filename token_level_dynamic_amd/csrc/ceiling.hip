@@ -437,6 +437,34 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __re
   sink[threadIdx.x + blockIdx.x * kThreads] = (float)x;
 }
 
+// The same stream through the LDS DMA the attention kernels use: each wave
+// moves 1 KiB chunks (16 bytes a lane, buffer_load_dwordx4 ... lds) into an
+// 8-slot ring of its own, at most 6 in flight, chunks grid-strided over the
+// buffer (at most 1 GiB: 32-bit buffer sizes). One value per lane is read
+// back at the end so the stores are live.
+__global__ __launch_bounds__(kThreads) void stream_lds_kernel(const u32x4* __restrict__ src,
+                                                              long long n16, float* sink) {
+  __shared__ uint4 ring[kThreads / 64][8][64];
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const long long nchunk = n16 / 64;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u32x4*>(src), (short)0, (int)(nchunk * 1024), 0x00020000);
+  const long long stride = (long long)gridDim.x * (kThreads / 64);
+  int slot = 0;
+  for (long long c = blockIdx.x * (long long)(kThreads / 64) + wave; c < nchunk; c += stride) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)&ring[wave][slot][0], 16,
+                                             (uint32_t)(c * 1024 + lane * 16), 0, 0, 0);
+    slot = (slot + 1) & 7;
+    __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6)
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0)
+  __syncthreads();
+  const uint4 v = ring[wave][0][lane];
+  sink[threadIdx.x + blockIdx.x * kThreads] = (float)(v.x ^ v.w);
+}
+
 }  // namespace
 
 // Models of a tile loop (512-thread workgroups, one per CU for the LDS it
@@ -605,16 +633,22 @@ extern "C" {
 // SIMD, 1 KiB + 3.5; 33 as 31 without FMAs; 34 as 31 without LDS; 35 as 32
 // without FMAs; 36 as 32 without LDS), 37/38 products in waves 0-3 beside 4
 // v_dot2_f32_bf16 / 4 FMA per product in waves 4-7 (simd_pair_kernel modes
-// 6 and 2).
+// 6 and 2), 39 the streaming reads of 12 through the LDS DMA (src_bytes at
+// most 1 GiB).
 // sink: blocks * 256 floats; clk: blocks * 4
 // int64. Returns a hipError_t.
 int ceiling_launch(int kind, int blocks, int iters, float* sink, long long* clk,
                    const void* src, long long src_bytes, hipStream_t stream) {
   if (blocks <= 0 || !sink) return (int)hipErrorInvalidValue;
-  if (kind == 12) {
+  if (kind == 12 || kind == 39) {
     if (!src || src_bytes <= 0 || src_bytes % 16) return (int)hipErrorInvalidValue;
-    hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(kThreads), 0, stream,
-                       static_cast<const u32x4*>(src), src_bytes / 16, sink);
+    if (kind == 39 && src_bytes > (1LL << 30)) return (int)hipErrorInvalidValue;
+    if (kind == 12)
+      hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(kThreads), 0, stream,
+                         static_cast<const u32x4*>(src), src_bytes / 16, sink);
+    else
+      hipLaunchKernelGGL(stream_lds_kernel, dim3(blocks), dim3(kThreads), 0, stream,
+                         static_cast<const u32x4*>(src), src_bytes / 16, sink);
     return (int)hipGetLastError();
   }
   if (iters <= 0 || !clk) return (int)hipErrorInvalidValue;
