@@ -284,7 +284,7 @@ def record_traffic(args) -> int:
             "mean of the warm-up and the two timed dispatches) times 1024 times the "
             "copy-kernel scale; written by bench.py --record-traffic, see "
             "hbm_traffic_gqa32k.md")
-    fz = "attn_bf16_fused_kernel<128>"
+    fz = "attn_bf16_fused_kernel<128, false>"
     if any(fz in k for k in fm):
         # the single-launch forward: one kernel for both branches
         fr, fw = _pick(fm, fz) * 1024 * fs, _pick(wm, fz) * 1024 * ws

@@ -62,17 +62,23 @@ template <int D>
 struct Smem {
   // Tiles are filled by bounds-checked buffer loads that write LDS
   // directly: one instruction moves 64 lanes x 16 B into 1 KiB of
-  // consecutive LDS. A tile of 64 rows is laid out as 64 x kChunks 16-byte
-  // slots, the last slot(s) of each row being padding, so kChunks
-  // instructions fill a tile exactly. Row strides in bf16: K rows carry 16 B
-  // of pad (stride = 4 mod 32 banks: conflict-free 16-byte operand reads),
-  // V rows 32 B (stride = 8 mod 32 banks: conflict-free transposing reads).
-  static constexpr int kChunks = D / 8 + 1;
-  static constexpr int vChunks = D / 8 + 2;
+  // consecutive LDS, so a tile of 64 rows is 64 x kChunks 16-byte slots and
+  // kChunks instructions fill it.
+  // d = 128: unpadded rows; logical chunk c of row r sits in slot c ^ swz(r)
+  // of the row, which spreads both the 16-byte K operand reads (16 rows,
+  // one chunk) and the transposing V reads (4 rows, 4 chunks, twice) over
+  // all 64 banks. d = 64: padded rows (the swizzle measured slower there):
+  // K rows carry 16 B of pad (16-byte operand reads conflict-free), V rows
+  // 32 B; pad slots read an out-of-range offset (zero).
+  static constexpr bool kSwz = D == 128;
+  static constexpr int kChunks = kSwz ? D / 8 : D / 8 + 1;
+  static constexpr int vChunks = kSwz ? D / 8 : D / 8 + 2;
   static constexpr int kStride = kChunks * 8;
   static constexpr int vStride = vChunks * 8;
   static constexpr int kElems = kKeys * kStride;
   static constexpr int vElems = kKeys * vStride;
+  // depends on r's low four bits only, so whole 16-row groups share it
+  __device__ static int swz(int r) { return kSwz ? ((r & 3) << 2) | ((r >> 2) & 3) : 0; }
 };
 
 struct Params {
@@ -256,8 +262,9 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
 
   // ---- tile staging: buffer loads straight into LDS ----------------------
   // Wave w issues the tile's instructions j = w, w+4, ...; lane l of
-  // instruction j fills slot j*64 + l = (row, chunk). Padding slots read an
-  // out-of-range offset (zero, no fault).
+  // instruction j fills slot j*64 + l = (row, physical chunk pc), reading
+  // the row's logical chunk pc ^ swz(row); pad slots read an out-of-range
+  // offset (zero, no fault).
   constexpr int KJ = (SM::kChunks + kWaves - 1) / kWaves;  // instructions per wave
   constexpr int VJ = (SM::vChunks + kWaves - 1) / kWaves;
   constexpr uint32_t kPadOff = 0x40000000u;
@@ -265,14 +272,16 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
 #pragma unroll
   for (int i = 0; i < KJ; ++i) {
     const int slot = (wave + kWaves * i) * 64 + lane;
-    const int row = slot / SM::kChunks, chunk = slot % SM::kChunks;
-    k_voff[i] = chunk < D / 8 ? (uint32_t)(row * k_st * 2 + chunk * 16) : kPadOff;
+    const int row = slot / SM::kChunks, pc = slot % SM::kChunks;
+    k_voff[i] =
+        pc < D / 8 ? (uint32_t)(row * k_st * 2 + (pc ^ SM::swz(row)) * 16) : kPadOff;
   }
 #pragma unroll
   for (int i = 0; i < VJ; ++i) {
     const int slot = (wave + kWaves * i) * 64 + lane;
-    const int row = slot / SM::vChunks, chunk = slot % SM::vChunks;
-    v_voff[i] = chunk < D / 8 ? (uint32_t)(row * v_st * 2 + chunk * 16) : kPadOff;
+    const int row = slot / SM::vChunks, pc = slot % SM::vChunks;
+    v_voff[i] =
+        pc < D / 8 ? (uint32_t)(row * v_st * 2 + (pc ^ SM::swz(row)) * 16) : kPadOff;
   }
   auto issue_kv = [&] __device__ (int t, uint16_t* kdst, uint16_t* vdst)
       __attribute__((always_inline)) {
@@ -290,6 +299,25 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
   const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
   typedef short v4i16 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
+  constexpr int DB0 = D / 32;
+  // Element offsets of this lane's fragment reads within a tile: the K
+  // operand of k-step s (row col; rows 32.. add 32 rows: same swizzle), and
+  // the transposing V reads of d block db, rows +0 and +8 of the 16-key
+  // half (kb and hh add whole 16-row groups: same swizzle)
+  constexpr int QS0 = D / 16;
+  int koff[QS0], voff_lo[DB0], voff_hi[DB0];
+#pragma unroll
+  for (int s = 0; s < QS0; ++s)
+    koff[s] = col * SM::kStride + (((2 * s + half) ^ SM::swz(col)) * 8);
+  {
+    const int rl = half * 4 + tr_row, rh = rl + 8;
+    const int cc = tr_col >> 3, within = tr_col & 7;
+#pragma unroll
+    for (int db = 0; db < DB0; ++db) {
+      voff_lo[db] = rl * SM::vStride + (((db * 4 + cc) ^ SM::swz(rl)) * 8) + within;
+      voff_hi[db] = rh * SM::vStride + (((db * 4 + cc) ^ SM::swz(rh)) * 8) + within;
+    }
+  }
 
   // ---- online softmax state ----------------------------------------------
   constexpr int DB = D / 32;  // 32-wide d blocks of the output
@@ -321,11 +349,9 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
   // +8+4*half+[0,4), matching its probabilities.
   auto read_vf = [&] __device__ (const uint16_t* vs, int kb, int hh, int db)
       __attribute__((always_inline)) {
-    const int kbase = kb * 32 + hh * 16 + half * 4 + tr_row;
-    const uint16_t* a0 = vs + kbase * SM::vStride + db * 32 + tr_col;
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(a0));
-    const v4i16 hi =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(a0 + 8 * SM::vStride));
+    const uint16_t* g0 = vs + (kb * 32 + hh * 16) * SM::vStride;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(g0 + voff_lo[db]));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(g0 + voff_hi[db]));
     const uint2 l2 = __builtin_bit_cast(uint2, lo);
     const uint2 h2 = __builtin_bit_cast(uint2, hi);
     return __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
@@ -417,11 +443,10 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
     f32x16 sc0, sc1;
     uint32_t pk0[8], pk1[8];   // bf16 probability pairs of blocks 0 and 1
     {
-      const uint16_t* krow = ks + col * SM::kStride + half * 8;
       bf16x8 kf[QS];
 #pragma unroll
       for (int s = 0; s < QS; ++s)
-        kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + s * 16));
+        kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ks + koff[s]));
       // all eight reads in flight before the first product (otherwise they
       // are issued two at a time, each pair waited for)
       __builtin_amdgcn_sched_barrier(0);
@@ -430,11 +455,11 @@ __device__ __forceinline__ void attn_block(const Params& p, int unit_bh, int w, 
         sc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qreg[s], s ? sc0 : (f32x16){},
                                                        0, 0, 0);
     }
-    const uint16_t* krow1 = ks + (32 + col) * SM::kStride + half * 8;
     bf16x8 kf1[QS];
 #pragma unroll
     for (int s = 0; s < QS; ++s)
-      kf1[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow1 + s * 16));
+      kf1[s] = __builtin_bit_cast(bf16x8,
+                                  *reinterpret_cast<const uint4*>(ks + 32 * SM::kStride + koff[s]));
     if (!full) mask_block(key0, sc0, mode);
     __builtin_amdgcn_sched_barrier(0);
     // QK(kb1), 8 pairs of block 0 spread over its QS MFMAs
