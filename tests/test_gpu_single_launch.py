@@ -120,3 +120,43 @@ def test_single_launch_scores_far_below_zero(name):
     say(f"  {len(rows)} rows, max_abs={err.max():.3e} at {worst} "
         f"(selected: {bool(rm[worst[0], worst[2]])}), max |ref|={np.abs(ref).max():.2f}")
     assert err.max() <= TOL
+
+
+# The same far-below inputs on the forward's other bf16 paths: a problem
+# small enough to split the global branch's key ranges (local band and split
+# global branch in one launch, then the merge of the ranges' maxima and sums)
+# and one whose B * Hkv neither divides nor is a multiple of 8 (two launches).
+FAR_BELOW_OTHER = {
+    "far_below_split_d128": ("gqa32k", dict(B=1, Hq=8, Hkv=2, n=3000, window=300, rho=0.2)),
+    "far_below_two_launch_d64": ("sweep64k", dict(B=1, Hq=12, Hkv=12, n=12000, window=400,
+                                                  rho=0.5)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FAR_BELOW_OTHER))
+def test_other_paths_scores_far_below_zero(name):
+    base, over = FAR_BELOW_OTHER[name]
+    w = get_workload(base, **over)
+    p = problem(w)
+    assert not single_launch(p)
+    inp = make_far_below(make_inputs(w, 3))
+    G = w.Hq // w.Hkv
+    say(f"[far below] {name}: {w}")
+    qd, kd, vd, gate = to_dev(inp)
+    got = run_forward(p, qd, kd, vd, gate)
+    del qd, kd, vd
+    rm, _, _ = oracle.select_queries(inp.gate, w.rho)
+    assert np.array_equal(host(got["mask"]), rm)
+    heads = sorted({0, G - 1, G, w.Hq - 1})
+    rows = [(b, h, i) for b in range(w.B) for h in heads for i in range(w.n)]
+    with OP.SharedInputs(q=inp.q, k=inp.k, v=inp.v, gate=inp.gate) as sh:
+        parts = OP.map_chunks(sh, "oracle.forward_rows",
+                              lambda c: ("@q", "@k", "@v", "@gate", w.window, w.rho, list(c)),
+                              rows, chunk=256)
+    ref = np.concatenate([x["o_rows"] for x in parts])
+    vals = gather_rows(got["o"], rows)
+    assert np.isfinite(vals).all(), "non-finite outputs"
+    err = np.abs(vals - ref)
+    worst = rows[int(err.max(axis=1).argmax())]
+    say(f"  {len(rows)} rows, max_abs={err.max():.3e} at {worst}, max |ref|={np.abs(ref).max():.2f}")
+    assert err.max() <= TOL
