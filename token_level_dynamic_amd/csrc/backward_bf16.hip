@@ -81,7 +81,7 @@ __device__ __forceinline__ uint32_t slot_off(int slot, int chunks, int dchunks, 
 // buffer-load-to-LDS instructions that fill a tile of `rows` rows.
 // Source: bytes [base, base + nbytes), row r of the tile at byte
 // soff + r * st2. Rows past the end read zero (hardware bounds check).
-template <int NCH, int CHUNKS, int DCH>
+template <int NCH, int CHUNKS, int DCH, bool SWZ = false>
 __device__ __forceinline__ void issue_rows(const uint16_t* base, int nbytes, uint16_t* dst,
                                            int soff, int st2, int wave, int lane) {
   typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -90,8 +90,14 @@ __device__ __forceinline__ void issue_rows(const uint16_t* base, int nbytes, uin
 #pragma unroll
   for (int i = 0; i < (NCH + kWaves - 1) / kWaves; ++i) {
     const int j = wave + kWaves * i;
-    if (j < NCH) {
-      const uint32_t voff = slot_off(j * 64 + lane, CHUNKS, DCH, st2);
+    // (wave < kWaves: with NCH a multiple of kWaves every wave issues all)
+    if (NCH % kWaves == 0 || j < NCH) {
+      // SWZ: slot (row, pc) takes the row's logical chunk pc ^ swz(row),
+      // swz as in KVTile (unpadded rows)
+      const int slot = j * 64 + lane, row = slot / CHUNKS, pc = slot % CHUNKS;
+      const uint32_t voff =
+          SWZ ? (uint32_t)(row * st2 + ((pc ^ (((row & 3) << 2) | ((row >> 2) & 3))) << 4))
+              : slot_off(slot, CHUNKS, DCH, st2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)(dst + j * 512), 16, voff, soff,
                                                0, 0);
     }
@@ -119,26 +125,6 @@ __device__ __forceinline__ void issue_part(const uint16_t* base, int nbytes, uin
   }
 }
 
-// Transposing fragment read: rows (a "key" or "query" index of the
-// contraction) r0 + {half*4 + [0,4)} and r0 + 8 + {half*4 + [0,4)} of a
-// row-major LDS tile, d column block `db`; each lane gets 8 values of its
-// own d column (l % 32), the A operand of a product whose B operand comes
-// from an accumulator's 8 consecutive elements (e = hh*8 + [0,8)).
-// Within each 16-lane group ds_read_b64_tr_b16 gives destination lane 4q+j
-// element e the element j of the 8 bytes addressed by source lane 4e+q.
-__device__ __forceinline__ bf16x8 read_tr(const uint16_t* tile, int stride, int r0, int db,
-                                          int lane) {
-  const int half = lane >> 5;
-  const int tr_row = (lane & 15) >> 2;
-  const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
-  const uint16_t* a0 = tile + (r0 + half * 4 + tr_row) * stride + db * 32 + tr_col;
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(a0));
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(a0 + 8 * stride));
-  const uint2 l2 = __builtin_bit_cast(uint2, lo);
-  const uint2 h2 = __builtin_bit_cast(uint2, hi);
-  return __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
-}
-
 // =========================================================================
 // dK / dV
 // =========================================================================
@@ -148,13 +134,27 @@ constexpr int kPairs = 4;  // wave pairs per workgroup
 constexpr int kKB = kKW * kPairs;  // keys per workgroup
 constexpr int kDkdvThreads = 2 * kPairs * 64;
 
+// Q and dO tiles are read two ways: rows as 16-byte operands (producer) and
+// 4 rows x 8 bytes at a time by the transposing read (consumer). d = 128:
+// unpadded rows whose logical 16-byte chunk c of row r sits in slot
+// c ^ swz(r), which spreads both kinds of read over all 64 banks. d = 64:
+// 32 B of padding per row (two-way conflicts on both kinds).
 template <int D>
 struct QTile {
-  static constexpr int kChunks = D / 8 + 2;    // 32 B of padding per row
+  static constexpr bool kSwz = D == 128;
+  static constexpr int kChunks = kSwz ? D / 8 : D / 8 + 2;
   static constexpr int kStride = kChunks * 8;  // elements
   static constexpr int kElems = kQT * kStride;
   static constexpr int kInstr = kQT * kChunks / 64;
   static_assert(kQT * kChunks % 64 == 0, "tile must be whole instructions");
+  // depends on r's low four bits only, so whole 16-row groups share it
+  __device__ static int swz(int r) { return kSwz ? ((r & 3) << 2) | ((r >> 2) & 3) : 0; }
+  // source byte offset (row stride st2 bytes) of LDS slot `slot` of a tile;
+  // pad slots read an out-of-range offset (zero)
+  __device__ static uint32_t slot_src(int slot, int st2) {
+    const int row = slot / kChunks, pc = slot % kChunks;
+    return pc < D / 8 ? (uint32_t)(row * st2 + ((pc ^ swz(row)) << 4)) : kPadOff;
+  }
 };
 
 struct DkdvParams {
@@ -318,8 +318,8 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(DkdvParams p)
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int slot = (part + 2 * i) * 64 + lane;
-    voff_l[i] = slot_off(slot, QT::kChunks, DCH, lst2);
-    voff_g[i] = slot_off(slot, QT::kChunks, DCH, D * 2);
+    voff_l[i] = QT::slot_src(slot, lst2);
+    voff_g[i] = QT::slot_src(slot, D * 2);
   }
   const float* row_l = (cw == 1 ? p.L2_l : p.D_l) + ((long long)b * p.Hq + hk * G) * p.n;
   const float* row_g = (cw == 1 ? p.L2_g : p.D_g) + ((long long)b * p.Hq + hk * G) * p.ksel;
@@ -379,6 +379,44 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(DkdvParams p)
     advance();
   };
 
+  // Element offsets of this lane's tile reads: the producer's operand of
+  // k-step s (row col, logical chunk 2s + half), the consumer's transposing
+  // reads of d block db, rows half*4 + (lane & 15)/4 and 8 more (the second
+  // 16-row half adds 16 rows: same swizzle).
+  int poff[QS], toff_lo[DB], toff_hi[DB];
+#pragma unroll
+  for (int s = 0; s < QS; ++s) poff[s] = col * QT::kStride + (((2 * s + half) ^ QT::swz(col)) << 3);
+  {
+    const int rl = half * 4 + ((lane & 15) >> 2), rh = rl + 8;
+    const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+    const int cc = tr_col >> 3, within = tr_col & 7;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      toff_lo[db] = rl * QT::kStride + (((db * 4 + cc) ^ QT::swz(rl)) << 3) + within;
+      toff_hi[db] = rh * QT::kStride + (((db * 4 + cc) ^ QT::swz(rh)) << 3) + within;
+    }
+  }
+  auto read_qt = [&] __device__ (const uint16_t* tile, int hh, int db)
+      __attribute__((always_inline)) {
+    const uint16_t* g0 = tile + hh * 16 * QT::kStride;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(g0 + toff_lo[db]));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(g0 + toff_hi[db]));
+    const uint2 l2 = __builtin_bit_cast(uint2, lo);
+    const uint2 h2 = __builtin_bit_cast(uint2, hi);
+    return __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+  };
+
+  // Whether some row of tile t reads some key of this wave pair: row pos
+  // reads key j iff 0 <= pos - j < wlim, so some j of [key0, key0 + 31] iff
+  // 0 <= pos - key0 < wlim + 31. Both waves of the pair skip a tile none of
+  // whose rows does (its P and dS are zero). Rows past the end of the list
+  // read zero Q and dO rows and add exactly zero either way.
+  auto pair_live = [&] __device__ (int t, const float* rc) __attribute__((always_inline)) {
+    const uint32_t wlim = t < T_gs ? 0x80000000u : (uint32_t)p.W;
+    const int pos = reinterpret_cast<const int*>(rc)[2 * kSlot + col];
+    return __builtin_amdgcn_ballot_w64((uint32_t)(pos - key0) < wlim + 31u) != 0;
+  };
+
   bf16x8 kreg[QS], vreg[QS];  // producer: K and V rows of the lane's key
   f32x16 acc_dk[DB], acc_dv[DB];  // consumer: dK^T, dV^T
 
@@ -388,18 +426,17 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(DkdvParams p)
   // and dS = P (dP - Dr), packed to bf16 and handed over.
   auto produce = [&] __device__ (int t, const uint16_t* qc, const uint16_t* oc, const float* rc,
                                  uint16_t* ps) __attribute__((always_inline)) {
+    if (!pair_live(t, rc)) return;
     // key j is read by row pos iff 0 <= pos - j < wlim (window, or any
     // earlier key for selected rows). Rows past the end of the tile's list
     // have zero Q / dO rows and zero row terms, so they add exactly zero.
     const uint32_t wlim = t < T_gs ? 0x80000000u : (uint32_t)p.W;
-    const uint16_t* qrow = qc + col * QT::kStride + half * 8;
-    const uint16_t* orow = oc + col * QT::kStride + half * 8;
     f32x16 s_acc = (f32x16){}, p_acc = (f32x16){};
 #pragma unroll
     for (int s = 0; s < QS; ++s) {
-      s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kreg[s], ld16(qrow + s * 16), s_acc, 0, 0,
+      s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kreg[s], ld16(qc + poff[s]), s_acc, 0, 0,
                                                       0);
-      p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vreg[s], ld16(orow + s * 16), p_acc, 0, 0,
+      p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vreg[s], ld16(oc + poff[s]), p_acc, 0, 0,
                                                       0);
     }
     const float l2 = rc[col];
@@ -447,8 +484,9 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(DkdvParams p)
 
   // Consumer work for a tile: dV^T += dO^T P and dK^T += Q^T dS, contraction
   // rows 0..15 then 16..31.
-  auto consume = [&] __device__ (const uint16_t* qc, const uint16_t* oc, const uint16_t* ps)
-      __attribute__((always_inline)) {
+  auto consume = [&] __device__ (int t, const uint16_t* qc, const uint16_t* oc, const float* rc,
+                                 const uint16_t* ps) __attribute__((always_inline)) {
+    if (!pair_live(t, rc)) return;
     const uint16_t* pt = ps + pw * kPsPair;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -456,10 +494,10 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(DkdvParams p)
       const bf16x8 sb = read_tr_ps(pt + kQT * kKW, hh * 16, lane);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        acc_dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            read_tr(oc, QT::kStride, hh * 16, db, lane), pb, acc_dv[db], 0, 0, 0);
-        acc_dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            read_tr(qc, QT::kStride, hh * 16, db, lane), sb, acc_dk[db], 0, 0, 0);
+        acc_dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_qt(oc, hh, db), pb,
+                                                              acc_dv[db], 0, 0, 0);
+        acc_dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_qt(qc, hh, db), sb,
+                                                              acc_dk[db], 0, 0, 0);
       }
     }
   };
@@ -501,11 +539,11 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(DkdvParams p)
     acc_dk[i] = (f32x16){};
     acc_dv[i] = (f32x16){};
   }
-  auto cstep = [&] __device__ (int u, const uint16_t* qp, const uint16_t* op, const uint16_t* psr,
-                               uint16_t* qn, uint16_t* on, float* rn)
+  auto cstep = [&] __device__ (int u, const uint16_t* qp, const uint16_t* op, const float* rp,
+                               const uint16_t* psr, uint16_t* qn, uint16_t* on, float* rn)
       __attribute__((always_inline)) {
     if (u + 1 < T) issue(qn, on, rn);
-    if (u >= 1) consume(qp, op, psr);
+    if (u >= 1) consume(u - 1, qp, op, rp, psr);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
   };
@@ -514,9 +552,9 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(DkdvParams p)
   __syncthreads();
 #pragma unroll 1
   for (int u = 0; u <= T; u += 3) {
-    cstep(u, Q2, O2, PS2, Q1, O1, R1);
-    if (u + 1 <= T) cstep(u + 1, Q0, O0, PS0, Q2, O2, R2);
-    if (u + 2 <= T) cstep(u + 2, Q1, O1, PS1, Q0, O0, R0);
+    cstep(u, Q2, O2, R2, PS2, Q1, O1, R1);
+    if (u + 1 <= T) cstep(u + 1, Q0, O0, R0, PS0, Q2, O2, R2);
+    if (u + 2 <= T) cstep(u + 2, Q1, O1, R1, PS1, Q0, O0, R0);
   }
 
   if (key >= p.n) return;
@@ -544,10 +582,15 @@ constexpr int kKeys = 64;  // keys per tile
 
 template <int D>
 struct KVTile {
-  // K rows are read both as 16-byte operands and transposed: 32 B of pad
+  // K rows are read both as 16-byte operands and transposed. d = 128:
+  // unpadded rows, logical 16-byte chunk c of row r in slot c ^ swz(r), which
+  // spreads both kinds of read over all 64 banks; d = 64: 32 B of pad
   // (conflict-free transposing reads). V rows only as 16-byte operands: 16 B.
-  static constexpr int kChunks = D / 8 + 2;
+  static constexpr bool kSwz = D == 128;
+  static constexpr int kChunks = kSwz ? D / 8 : D / 8 + 2;
   static constexpr int vChunks = D / 8 + 1;
+  // depends on r's low four bits only, so whole 16-row groups share it
+  __device__ static int swz(int r) { return kSwz ? ((r & 3) << 2) | ((r >> 2) & 3) : 0; }
   static constexpr int kStride = kChunks * 8;
   static constexpr int vStride = vChunks * 8;
   static constexpr int kElems = kKeys * kStride;
@@ -657,8 +700,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqParams p) {
   const int v_bytes = ((p.n - 1) * p.vv.st + D) * 2;
   auto issue_kv = [&] __device__ (int t, uint16_t* kdst, uint16_t* vdst)
       __attribute__((always_inline)) {
-    issue_rows<KT::kInstr, KT::kChunks, DCH>(kg, k_bytes, kdst, t * kKeys * k_st2, k_st2, wave,
-                                             lane);
+    issue_rows<KT::kInstr, KT::kChunks, DCH, KT::kSwz>(kg, k_bytes, kdst, t * kKeys * k_st2,
+                                                       k_st2, wave, lane);
     issue_rows<KT::vInstr, KT::vChunks, DCH>(vg, v_bytes, vdst, t * kKeys * v_st2, v_st2, wave,
                                              lane);
   };
@@ -672,16 +715,43 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqParams p) {
     return wave_on && key0 <= wkey_hi && key0 + kKeys - 1 >= wkey_lo;
   };
 
+  // Element offsets of this lane's K tile reads: the operand of k-step s
+  // (row col, logical chunk 2s + half) and the transposing reads of d block
+  // db, rows half*4 + (lane & 15)/4 and 8 more; whole 16-row groups added
+  // to either keep the swizzle.
+  int koff[QS], toff_lo[DB], toff_hi[DB];
+#pragma unroll
+  for (int s = 0; s < QS; ++s) koff[s] = col * KT::kStride + (((2 * s + half) ^ KT::swz(col)) << 3);
+  {
+    const int rl = half * 4 + ((lane & 15) >> 2), rh = rl + 8;
+    const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+    const int cc = tr_col >> 3, within = tr_col & 7;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      toff_lo[db] = rl * KT::kStride + (((db * 4 + cc) ^ KT::swz(rl)) << 3) + within;
+      toff_hi[db] = rh * KT::kStride + (((db * 4 + cc) ^ KT::swz(rh)) << 3) + within;
+    }
+  }
+  auto read_kt = [&] __device__ (const uint16_t* ks, int r0, int db)
+      __attribute__((always_inline)) {
+    const uint16_t* g0 = ks + r0 * KT::kStride;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(g0 + toff_lo[db]));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(g0 + toff_hi[db]));
+    const uint2 l2 = __builtin_bit_cast(uint2, lo);
+    const uint2 h2 = __builtin_bit_cast(uint2, hi);
+    return __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+  };
+
   auto tile = [&] __device__ (int t, const uint16_t* ks, const uint16_t* vs)
       __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 sacc = (f32x16){}, pacc = (f32x16){};
-      const uint16_t* krow = ks + (kb * 32 + col) * KT::kStride + half * 8;
+      const uint16_t* kblk = ks + kb * 32 * KT::kStride;
       const uint16_t* vrow = vs + (kb * 32 + col) * KT::vStride + half * 8;
 #pragma unroll
       for (int s = 0; s < QS; ++s) {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld16(krow + s * 16), qreg[s], sacc, 0, 0,
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld16(kblk + koff[s]), qreg[s], sacc, 0, 0,
                                                        0);
         pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld16(vrow + s * 16), oreg[s], pacc, 0, 0,
                                                        0);
@@ -726,8 +796,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqParams p) {
         for (int hh = 0; hh < 2; ++hh) {
           const bf16x8 sb = __builtin_bit_cast(
               bf16x8, make_uint4(dk2[4 * hh], dk2[4 * hh + 1], dk2[4 * hh + 2], dk2[4 * hh + 3]));
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              read_tr(ks, KT::kStride, kb * 32 + hh * 16, db, lane), sb, acc[db], 0, 0, 0);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_kt(ks, kb * 32 + hh * 16, db),
+                                                            sb, acc[db], 0, 0, 0);
         }
       }
     }
