@@ -139,7 +139,8 @@ __device__ __forceinline__ void issue_tile(const uint16_t* base, int nbytes, uin
 #pragma unroll
   for (int i = 0; i < NJ; ++i) {
     const int j = wave + kWaves * i;
-    if (j < NCH)
+    // (wave < kWaves: with NCH a multiple of kWaves every wave issues NJ)
+    if (NCH == NJ * kWaves || j < NCH)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)(dst + j * 512), 16, voff[i], soff,
                                                0, 0);
   }
