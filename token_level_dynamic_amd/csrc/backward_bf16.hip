@@ -746,6 +746,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqParams p) {
       __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      // A 32-key block no row of the wave reads (past the last row's
+      // position, or below the first row's window) adds exactly zero: skip.
+      {
+        const int kb0 = t * kKeys + kb * 32;
+        if (kb0 > wkey_hi || kb0 + 31 < wkey_lo) continue;
+      }
       f32x16 sacc = (f32x16){}, pacc = (f32x16){};
       const uint16_t* kblk = ks + kb * 32 * KT::kStride;
       const uint16_t* vrow = vs + (kb * 32 + col) * KT::vStride + half * 8;
