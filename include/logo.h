@@ -390,7 +390,9 @@ const char* logo_last_error(void);
  * 10 the local band and the key-range-split global branch in one launch
  * plus their merge),
  * the summed milliseconds
- * and the number of launches into arrays of `n_stages` entries. */
+ * and the number of launches into arrays of `n_stages` entries. The events
+ * are timing-only (created without the system-scope fence, so recording one
+ * flushes no cache); they order nothing for the caller. */
 logo_status logo_profile_begin(void);
 logo_status logo_profile_end(double* stage_ms, int64_t* stage_launches,
                              int32_t n_stages);

@@ -184,8 +184,12 @@ long prof_start(int stage, hipStream_t s) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
   if (!g_prof.on || g_prof.recs.size() >= kMaxRecords) return -1;
   while (g_prof.pool.size() < 2 * (g_prof.recs.size() + 1)) {
+    // Timing only: no system-scope fence when the event completes, so
+    // recording one writes back and invalidates no cache (the kernel after
+    // it would otherwise start on a cold L2). Nothing reads results through
+    // these events; callers synchronise the stream themselves.
     hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) return -1;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return -1;
     g_prof.pool.push_back(e);
   }
   Profiler::Rec r{g_prof.pool[2 * g_prof.recs.size()], g_prof.pool[2 * g_prof.recs.size() + 1],
