@@ -134,18 +134,27 @@ def _round(x):
 
 def test_workspace_split_partials(L):
     # A bf16 problem with fewer than 512 global row-block workgroups splits
-    # each block's keys over ceil(512 / workgroups) ranges, at most 8 and at
-    # least 4 key tiles of 64 each; the workspace then adds
+    # each block's keys over ceil(512 / workgroups) ranges, or, when the
+    # local band's workgroups (every row) and two ranges per global block fit
+    # in 512, over the most ranges that still fit beside them; at most 8 and
+    # at least 4 key tiles of 64 each. The workspace then adds
     # splits * B * Hq * k * (d + 4) float32 partials.
     # n=1000, rho=0.2: k=200, 7 row blocks x 2 heads per (b, kv head) = 4
-    # workgroups each, 16 in all; 16 key tiles -> 4 ranges
+    # workgroups each, 16 in all; 64 local workgroups; 16 key tiles -> 4 ranges
     k = T.logo_target_count(0.2, 1000)
     base = _round(2 * 4 * k * 128 * 4) + 256
     assert _ws_bytes(L, n=1000) == base + _round(4 * 2 * 4 * k * (128 + 4) * 4)
-    # d = 64, n = 4000 (63 tiles): 8 ranges
+    # d = 64, n = 4000: k=800, 13 global workgroups per (b, kv head), 52 in
+    # all; 4 x 63 = 252 local workgroups; (512 - 252) // 52 = 5 ranges
     k = T.logo_target_count(0.2, 4000)
     base = _round(2 * 4 * k * 64 * 4) + 256
-    assert _ws_bytes(L, n=4000, d=64) == base + _round(8 * 2 * 4 * k * (64 + 4) * 4)
+    assert _ws_bytes(L, n=4000, d=64) == base + _round(5 * 2 * 4 * k * (64 + 4) * 4)
+    # B=2, 16 query / 4 kv heads, n = 4000: k=800, 25 x 4 units -> 25
+    # global workgroups per (b, kv head), 200 in all; 2 x 4 x 125 = 1000
+    # local workgroups do not fit beside them: ceil(512 / 200) = 3 ranges
+    k = T.logo_target_count(0.2, 4000)
+    base = _round(2 * 16 * k * 128 * 4) + 256
+    assert _ws_bytes(L, n=4000, Hq=16, Hkv=4) == base + _round(3 * 2 * 16 * k * (128 + 4) * 4)
     # two key tiles: too few to split (single launch: + unselected positions);
     # float32: never split, never a single launch
     assert _ws_bytes(L, n=100) == _round(2 * 4 * 20 * 128 * 4) + 256 + _round(2 * 80 * 4)

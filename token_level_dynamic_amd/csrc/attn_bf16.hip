@@ -1090,6 +1090,14 @@ int attn_bf16_splits(const Dims& d) {
   const long long total = (long long)d.B * d.Hkv * ((units + kWaves - 1) / kWaves);
   if (total >= kTarget) return 1;
   long long s = (kTarget + total - 1) / total;
+  // The paired launch also runs the local band's workgroups (every row).
+  // When they and at least two ranges per global row block fit in one
+  // round of kTarget workgroups, take the most ranges that still fit: a
+  // second round costs more than the longer ranges (4K layer: 8 ranges,
+  // 704 workgroups, 0.072 ms; 4 ranges, 480 workgroups, 0.061 ms).
+  const long long lunits = ((long long)d.n + kRows - 1) / kRows * G;
+  const long long local = (long long)d.B * d.Hkv * ((lunits + kWaves - 1) / kWaves);
+  if (local + 2 * total <= kTarget) s = (kTarget - local) / total;
   s = std::min<long long>(s, 8);
   s = std::min<long long>(s, std::max<long long>(1, ((long long)d.n + kKeys - 1) / kKeys / 4));
   return (int)std::max<long long>(s, 1);
