@@ -68,6 +68,12 @@ __device__ __forceinline__ bf16x8 ld16(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
 
+// XOR swizzle of a d = 128 tile's 16-byte chunks by the row's low four bits:
+// logical chunk c of row r sits in slot c ^ swz16(r). Both the 16-byte row
+// reads (16 rows, one chunk) and the transposing reads (4 rows, 4 chunks)
+// then cover all 64 banks once; a whole 16-row group shares the pattern.
+__device__ __forceinline__ int swz16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
 // Lane l of instruction j fills LDS slot j*64 + l of a tile whose rows are
 // `chunks` 16-byte slots long (the last ones padding). Returns the byte
 // offset of that slot's source within a row block of row stride `st2`
@@ -92,12 +98,11 @@ __device__ __forceinline__ void issue_rows(const uint16_t* base, int nbytes, uin
     const int j = wave + kWaves * i;
     // (wave < kWaves: with NCH a multiple of kWaves every wave issues all)
     if (NCH % kWaves == 0 || j < NCH) {
-      // SWZ: slot (row, pc) takes the row's logical chunk pc ^ swz(row),
-      // swz as in KVTile (unpadded rows)
+      // SWZ: slot (row, pc) takes the row's logical chunk pc ^ swz16(row)
+      // (unpadded rows)
       const int slot = j * 64 + lane, row = slot / CHUNKS, pc = slot % CHUNKS;
-      const uint32_t voff =
-          SWZ ? (uint32_t)(row * st2 + ((pc ^ (((row & 3) << 2) | ((row >> 2) & 3))) << 4))
-              : slot_off(slot, CHUNKS, DCH, st2);
+      const uint32_t voff = SWZ ? (uint32_t)(row * st2 + ((pc ^ swz16(row)) << 4))
+                                : slot_off(slot, CHUNKS, DCH, st2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)(dst + j * 512), 16, voff, soff,
                                                0, 0);
     }
@@ -148,7 +153,7 @@ struct QTile {
   static constexpr int kInstr = kQT * kChunks / 64;
   static_assert(kQT * kChunks % 64 == 0, "tile must be whole instructions");
   // depends on r's low four bits only, so whole 16-row groups share it
-  __device__ static int swz(int r) { return kSwz ? ((r & 3) << 2) | ((r >> 2) & 3) : 0; }
+  __device__ static int swz(int r) { return kSwz ? swz16(r) : 0; }
   // source byte offset (row stride st2 bytes) of LDS slot `slot` of a tile;
   // pad slots read an out-of-range offset (zero)
   __device__ static uint32_t slot_src(int slot, int st2) {
@@ -590,7 +595,7 @@ struct KVTile {
   static constexpr int kChunks = kSwz ? D / 8 : D / 8 + 2;
   static constexpr int vChunks = D / 8 + 1;
   // depends on r's low four bits only, so whole 16-row groups share it
-  __device__ static int swz(int r) { return kSwz ? ((r & 3) << 2) | ((r >> 2) & 3) : 0; }
+  __device__ static int swz(int r) { return kSwz ? swz16(r) : 0; }
   static constexpr int kStride = kChunks * 8;
   static constexpr int vStride = vChunks * 8;
   static constexpr int kElems = kKeys * kStride;
